@@ -1,0 +1,157 @@
+"""Python access to the CPU oracle (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package.  It loads liboracle.so, built from oracle.c with gcc, and wraps
+each function with numpy arrays.  Nothing here touches a GPU.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "oracle.c")
+LIB = os.path.join(_HERE, "liboracle.so")
+
+ERR_BAD_EXPERT = 1
+ERR_DUP_EXPERT = 2
+
+GCC_FLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-Wall", "-Wextra"]
+
+
+def compile_oracle(src: str, out: str) -> str:
+    """Compile one oracle source file into a shared library (single-threaded C)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(LIB):
+        compile_oracle(SRC, LIB)
+    return LIB
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+class Oracle:
+    """numpy front end of one compiled oracle library."""
+
+    def __init__(self, path: str = LIB):
+        L = C.CDLL(path)
+        P = C.c_void_p
+        L.oracle_f32_to_bf16.argtypes = [C.c_float]
+        L.oracle_f32_to_bf16.restype = C.c_uint16
+        L.oracle_bf16_to_double.argtypes = [C.c_uint16]
+        L.oracle_bf16_to_double.restype = C.c_double
+        L.oracle_f32_to_bf16_array.argtypes = [P, P, C.c_int64]
+        L.oracle_f32_to_bf16_array.restype = None
+        L.oracle_layout.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
+        L.oracle_layout.restype = C.c_int
+        L.oracle_dispatch.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
+                                      P, P, P, P, P, P, P, P, P, P]
+        L.oracle_dispatch.restype = C.c_int
+        L.oracle_combine.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, P, P, P, P, P]
+        L.oracle_combine.restype = C.c_int
+        self.L = L
+        self.path = path
+
+    def f32_to_bf16(self, a) -> np.ndarray:
+        a = _c(a, np.float32)
+        out = np.empty(a.shape, np.uint16)
+        self.L.oracle_f32_to_bf16_array(_p(a), _p(out), a.size)
+        return out
+
+    def layout(self, topk_idx, E: int, G: int):
+        """Returns (tokens_per_expert[E], tokens_per_group[G], is_token_in_group[T], status)."""
+        idx = _c(topk_idx, np.int32)
+        T, k = idx.shape
+        tpe = np.zeros(E, np.int32)
+        tpg = np.zeros(G, np.int32)
+        bm = np.zeros(T, np.uint32)
+        st = self.L.oracle_layout(T, k, E, G, _p(idx), _p(tpe), _p(tpg), _p(bm))
+        if st < 0:
+            raise ValueError("oracle_layout: bad shape")
+        return tpe, tpg, bm, st
+
+    def dispatch(self, x, x_scales, topk_idx, topk_weights, E: int):
+        """Returns a dict with recv_x [T*k][...], recv_scales, recv_src_idx [T*k],
+        recv_weights [T*k], expert_offsets [E+1], slot_to_row [T][k], status.
+        Rows at or past R = expert_offsets[E] stay zero (unused capacity)."""
+        idx = _c(topk_idx, np.int32)
+        T, k = idx.shape
+        x = np.ascontiguousarray(x)
+        row_bytes = int(np.prod(x.shape[1:])) * x.itemsize
+        cap = T * k
+        recv_x = np.zeros((cap,) + x.shape[1:], x.dtype)
+        if x_scales is not None:
+            xs = np.ascontiguousarray(x_scales)
+            srb = int(np.prod(xs.shape[1:])) * xs.itemsize
+            recv_scales = np.zeros((cap,) + xs.shape[1:], xs.dtype)
+        else:
+            xs, srb, recv_scales = None, 0, None
+        src = np.full(cap, -1, np.int32)
+        rw = np.zeros(cap, np.float32)
+        off = np.zeros(E + 1, np.int32)
+        s2r = np.zeros((T, k), np.int32)
+        w = _c(topk_weights, np.float32)
+        st = self.L.oracle_dispatch(T, k, E, row_bytes, srb, _p(x), _p(xs), _p(idx), _p(w),
+                                    _p(recv_x), _p(recv_scales), _p(src), _p(rw), _p(off), _p(s2r))
+        if st < 0:
+            raise ValueError("oracle_dispatch: bad shape")
+        return dict(recv_x=recv_x, recv_scales=recv_scales, recv_src_idx=src, recv_weights=rw,
+                    expert_offsets=off, slot_to_row=s2r, status=st)
+
+    def combine(self, expert_out_bf16, recv_weights, slot_to_row, want_f32=True, want_bf16=True):
+        """expert_out_bf16: uint16 [R][H].  Returns (out_f32 [T][H] or None, out_bf16 [T][H] or None)."""
+        eo = _c(expert_out_bf16, np.uint16)
+        R, H = eo.shape
+        s2r = _c(slot_to_row, np.int32)
+        T, k = s2r.shape
+        rw = _c(recv_weights, np.float32)
+        of = np.zeros((T, H), np.float32) if want_f32 else None
+        ob = np.zeros((T, H), np.uint16) if want_bf16 else None
+        st = self.L.oracle_combine(T, k, H, R, _p(eo), _p(rw), _p(s2r), _p(of), _p(ob))
+        if st < 0:
+            raise ValueError("oracle_combine: bad arguments")
+        return of, ob
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use if missing)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def f32_to_bf16(a):
+    return get().f32_to_bf16(a)
+
+
+def layout(topk_idx, E, G):
+    return get().layout(topk_idx, E, G)
+
+
+def dispatch(x, x_scales, topk_idx, topk_weights, E):
+    return get().dispatch(x, x_scales, topk_idx, topk_weights, E)
+
+
+def combine(expert_out_bf16, recv_weights, slot_to_row, want_f32=True, want_bf16=True):
+    return get().combine(expert_out_bf16, recv_weights, slot_to_row, want_f32, want_bf16)

@@ -1,0 +1,253 @@
+/*
+ * CPU oracle for one GPU's share of MoE expert-parallel
+ * get_dispatch_layout -> dispatch -> combine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this code; the library under test never
+ * does.  It is plain, single-threaded C99 written straight from the
+ * definitions, shares no source with the GPU path, and is meant to be checked
+ * by eye against the passages cited below.
+ *
+ * Source: "MSCCLPP EP implementation - #852" (MSCCL++ pull request page).
+ *   - PR description, "Scope": the layout call, intranode dispatch and
+ *     intranode combine are the three operations of the path.
+ *   - Review file table, entry for the high-throughput layout kernel: the
+ *     layout produces token counts and the token-in-rank flags.
+ *   - Commit message fixing internode combine: combine runs in the reverse
+ *     direction of dispatch and consumes the receiver-side bookkeeping that
+ *     dispatch returned (the "handle").
+ *   - Commit message on combine byte accounting: each expert returns one copy
+ *     per dispatched token, so combine reads one row per routed copy.
+ *   - Commit messages on warp geometry and the review's code-scanning excerpt:
+ *     hidden rows move in 16-byte units.
+ *
+ * Readings where the page is silent (each is a documented choice):
+ *   - a "rank" of the page is a destination group g of this GPU; expert e
+ *     belongs to group e / (E/G) (equal, contiguous expert blocks per rank);
+ *   - tokens_per_group counts a token once per group it reaches;
+ *   - is_token_in_group is one uint32 per token, bit g;
+ *   - a masked slot holds -1; any other id outside [0,E) is an error and the
+ *     slot is treated as masked;
+ *   - received rows are ordered by (expert, token, slot) ascending: each
+ *     expert's rows are contiguous and stable in token order;
+ *   - recv_src_idx holds the source token index;
+ *   - combine sums slots j = 0..k-1 in ascending order with fp32 fused
+ *     multiply-add, then rounds once to bf16 (nearest, ties to even); a token
+ *     whose every slot is masked gets +0.
+ *
+ * Error codes (bit mask, same meaning as the library's device status bits):
+ *   1  an expert id outside {-1} U [0,E)      (slot treated as masked)
+ *   2  an expert id repeated within one token  (each copy is its own slot)
+ *  -1  bad shape argument
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_ERR_BAD_EXPERT 1
+#define ORACLE_ERR_DUP_EXPERT 2
+
+/* ------------------------------------------------------------------------ */
+/* bf16 <-> binary32.                                                        */
+/* bf16 is the upper half of an IEEE binary32: sign, 8 exponent bits and 7   */
+/* fraction bits.                                                            */
+/* ------------------------------------------------------------------------ */
+
+double oracle_bf16_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a binary32 value to the nearest bf16 value, ties to even.
+ * The bf16 grid near |v| in [2^(p-1), 2^p) is spaced 2^(p-8) (8 significant
+ * bits); below the smallest normal 2^-126 the spacing stays 2^-133.  The value
+ * is divided by the spacing (exact: a power of two), rounded to an integer
+ * with rint() in the default round-to-nearest-even mode, and scaled back.
+ * A result of 2^128 or more is +-infinity; NaN maps to the quiet NaN 0x7FC0
+ * with the input's sign. */
+uint16_t oracle_f32_to_bf16(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(v)) return (uint16_t)(sign | 0x7F80u);
+    double d = fabs((double)v);
+    if (d == 0.0) return sign;
+    int p;
+    frexp(d, &p);                 /* d in [2^(p-1), 2^p) */
+    if (p < -125) p = -125;       /* subnormal range keeps the 2^-133 spacing */
+    double spacing = ldexp(1.0, p - 8);
+    double r = rint(d / spacing) * spacing;
+    if (r >= ldexp(1.0, 128)) return (uint16_t)(sign | 0x7F80u);
+    float rf = (float)r;          /* exact: r is a bf16 value */
+    uint32_t ru;
+    memcpy(&ru, &rf, sizeof ru);
+    return (uint16_t)(sign | (ru >> 16));
+}
+
+/* Vector helpers for the harness (convert arrays element by element). */
+void oracle_f32_to_bf16_array(const float* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(in[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* validation                                                               */
+/* ------------------------------------------------------------------------ */
+
+static int bad_shape(int T, int k, int E, int G)
+{
+    if (T < 0 || k < 1 || k > 32 || E < 1 || G < 1 || G > 32) return 1;
+    if (E % G != 0) return 1;
+    return 0;
+}
+
+/* Is slot (t,j) routed, i.e. does it hold an id in [0,E)? */
+static int routed(int32_t id, int E) { return id >= 0 && id < E; }
+
+/* Status bits for the routing table: ids out of range and repeats. */
+static int routing_status(int T, int k, int E, const int32_t* topk_idx)
+{
+    int st = 0;
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int32_t id = topk_idx[(int64_t)t * k + j];
+            if (id != -1 && !routed(id, E)) st |= ORACLE_ERR_BAD_EXPERT;
+            if (!routed(id, E)) continue;
+            for (int jj = 0; jj < j; ++jj)
+                if (topk_idx[(int64_t)t * k + jj] == id) st |= ORACLE_ERR_DUP_EXPERT;
+        }
+    }
+    return st;
+}
+
+/* ------------------------------------------------------------------------ */
+/* layout: tokens per expert, tokens per group, token-in-group bitmap        */
+/* ------------------------------------------------------------------------ */
+
+int oracle_layout(int T, int k, int E, int G, const int32_t* topk_idx,
+                  int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                  uint32_t* is_token_in_group)
+{
+    if (bad_shape(T, k, E, G)) return -1;
+    int experts_per_group = E / G;
+
+    /* tokens_per_expert[e] = number of slots (t,j) whose id is e */
+    for (int e = 0; e < E; ++e) tokens_per_expert[e] = 0;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t id = topk_idx[(int64_t)t * k + j];
+            if (routed(id, E)) tokens_per_expert[id] += 1;
+        }
+
+    /* bit g of is_token_in_group[t] = some routed slot of t lands in group g */
+    for (int t = 0; t < T; ++t) {
+        uint32_t bits = 0;
+        for (int j = 0; j < k; ++j) {
+            int32_t id = topk_idx[(int64_t)t * k + j];
+            if (routed(id, E)) bits |= 1u << (id / experts_per_group);
+        }
+        is_token_in_group[t] = bits;
+    }
+
+    /* tokens_per_group[g] = number of tokens with bit g set */
+    for (int g = 0; g < G; ++g) {
+        int32_t c = 0;
+        for (int t = 0; t < T; ++t) c += (int32_t)((is_token_in_group[t] >> g) & 1u);
+        tokens_per_group[g] = c;
+    }
+    return routing_status(T, k, E, topk_idx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* dispatch: pack every routed copy into per-expert receive rows             */
+/* ------------------------------------------------------------------------ */
+
+/* x: [T][row_bytes] raw row bytes (bf16 or fp8 codes; copied, never read as
+ * numbers).  x_scales: [T][scale_row_bytes] or NULL.  Outputs have capacity
+ * T*k rows; rows at or past R = expert_offsets[E] are left untouched. */
+int oracle_dispatch(int T, int k, int E, int64_t row_bytes, int64_t scale_row_bytes,
+                    const uint8_t* x, const uint8_t* x_scales,
+                    const int32_t* topk_idx, const float* topk_weights,
+                    uint8_t* recv_x, uint8_t* recv_scales,
+                    int32_t* recv_src_idx, float* recv_weights,
+                    int32_t* expert_offsets, int32_t* slot_to_row)
+{
+    if (T < 0 || k < 1 || k > 32 || E < 1 || row_bytes < 0 || scale_row_bytes < 0) return -1;
+
+    /* counts and exclusive prefix: expert e owns rows [off[e], off[e+1]) */
+    int64_t* cursor = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    if (!cursor) return -1;
+    for (int t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int32_t id = topk_idx[(int64_t)t * k + j];
+            if (routed(id, E)) cursor[id] += 1;
+        }
+    int64_t run = 0;
+    for (int e = 0; e < E; ++e) {
+        int64_t c = cursor[e];
+        expert_offsets[e] = (int32_t)run;
+        cursor[e] = run;
+        run += c;
+    }
+    expert_offsets[E] = (int32_t)run;
+
+    /* visit slots in (t, j) order; each expert's cursor hands out its rows in
+     * that order, so an expert's rows are stable in token order */
+    for (int t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int64_t s = (int64_t)t * k + j;
+            int32_t id = topk_idx[s];
+            if (!routed(id, E)) {
+                slot_to_row[s] = -1;
+                continue;
+            }
+            int64_t r = cursor[id]++;
+            memcpy(recv_x + r * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);
+            if (x_scales && recv_scales && scale_row_bytes > 0)
+                memcpy(recv_scales + r * scale_row_bytes, x_scales + (int64_t)t * scale_row_bytes,
+                       (size_t)scale_row_bytes);
+            recv_src_idx[r] = t;
+            recv_weights[r] = topk_weights[s];
+            slot_to_row[s] = (int32_t)r;
+        }
+    }
+    free(cursor);
+    return routing_status(T, k, E, topk_idx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* combine: weighted top-k sum of the expert outputs, per token               */
+/* ------------------------------------------------------------------------ */
+
+/* expert_out: bf16 [R][H]; recv_weights: [R]; slot_to_row: [T][k] (-1 masked).
+ * out[t][h] = sum over j = 0..k-1 (ascending) of recv_weights[r] * expert_out[r][h]
+ * with r = slot_to_row[t][j] >= 0, accumulated in fp32 by fused multiply-add
+ * from 0.0f.  out_f32 receives the fp32 sum, out_bf16 its bf16 rounding;
+ * either may be NULL. */
+int oracle_combine(int T, int k, int H, int64_t R, const uint16_t* expert_out,
+                   const float* recv_weights, const int32_t* slot_to_row,
+                   float* out_f32, uint16_t* out_bf16)
+{
+    if (T < 0 || k < 1 || H < 0 || R < 0) return -1;
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                int32_t r = slot_to_row[(int64_t)t * k + j];
+                if (r < 0) continue;
+                if ((int64_t)r >= R) return -1;
+                float v = (float)oracle_bf16_to_double(expert_out[(int64_t)r * H + h]);
+                acc = fmaf(recv_weights[r], v, acc);
+            }
+            if (out_f32) out_f32[(int64_t)t * H + h] = acc;
+            if (out_bf16) out_bf16[(int64_t)t * H + h] = oracle_f32_to_bf16(acc);
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,364 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check takes an ``Oracle`` object (so the same checks run against
+deliberately broken copies of the oracle in the mutation tests) and raises
+AssertionError when a fact fails.  The facts come from the definitions of the
+operations on the "MSCCLPP EP implementation - #852" page (layout counts and
+token-in-rank flags; dispatch/combine as inverse directions sharing a handle;
+one combine read per routed copy), from arithmetic closed forms, and from a
+library routine (torch's float -> bfloat16 cast).  None of them re-types the
+oracle's own loops: integer results are compared with a sort-based
+formulation over every routing of tiny shapes, and sums with closed forms.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+import torch
+
+from combine_ep_get_dispatch_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# bf16 helpers that are not the oracle's
+# ---------------------------------------------------------------------------
+
+def torch_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(f32, np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Distance between bf16 encodings on the sign-magnitude ordered line."""
+    def ordered(u):
+        u = np.asarray(u, np.int64)
+        return np.where(u & 0x8000, -(u & 0x7FFF), u)
+    return np.abs(ordered(a) - ordered(b))
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding against the library cast
+# ---------------------------------------------------------------------------
+
+def check_bf16_rounding(orc):
+    rng = np.random.default_rng(7)
+    parts = [
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(5000) * 1e30).astype(np.float32),
+        (rng.standard_normal(5000) * 1e-30).astype(np.float32),
+    ]
+    # exact ties: low half 0x8000 with even and odd kept parts, and near-ties
+    hi = rng.integers(0, 0x7F7F, size=4000, dtype=np.uint32)
+    for low in (0x8000, 0x7FFF, 0x8001, 0x0000, 0xFFFF):
+        bits = (hi << 16) | np.uint32(low)
+        parts.append(bits.view(np.float32))
+        parts.append((bits | np.uint32(0x80000000)).view(np.float32))
+    # subnormals, zero, the overflow edge, infinities
+    sub = np.arange(1, 70000, 7, dtype=np.uint32)
+    parts.append(sub.view(np.float32))
+    edge = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 3.39e38, 3.3961e38, 3.4e38,
+                     np.finfo(np.float32).max, 1e-45, -1e-45, 1.17549435e-38], np.float32)
+    parts.append(edge)
+    v = np.concatenate(parts)
+    got = orc.f32_to_bf16(v)
+    want = torch_bf16_bits(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"bf16 rounding differs from torch at {v[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+    nan = orc.f32_to_bf16(np.array([np.nan], np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x007F) != 0, "NaN must stay NaN"
+
+
+# ---------------------------------------------------------------------------
+# brute force over every routing of tiny shapes
+# ---------------------------------------------------------------------------
+
+def token_options(E: int, k: int):
+    """Every slot assignment of one token: each slot masked (-1) or an expert,
+    routed experts pairwise distinct."""
+    opts = []
+    for combo in itertools.product(range(-1, E), repeat=k):
+        routed = [e for e in combo if e >= 0]
+        if len(routed) == len(set(routed)):
+            opts.append(combo)
+    return opts
+
+
+def sorted_key_reference(idx: np.ndarray, E: int, G: int):
+    """Layout and dispatch rows by a different route than the oracle's: a
+    Counter for the counts, Python sets for group membership, and one global
+    sort of the (expert, token, slot) keys for the receive order."""
+    T, k = idx.shape
+    per_group = E // G
+    tpe = np.zeros(E, np.int64)
+    groups_of = []
+    keys = []
+    for t in range(T):
+        gs = set()
+        for j in range(k):
+            e = int(idx[t, j])
+            if e >= 0:
+                tpe[e] += 1
+                gs.add(e // per_group)
+                keys.append((e, t, j))
+        groups_of.append(gs)
+    tpg = np.array([sum(1 for gs in groups_of if g in gs) for g in range(G)], np.int64)
+    bm = np.array([sum(1 << g for g in gs) for gs in groups_of], np.uint64)
+    keys.sort()
+    s2r = -np.ones((T, k), np.int64)
+    for r, (e, t, j) in enumerate(keys):
+        s2r[t, j] = r
+    off = np.concatenate([[0], np.cumsum(tpe)])
+    return tpe, tpg, bm, off, s2r, keys
+
+
+def check_bruteforce(orc, shapes=((1, 1, 2, 1), (2, 1, 2, 2), (3, 1, 4, 2), (2, 2, 4, 2),
+                                  (3, 2, 4, 2), (2, 2, 4, 1), (2, 2, 4, 4), (2, 3, 3, 3))):
+    H = 8
+    for (T, k, E, G) in shapes:
+        opts = token_options(E, k)
+        # structured payload: every element of token t is t+1, every weight
+        # names its slot, so a misplaced row or weight is visible
+        x = torch_bf16_bits(np.repeat((np.arange(T, dtype=np.float32) + 1)[:, None], H, axis=1))
+        w = (np.arange(T * k, dtype=np.float32).reshape(T, k) + 1) / 64.0
+        for choice in itertools.product(range(len(opts)), repeat=T):
+            idx = np.array([opts[c] for c in choice], np.int32).reshape(T, k)
+            tpe, tpg, bm, off, s2r, keys = sorted_key_reference(idx, E, G)
+            o_tpe, o_tpg, o_bm, st = orc.layout(idx, E, G)
+            assert st == 0, (idx, st)
+            assert np.array_equal(o_tpe, tpe), (idx, o_tpe, tpe)
+            assert np.array_equal(o_tpg, tpg), (idx, o_tpg, tpg)
+            assert np.array_equal(o_bm.astype(np.uint64), bm), (idx, o_bm, bm)
+            d = orc.dispatch(x, None, idx, w, E)
+            assert np.array_equal(d["expert_offsets"], off), (idx, d["expert_offsets"], off)
+            assert np.array_equal(d["slot_to_row"], s2r), (idx, d["slot_to_row"], s2r)
+            R = len(keys)
+            for r, (e, t, j) in enumerate(keys):
+                assert d["recv_src_idx"][r] == t
+                assert d["recv_weights"][r] == w[t, j]
+                assert np.array_equal(d["recv_x"][r], x[t])
+            # identity experts: out[t] = (t+1) * sum of its routed weights,
+            # exact in fp32 for these small dyadic weights
+            eo = d["recv_x"][:R].reshape(R, H)
+            of, ob = orc.combine(eo, d["recv_weights"][:R], d["slot_to_row"])
+            for t in range(T):
+                want = (t + 1) * float(sum(w[t, j] for j in range(k) if idx[t, j] >= 0))
+                assert np.all(of[t] == np.float32(want)), (idx, t, of[t], want)
+
+
+# ---------------------------------------------------------------------------
+# invariants on config-shaped inputs
+# ---------------------------------------------------------------------------
+
+def check_layout_invariants(orc, wl):
+    tpe, tpg, bm, st = orc.layout(wl.topk_idx, wl.E, wl.G)
+    idx = wl.topk_idx
+    assert st == 0
+    assert int(tpe.sum()) == wl.T * wl.k - int((idx < 0).sum()), "expert counts must sum to T*k - masked"
+    assert np.all(tpe >= 0)
+    for g in range(wl.G):
+        col = (bm >> np.uint32(g)) & 1
+        assert int(tpg[g]) == int(col.sum()), "tokens_per_group must be the popcount of its bitmap column"
+    assert np.all(tpg <= wl.T)
+    assert np.all(bm < (np.uint64(1) << np.uint64(wl.G)))
+    reached = int((idx >= 0).any(axis=1).sum()) if wl.T else 0
+    assert int(tpg.sum()) >= reached
+    assert int((bm != 0).sum()) == reached, "a token has bits iff it has a routed slot"
+    # a token's bit count never exceeds its routed slots
+    nslots = (idx >= 0).sum(axis=1)
+    bits = np.array([bin(int(b)).count("1") for b in bm], np.int64)
+    assert np.all(bits <= nslots)
+    if wl.E == wl.G:
+        assert np.array_equal(tpg, tpe), "one expert per group: group counts equal expert counts"
+    return tpe, tpg, bm
+
+
+def check_dispatch_invariants(orc, wl, d=None):
+    if d is None:
+        d = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+    tpe, _, _, _ = orc.layout(wl.topk_idx, wl.E, wl.G)
+    off = d["expert_offsets"].astype(np.int64)
+    s2r = d["slot_to_row"]
+    idx = wl.topk_idx
+    R = wl.num_routed
+    assert off[0] == 0 and off[-1] == R
+    assert np.all(np.diff(off) >= 0)
+    assert np.array_equal(np.diff(off), tpe.astype(np.int64)), "segment sizes are the expert counts"
+    assert np.all(s2r[idx < 0] == -1)
+    rows = s2r[idx >= 0]
+    assert np.array_equal(np.sort(rows), np.arange(R)), "slot_to_row must be a bijection onto [0,R)"
+    t_of = np.broadcast_to(np.arange(wl.T)[:, None], idx.shape)[idx >= 0]
+    e_of = idx[idx >= 0]
+    assert np.all((off[e_of] <= rows) & (rows < off[e_of + 1])), "row lies in its expert's segment"
+    assert np.array_equal(d["recv_src_idx"][rows], t_of), "src_idx names the source token"
+    assert np.array_equal(d["recv_weights"][rows].view(np.uint32),
+                          wl.topk_weights[idx >= 0].view(np.uint32)), "weights copied bit for bit"
+    src = d["recv_src_idx"][:R]
+    assert np.array_equal(d["recv_x"][:R], wl.x[src]), "every received row equals its source row"
+    if wl.x_scales is not None:
+        assert np.array_equal(d["recv_scales"][:R].view(np.uint32), wl.x_scales[src].view(np.uint32))
+    for e in range(wl.E):
+        seg = src[off[e]:off[e + 1]]
+        assert np.all(np.diff(seg) > 0), "stable in token order (strictly increasing sources)"
+    return d
+
+
+# ---------------------------------------------------------------------------
+# combine closed forms
+# ---------------------------------------------------------------------------
+
+def _dispatch_and_experts(orc, wl):
+    d = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+    R = wl.num_routed
+    re = W.row_experts(d["expert_offsets"])
+    eo = W.expert_outputs(wl, d["recv_x"][:R], None if d["recv_scales"] is None else d["recv_scales"][:R], re)
+    eo_bits = eo.view(torch.int16).numpy().view(np.uint16)
+    return d, eo_bits
+
+
+def check_combine_exact_dyadic(orc, T=64, H=64, E=16, G=4, k=4, seed=11):
+    """Identity experts, weights 1/2, 1/4, 1/8, 1/8 in some slot order: every
+    partial sum is exact in fp32, so the result is x itself, bit for bit."""
+    wl = W.make_workload("dyadic", T, H, E, G, k, seed=seed, expert_kind="identity")
+    rng = np.random.default_rng(seed)
+    base = np.array([0.5, 0.25, 0.125, 0.125], np.float32)
+    wl.topk_weights = np.stack([rng.permutation(base) for _ in range(T)]).astype(np.float32)
+    d, eo = _dispatch_and_experts(orc, wl)
+    of, ob = orc.combine(eo, d["recv_weights"], d["slot_to_row"])
+    assert np.array_equal(of, bf16_to_f64(wl.x).astype(np.float32)), "sum of dyadic weights = 1 must return x"
+    assert np.array_equal(ob, wl.x)
+
+
+def check_combine_k1_inverse(orc, T=200, H=48, E=8, G=2, seed=12):
+    """k = 1 with weight 1.0: combine is the inverse permutation of dispatch."""
+    wl = W.make_workload("k1", T, H, E, G, 1, seed=seed, expert_kind="identity")
+    wl.topk_weights = np.ones((T, 1), np.float32)
+    d, eo = _dispatch_and_experts(orc, wl)
+    of, ob = orc.combine(eo, d["recv_weights"], d["slot_to_row"])
+    assert np.array_equal(ob, wl.x)
+
+
+def check_combine_round_trip(orc, wl):
+    """Identity experts and weights summing to one: combine returns x to within
+    one bf16 ulp (the fp32 sum is within a few fp32 ulps of x)."""
+    assert wl.expert_kind in ("identity",)
+    d, eo = _dispatch_and_experts(orc, wl)
+    of, ob = orc.combine(eo, d["recv_weights"], d["slot_to_row"])
+    routed = (wl.topk_idx >= 0).any(axis=1)
+    dist = bf16_ulp_distance(ob[routed], wl.x[routed])
+    assert dist.size == 0 or int(dist.max()) <= 1, f"round trip off by {int(dist.max())} ulp"
+    assert np.all(of[~routed] == 0.0)
+
+
+def check_combine_closed_form(orc, wl, rel_bound):
+    """out[t][h] = x[t][h] * sum_j w_j * c(e_j) for the stand-in expert
+    multipliers c; compared in fp64 against a bound on the bf16 rounding of the
+    expert outputs plus fp32 accumulation.  Every term has the sign of x, so
+    the relative bound is well defined."""
+    d, eo = _dispatch_and_experts(orc, wl)
+    of, ob = orc.combine(eo, d["recv_weights"], d["slot_to_row"])
+    c = W.expert_factors(wl.expert_kind, wl.E).astype(np.float64)
+    idx = wl.topk_idx
+    w = np.where(idx >= 0, wl.topk_weights.astype(np.float64), 0.0)
+    mult = (w * c[np.maximum(idx, 0)]).sum(axis=1)
+    if wl.x_dtype == W.X_BF16:
+        xv = bf16_to_f64(wl.x)
+    else:
+        codes = torch.from_numpy(wl.x).view(torch.float8_e4m3fn).double().numpy()
+        xv = (codes.reshape(wl.T, wl.num_scales, wl.scale_block)
+              * wl.x_scales.astype(np.float64)[:, :, None]).reshape(wl.T, wl.H)
+    exact = xv * mult[:, None]
+    nz = exact != 0
+    rel = np.abs(of.astype(np.float64)[nz] - exact[nz]) / np.abs(exact[nz])
+    assert rel.size == 0 or rel.max() <= rel_bound, f"closed form off by {rel.max():.3e} > {rel_bound:.3e}"
+    assert np.all(of[~nz] == 0.0)
+    # the bf16 output is the fp32 sum rounded once
+    assert np.array_equal(ob, torch_bf16_bits(of))
+
+
+# ---------------------------------------------------------------------------
+# hand-worked example
+# ---------------------------------------------------------------------------
+
+def check_worked_example(orc, path=os.path.join(GOLDEN, "worked_example.json")):
+    with open(path) as f:
+        g = json.load(f)
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_weights"], np.float32)
+    x = torch_bf16_bits(np.array(g["x"], np.float32))
+    E, G = g["E"], g["G"]
+    tpe, tpg, bm, st = orc.layout(idx, E, G)
+    assert st == 0
+    assert tpe.tolist() == g["tokens_per_expert"]
+    assert tpg.tolist() == g["tokens_per_group"]
+    assert bm.tolist() == g["is_token_in_group"]
+    d = orc.dispatch(x, None, idx, w, E)
+    R = d["expert_offsets"][-1]
+    assert d["expert_offsets"].tolist() == g["expert_offsets"]
+    assert d["slot_to_row"].tolist() == g["slot_to_row"]
+    assert d["recv_src_idx"][:R].tolist() == g["recv_src_idx"]
+    assert d["recv_weights"][:R].tolist() == g["recv_weights"]
+    eo = torch_bf16_bits(np.array(g["expert_out"], np.float32))
+    of, ob = orc.combine(eo, d["recv_weights"][:R], d["slot_to_row"])
+    assert of.tolist() == g["out"]
+    assert np.array_equal(ob, torch_bf16_bits(np.array(g["out"], np.float32)))
+
+
+def check_error_status(orc):
+    idx = np.array([[0, 5], [1, 1], [-1, 2]], np.int32)   # 5 >= E: bad id; repeat in token 1
+    tpe, tpg, bm, st = orc.layout(idx, 4, 2)
+    assert st & 1 and st & 2
+    assert tpe.tolist() == [1, 2, 1, 0], "bad id is skipped; a repeat counts as two slots"
+    idx2 = np.array([[0, -7]], np.int32)
+    _, _, _, st2 = orc.layout(idx2, 4, 2)
+    assert st2 == 1, "a negative id other than -1 is a bad id"
+
+
+ALL_BASIC = [check_bf16_rounding, check_bruteforce, check_combine_exact_dyadic, check_combine_k1_inverse,
+             check_worked_example, check_error_status]
+
+
+def small_configs():
+    """Config-shaped workloads small enough for a quick CPU pass."""
+    return [
+        W.config(1),
+        W.make_workload("uniform_mid", 512, 64, 64, 8, 8, seed=21, expert_kind="scale_by_id"),
+        W.make_workload("zipf_mid", 512, 64, 256, 8, 8, seed=22, routing="zipf", mask_frac=0.05,
+                        expert_kind="scale_by_id"),
+        W.make_workload("fp8_mid", 32, 512, 32, 8, 8, seed=23, x_dtype=W.X_FP8, scale_block=128,
+                        expert_kind="dequant_identity"),
+        W.make_workload("mixtral_mid", 1024, 64, 8, 8, 2, seed=24, expert_kind="double_odd"),
+    ]
+
+
+def run_all(orc):
+    """Every pin in one go (used by the mutation test)."""
+    for chk in ALL_BASIC:
+        chk(orc)
+    for wl in small_configs():
+        check_layout_invariants(orc, wl)
+        check_dispatch_invariants(orc, wl)
+    wl1 = W.config(1)
+    check_combine_round_trip(orc, wl1)
+    for wl in small_configs()[1:]:
+        check_combine_closed_form(orc, wl, rel_bound=CLOSED_FORM_BOUND[wl.expert_kind])
+
+
+# bf16 rounding of each stand-in expert output (<= 2^-8 relative: 8 significant
+# bits, round to nearest) plus fp32
+# accumulation of up to 8 same-sign terms (< 9 * 2^-24 relative)
+# (the fp8 dequantisation adds one fp32 rounding before the bf16 one)
+CLOSED_FORM_BOUND = {
+    "scale_by_id": 2.0 ** -8 + 9 * 2.0 ** -24,
+    "dequant_identity": 2.0 ** -8 + 10 * 2.0 ** -24,
+    "double_odd": 9 * 2.0 ** -24,
+    "identity": 9 * 2.0 ** -24,
+}

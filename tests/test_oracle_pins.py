@@ -1,0 +1,75 @@
+"""Pins of the CPU oracle (no GPU): library cast, brute force, invariants,
+closed forms and a hand-worked example."""
+import numpy as np
+import pytest
+
+from combine_ep_get_dispatch_amd import workloads as W
+import oracle_checks as K
+
+
+def test_bf16_rounding_matches_library_cast(orc):
+    K.check_bf16_rounding(orc)
+
+
+def test_bruteforce_every_tiny_routing(orc):
+    K.check_bruteforce(orc)
+
+
+def test_worked_example(orc):
+    K.check_worked_example(orc)
+
+
+def test_error_status_bits(orc):
+    K.check_error_status(orc)
+
+
+@pytest.mark.parametrize("i", range(5))
+def test_layout_and_dispatch_invariants(orc, i):
+    wl = K.small_configs()[i]
+    K.check_layout_invariants(orc, wl)
+    K.check_dispatch_invariants(orc, wl)
+
+
+def test_combine_dyadic_weights_exact(orc):
+    K.check_combine_exact_dyadic(orc)
+
+
+def test_combine_k1_is_inverse_permutation(orc):
+    K.check_combine_k1_inverse(orc)
+
+
+def test_combine_round_trip_tiny_config(orc):
+    K.check_combine_round_trip(orc, W.config(1))
+
+
+@pytest.mark.parametrize("i", [1, 2, 3, 4])
+def test_combine_closed_forms(orc, i):
+    wl = K.small_configs()[i]
+    K.check_combine_closed_form(orc, wl, K.CLOSED_FORM_BOUND[wl.expert_kind])
+
+
+def test_edge_shapes(orc):
+    # T = 0; every slot masked; k = 1; G = 1; G = E; 16-byte rows
+    cases = [
+        W.make_workload("empty", 0, 8, 4, 2, 2, seed=1),
+        W.make_workload("all_masked", 5, 8, 4, 2, 2, seed=2, mask_frac=1.0),
+        W.make_workload("k1", 33, 8, 4, 2, 1, seed=3),
+        W.make_workload("g1", 40, 8, 16, 1, 4, seed=4),
+        W.make_workload("g_eq_e", 40, 8, 16, 16, 4, seed=5),
+        W.make_workload("fp8_16B", 20, 128, 8, 2, 2, seed=6, x_dtype=W.X_FP8, scale_block=128),
+    ]
+    for wl in cases:
+        K.check_layout_invariants(orc, wl)
+        d = K.check_dispatch_invariants(orc, wl)
+        if wl.name == "all_masked":
+            assert d["expert_offsets"][-1] == 0
+            eo = np.zeros((0, wl.H), np.uint16)
+            of, ob = orc.combine(eo, d["recv_weights"][:0], d["slot_to_row"])
+            assert np.all(of == 0) and np.all(ob == 0), "an all-masked token sums to +0"
+
+
+def test_full_size_dispatch_invariants(orc):
+    """The DeepSeek-V3-shaped workload at its real size (dispatch only)."""
+    wl = W.config(2)
+    K.check_layout_invariants(orc, wl)
+    K.check_dispatch_invariants(orc, wl)
