@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of one GPU's share of MoE EP layout -> dispatch -> combine.
+
+One step = ep_get_dispatch_layout + ep_dispatch + ep_combine (bf16 out) over
+one batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168
+bf16, E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
+stand-in expert outputs are resident in HBM before the timed region; the
+timed region is exactly K steps between two device synchronisations.  HIP
+events on the launch stream time each call (one kernel each) inside that
+region; the dominant kernel's algorithmic bytes over its mean duration give
+the roofline entry.  The CPU oracle, timed on a bounded sample of the same
+workload on the host, is the reported baseline.
+
+Prints one JSON line.  `--gpus` above 1 is refused: this build runs one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at T=4096 H=7168 E=256 k=8"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def make_inputs(wl, dev):
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(wl.x).view(np.uint8).reshape(wl.T, wl.row_bytes)).to(dev)
+    xs = torch.from_numpy(wl.x_scales).to(dev) if wl.x_scales is not None else None
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    w = torch.from_numpy(wl.topk_weights).to(dev)
+    return x, xs, idx, w
+
+
+def shape_of(M, W, wl):
+    dt = M.FP8_E4M3 if wl.x_dtype == W.X_FP8 else M.BF16
+    return M.moedisp_shape.make(wl.T, wl.H, wl.E, wl.G, wl.k, dt, wl.scale_block)
+
+
+def run_gpu(cid, steps, warmup, dev):
+    """Time `steps` layout+dispatch+combine steps of config `cid`."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    from combine_ep_get_dispatch_amd import workloads as W
+    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS, algorithmic_bytes
+
+    wl = W.config(cid)
+    shape = shape_of(M, W, wl)
+    bufs = M.EpBuffers(shape, dev)
+    x, xs, idx, w = make_inputs(wl, dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    # one dispatch to size the stand-in expert outputs (outside timing)
+    bufs.layout(idx)
+    bufs.dispatch(x, xs, idx, w)
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} on config {cid}")
+    R = int(bufs.expert_offsets[-1].item())
+    offs = bufs.expert_offsets.cpu().numpy()
+    row_expert = W.row_experts(offs)
+    eo = torch.zeros((wl.T * wl.k, wl.H), dtype=torch.bfloat16, device=dev)
+    rs = bufs.recv_scales[:R] if bufs.recv_scales is not None else None
+    eo[:R] = W.expert_outputs(wl, bufs.recv_x[:R], rs, row_expert, device=dev)
+    del rs
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bufs.layout(idx, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bufs.dispatch(x, xs, idx, w, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} after timed steps on config {cid}")
+
+    elapsed = t1 - t0
+    lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
+    dis = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
+    B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
+    ms_step = elapsed / steps * 1e3
+    res = dict(
+        config=cid, workload=wl.name, T=wl.T, H=wl.H, E=wl.E, G=wl.G, k=wl.k, x_dtype=wl.x_dtype, R=R,
+        routing=wl.meta["routing"], mask_frac=wl.meta["mask_frac"],
+        ms_per_step=ms_step, tokens_per_s=wl.T / (ms_step * 1e-3),
+        step_gbps=B["step"] / (ms_step * 1e-3) / 1e9,
+        layout_us=float(lay.mean()), dispatch_us=float(dis.mean()), combine_us=float(com.mean()),
+        dispatch_us_min=float(dis.min()), combine_us_min=float(com.min()),
+        dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
+        combine_gbps=B["combine"] / (com.mean() * 1e-6) / 1e9,
+        dc_tokens_per_s=wl.T / ((dis.mean() + com.mean()) * 1e-6),
+        bytes=B,
+    )
+    res["dc_gbps"] = B["dispatch_combine"] / ((dis.mean() + com.mean()) * 1e-6) / 1e9
+    res["dc_frac"] = res["dc_gbps"] / HBM_PEAK_GBPS
+    del bufs, eo, out, x, xs, idx, w
+    torch.cuda.empty_cache()
+    return res
+
+
+def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
+    """Achievable HBM copy bandwidth (read + write bytes) with the library's
+    plain 16-byte copy kernel."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        M.ep_probe_copy(dst, src, nbytes)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        M.ep_probe_copy(dst, src, nbytes)
+    e.record()
+    torch.cuda.synchronize()
+    us = s.elapsed_time(e) * 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (us * 1e-6) / 1e9
+
+
+def cpu_baseline(budget_s: float = 12.0):
+    """The CPU oracle (single-threaded C) on the same DeepSeek-V3-shaped
+    workload, full steps of layout + dispatch + combine until about
+    `budget_s` seconds of oracle time have run (at least one step)."""
+    import oracle
+    from combine_ep_get_dispatch_amd import workloads as W
+    import torch
+
+    oracle.build(force=False)
+    orc = oracle.get()
+    wl = W.config(2)
+    # stand-in expert outputs from one untimed oracle dispatch
+    d = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+    R = int(d["expert_offsets"][-1])
+    eo = W.expert_outputs(wl, d["recv_x"][:R], None, W.row_experts(d["expert_offsets"]))
+    eo_bits = eo.view(torch.int16).numpy().view(np.uint16)
+    del d
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 8):
+        t0 = time.perf_counter()
+        orc.layout(wl.topk_idx, wl.E, wl.G)
+        dd = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+        orc.combine(eo_bits, dd["recv_weights"][:R], dd["slot_to_row"], want_f32=False, want_bf16=True)
+        times.append(time.perf_counter() - t0)
+        del dd
+    per_step = float(np.median(times))
+    try:
+        cpu = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
+        model = next((l.split(":", 1)[1].strip() for l in cpu.splitlines() if l.startswith("Model name")), "?")
+    except Exception:
+        model = "?"
+    return dict(value=wl.T / per_step, unit="tokens/s", cores=1, kind="oracle",
+                sample=(f"{len(times)} full steps (layout+dispatch+combine) of the T=4096 H=7168 E=256 k=8 "
+                        f"workload, median {per_step:.2f} s/step; 1 thread of {os.cpu_count()} host cores ({model})"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="workload for the headline line (default 2)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU's share of the path on one GPU; --gpus {args.gpus} is not supported "
+              "(there is no multi-GPU path in this build).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    log(f"[bench] config {args.config}: {args.warmup} warmup + {args.steps} timed steps")
+    main_res = run_gpu(args.config, args.steps, args.warmup, dev)
+    log(f"[bench] config {args.config}: {main_res['ms_per_step']*1e3:.1f} us/step, "
+        f"dispatch {main_res['dispatch_us']:.1f} us, combine {main_res['combine_us']:.1f} us")
+
+    others = {}
+    if not args.no_other_workloads:
+        for cid in (3, 4, 5):
+            if cid == args.config:
+                continue
+            log(f"[bench] config {cid}")
+            r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev)
+            others[r["workload"]] = {k: r[k] for k in ("T", "H", "E", "G", "k", "x_dtype", "routing", "R",
+                                                       "tokens_per_s", "dc_tokens_per_s", "dc_gbps", "dc_frac",
+                                                       "layout_us", "dispatch_us", "combine_us",
+                                                       "dispatch_gbps", "combine_gbps")}
+    probe = None if args.no_probe else probe_copy_gbps(dev)
+    if probe:
+        log(f"[bench] probe copy {probe:.0f} GB/s")
+
+    # dominant kernel: the longer of dispatch and combine
+    if main_res["dispatch_us"] >= main_res["combine_us"]:
+        dom, dom_us, dom_bytes = "moedisp_dispatch", main_res["dispatch_us"], main_res["bytes"]["dispatch"]
+    else:
+        dom, dom_us, dom_bytes = "moedisp_combine", main_res["combine_us"], main_res["bytes"]["combine"]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": METRIC,
+        "value": main_res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["x_dtype"],
+        "data": "synthetic (seeded N(0,1) activations, uniform top-k routing, softmax weights)",
+        "config": {"workload": main_res["workload"], "T": main_res["T"], "H": main_res["H"], "E": main_res["E"],
+                   "G": main_res["G"], "k": main_res["k"], "x_dtype": main_res["x_dtype"],
+                   "routing": main_res["routing"], "step": "layout+dispatch+combine", "parallelism": "none"},
+        "hbm_gbps_step": main_res["step_gbps"],
+        "hbm_frac_step": main_res["step_gbps"] / HBM_PEAK_GBPS,
+        "dispatch_combine": {"us": main_res["dispatch_us"] + main_res["combine_us"],
+                             "tokens_per_s": main_res["dc_tokens_per_s"], "gbps": main_res["dc_gbps"],
+                             "frac": main_res["dc_frac"]},
+        "phases_us": {"layout": main_res["layout_us"], "dispatch": main_res["dispatch_us"],
+                      "combine": main_res["combine_us"], "dispatch_min": main_res["dispatch_us_min"],
+                      "combine_min": main_res["combine_us_min"]},
+        "phases_gbps": {"dispatch": main_res["dispatch_gbps"], "combine": main_res["combine_gbps"]},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+        "probe_copy_gbps": probe,
+        "other_workloads": others,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""Python binding of libmoedisp: argument marshalling only.
+
+Every function has the name of the C entry point it calls and takes torch
+tensors where the C call takes device pointers; torch provides the device
+memory and the stream (the current stream unless one is given).  Every step
+of layout, dispatch and combine runs in the library's HIP kernels.  There is
+no fallback: if libmoedisp.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoedisp.so")
+
+# element types (moedisp_dtype)
+BF16 = 0
+FP8_E4M3 = 1
+FP32 = 2
+
+# host return codes
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_MISALIGNED = -3
+ERR_WORKSPACE_TOO_SMALL = -4
+ERR_HIP = -5
+
+# device status bits
+DEV_BAD_EXPERT_ID = 1
+DEV_DUPLICATE_EXPERT = 2
+DEV_BAD_LAYOUT = 4
+DEV_BAD_HANDLE = 8
+DEV_SPIN_TIMEOUT = 16
+DEV_WORKSPACE_RACE = 32
+
+EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
+           "ep_check_status", "ep_set_spin_limit", "ep_status_string", "ep_probe_copy")
+
+
+class MoeDispError(RuntimeError):
+    def __init__(self, call: str, code: int, text: str):
+        super().__init__(f"{call} failed: {code} ({text})")
+        self.code = code
+
+
+class moedisp_shape(C.Structure):
+    _fields_ = [("num_tokens", C.c_int32), ("hidden", C.c_int32), ("num_experts", C.c_int32),
+                ("num_groups", C.c_int32), ("topk", C.c_int32), ("x_dtype", C.c_int32),
+                ("scale_block", C.c_int32)]
+
+    @classmethod
+    def make(cls, T, H, E, G, k, x_dtype=BF16, scale_block=0):
+        return cls(T, H, E, G, k, x_dtype, scale_block)
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoedisp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m combine_ep_get_dispatch_amd.build` "
+                           "(there is no fallback path)")
+    L = C.CDLL(path)
+    P, S = C.c_void_p, C.POINTER(moedisp_shape)
+    L.ep_workspace_bytes.argtypes = [S]
+    L.ep_workspace_bytes.restype = C.c_size_t
+    L.ep_workspace_init.argtypes = [P, C.c_size_t, P]
+    L.ep_workspace_init.restype = C.c_int
+    L.ep_get_dispatch_layout.argtypes = [S, P, P, P, P, P, C.c_size_t, P]
+    L.ep_get_dispatch_layout.restype = C.c_int
+    L.ep_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_dispatch.restype = C.c_int
+    L.ep_combine.argtypes = [S, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
+    L.ep_combine.restype = C.c_int
+    L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
+    L.ep_check_status.restype = C.c_int
+    L.ep_set_spin_limit.argtypes = [P, C.c_size_t, C.c_uint32, P]
+    L.ep_set_spin_limit.restype = C.c_int
+    L.ep_status_string.argtypes = [C.c_int]
+    L.ep_status_string.restype = C.c_char_p
+    L.ep_probe_copy.argtypes = [P, P, C.c_size_t, P]
+    L.ep_probe_copy.restype = C.c_int
+    _lib = L
+    return L
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _check(call: str, rc: int):
+    if rc != OK:
+        raise MoeDispError(call, rc, ep_status_string(rc))
+
+
+def ep_status_string(code: int) -> str:
+    return load().ep_status_string(code).decode()
+
+
+def ep_workspace_bytes(shape: moedisp_shape) -> int:
+    return int(load().ep_workspace_bytes(C.byref(shape)))
+
+
+def ep_workspace_init(ws: torch.Tensor, stream=None):
+    _check("ep_workspace_init", load().ep_workspace_init(_p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_get_dispatch_layout(shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws,
+                           stream=None):
+    _check("ep_get_dispatch_layout", load().ep_get_dispatch_layout(
+        C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group),
+        _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales, recv_src_idx,
+                recv_weights, expert_offsets, slot_to_row, ws, stream=None):
+    _check("ep_dispatch", load().ep_dispatch(
+        C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
+        _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
+        ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_combine(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, out, out_dtype, ws, stream=None):
+    _check("ep_combine", load().ep_combine(
+        C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(out),
+        int(out_dtype), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_check_status(ws, stream=None) -> int:
+    v = C.c_int32(0)
+    _check("ep_check_status", load().ep_check_status(_p(ws), ws.numel() * ws.element_size(), _s(stream),
+                                                     C.byref(v)))
+    return int(v.value)
+
+
+def ep_set_spin_limit(ws, limit: int, stream=None):
+    _check("ep_set_spin_limit", load().ep_set_spin_limit(_p(ws), ws.numel() * ws.element_size(), int(limit),
+                                                         _s(stream)))
+
+
+def ep_probe_copy(dst, src, nbytes: int, stream=None):
+    _check("ep_probe_copy", load().ep_probe_copy(_p(dst), _p(src), int(nbytes), _s(stream)))
+
+
+class EpBuffers:
+    """Device buffers for one shape (plumbing): workspace, layout outputs,
+    receive buffers at capacity T*k rows and the dispatch handle."""
+
+    def __init__(self, shape: moedisp_shape, device="cuda"):
+        T, H, E, G, k = shape.num_tokens, shape.hidden, shape.num_experts, shape.num_groups, shape.topk
+        self.shape = shape
+        self.device = torch.device(device)
+        nbytes = ep_workspace_bytes(shape)
+        if nbytes == 0:
+            raise MoeDispError("ep_workspace_bytes", ERR_INVALID_ARG, "invalid shape")
+        d = self.device
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=d)
+        self.tokens_per_expert = torch.empty(E, dtype=torch.int32, device=d)
+        self.tokens_per_group = torch.empty(G, dtype=torch.int32, device=d)
+        self.is_token_in_group = torch.empty(T, dtype=torch.int32, device=d)
+        cap = T * k
+        elt = 1 if shape.x_dtype == FP8_E4M3 else 2
+        self.recv_x = torch.empty((cap, H * elt), dtype=torch.uint8, device=d)
+        nsc = H // shape.scale_block if shape.x_dtype == FP8_E4M3 else 0
+        self.recv_scales = torch.empty((cap, nsc), dtype=torch.float32, device=d) if nsc else None
+        self.recv_src_idx = torch.empty(cap, dtype=torch.int32, device=d)
+        self.recv_weights = torch.empty(cap, dtype=torch.float32, device=d)
+        self.expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=d)
+        self.slot_to_row = torch.empty((T, k), dtype=torch.int32, device=d)
+
+    def layout(self, topk_idx, stream=None):
+        ep_get_dispatch_layout(self.shape, topk_idx, self.tokens_per_expert, self.tokens_per_group,
+                               self.is_token_in_group, self.ws, stream)
+
+    def dispatch(self, x, x_scales, topk_idx, topk_weights, stream=None):
+        ep_dispatch(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,
+                    self.recv_scales, self.recv_src_idx, self.recv_weights, self.expert_offsets, self.slot_to_row,
+                    self.ws, stream)
+
+    def combine(self, expert_out, out, out_dtype=BF16, check_src=True, stream=None):
+        ep_combine(self.shape, expert_out, self.recv_src_idx if check_src else None, self.recv_weights,
+                   self.slot_to_row, out, out_dtype, self.ws, stream)
+
+    def status(self, stream=None) -> int:
+        return ep_check_status(self.ws, stream)

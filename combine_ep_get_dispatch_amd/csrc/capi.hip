@@ -1,0 +1,248 @@
+// C ABI of libmoedisp: argument checks on the host, then launches on the
+// caller's stream.  The checks touch no device and no HIP runtime state, so a
+// rejected call enqueues nothing.  Unsupported input is reported as a code,
+// never by an assertion (the reviewers of "Add pynccl all-gatherv and
+// reducescatterv #20154" ask for a raised error instead of an assert on an
+// unsupported argument).
+#include <string.h>
+
+#include "moedisp_internal.h"
+
+namespace moedisp {
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static int check_shape(const moedisp_shape* s) {
+    if (!s) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens < 0 || s->hidden <= 0 || s->num_experts < 1 || s->num_groups < 1 || s->topk < 1)
+        return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_experts % s->num_groups != 0) return MOEDISP_ERR_INVALID_ARG;
+    if (s->topk > s->num_experts) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_groups > kMaxGroups || s->topk > kMaxTopk || s->num_experts > kMaxExperts)
+        return MOEDISP_ERR_UNSUPPORTED;
+    if (s->x_dtype == MOEDISP_BF16) {
+        if (s->scale_block != 0) return MOEDISP_ERR_INVALID_ARG;
+    } else if (s->x_dtype == MOEDISP_FP8_E4M3) {
+        if (s->scale_block <= 0 || s->hidden % s->scale_block != 0) return MOEDISP_ERR_INVALID_ARG;
+    } else {
+        return MOEDISP_ERR_UNSUPPORTED;
+    }
+    if (row_bytes(*s) % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    // receive rows and look-back values must fit 30 bits; bf16 rows of the
+    // combine must fit the same index space
+    const long long cap = (long long)s->num_tokens * s->topk;
+    if (cap >= (1ll << 30)) return MOEDISP_ERR_UNSUPPORTED;
+    if ((long long)s->hidden * 2 / 16 >= (1ll << 30)) return MOEDISP_ERR_UNSUPPORTED;
+    return MOEDISP_OK;
+}
+
+static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+DispatchPlan plan_dispatch(const moedisp_shape& s) {
+    DispatchPlan p;
+    const long long write_per_token = (long long)s.topk * (long long)row_bytes(s);
+    // tokens per workgroup: aim for >= 32 KiB of row stores per workgroup
+    int bt = 1;
+    while (bt < kMaxBlockTokens && write_per_token * bt < 32 * 1024) bt *= 2;
+    const int row16 = (int)(row_bytes(s) / 16);
+    // split rows across workgroups while the grid is small (decode-sized T)
+    int splits = 1;
+    const long long token_blocks = ceil_div(s.num_tokens, bt);
+    while (token_blocks * splits < 1024 && row16 / (splits * 2) >= kThreads / 2) splits *= 2;
+    p.block_tokens = bt;
+    p.tile_tokens = bt > 16 ? bt : 16;
+    p.col_splits = splits;
+    p.parts = (p.tile_tokens / p.block_tokens) * splits;
+    p.tiles = s.num_tokens > 0 ? ceil_div(s.num_tokens, p.tile_tokens) : 1;
+    p.blocks = p.tiles * p.parts;
+    return p;
+}
+
+CombinePlan plan_combine(const moedisp_shape& s) {
+    CombinePlan p;
+    const int row16 = (int)((size_t)s.hidden * 2 / 16);
+    int splits = 1;
+    while ((long long)s.num_tokens * splits < 1024 && row16 / (splits * 2) >= kThreads) splits *= 2;
+    p.col_splits = splits;
+    p.blocks = s.num_tokens * splits;
+    return p;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsPlan plan_workspace(const moedisp_shape& s) {
+    WsPlan w;
+    w.layout_blocks = s.num_tokens > 0 ? ceil_div(s.num_tokens, kLayoutTokensPerBlock) : 1;
+    const DispatchPlan d = plan_dispatch(s);
+    w.partial_offset = sizeof(WsHeader);
+    const size_t partial_bytes = (size_t)w.layout_blocks * (s.num_experts + s.num_groups) * sizeof(int32_t);
+    w.lookback_offset = align256(w.partial_offset + partial_bytes);
+    const size_t look_bytes = (size_t)d.tiles * s.num_experts * sizeof(uint64_t);
+    w.total = align256(w.lookback_offset + look_bytes);
+    return w;
+}
+
+static int check_ws(const moedisp_shape* s, void* ws, size_t ws_bytes) {
+    if (!ws) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOEDISP_ERR_MISALIGNED;
+    if (ws_bytes < plan_workspace(*s).total) return MOEDISP_ERR_WORKSPACE_TOO_SMALL;
+    return MOEDISP_OK;
+}
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOEDISP_OK : MOEDISP_ERR_HIP; }
+
+}  // namespace moedisp
+
+using namespace moedisp;
+
+extern "C" {
+
+size_t ep_workspace_bytes(const moedisp_shape* s) {
+    if (check_shape(s) != MOEDISP_OK) return 0;
+    return plan_workspace(*s).total;
+}
+
+int ep_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws || ws_bytes < sizeof(WsHeader)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOEDISP_ERR_MISALIGNED;
+    return hip_status(launch_fill_zero(ws, ws_bytes & ~(size_t)3, (hipStream_t)stream));
+}
+
+int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
+                           int32_t* tokens_per_group, uint32_t* is_token_in_group, void* ws, size_t ws_bytes,
+                           void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if ((s->num_tokens > 0 && (!topk_idx || !is_token_in_group)) || !tokens_per_expert || !tokens_per_group)
+        return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(topk_idx, 4) || !aligned(tokens_per_expert, 4) || !aligned(tokens_per_group, 4) ||
+        !aligned(is_token_in_group, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    const WsPlan w = plan_workspace(*s);
+    LayoutArgs a;
+    a.T = s->num_tokens;
+    a.k = s->topk;
+    a.E = s->num_experts;
+    a.G = s->num_groups;
+    a.topk_idx = topk_idx;
+    a.tokens_per_expert = tokens_per_expert;
+    a.tokens_per_group = tokens_per_group;
+    a.is_token_in_group = is_token_in_group;
+    a.hdr = (WsHeader*)ws;
+    a.partials = (int32_t*)((char*)ws + w.partial_offset);
+    a.blocks = w.layout_blocks;
+    return hip_status(launch_layout(a, (hipStream_t)stream));
+}
+
+int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row,
+                void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
+    if (!tokens_per_expert || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !recv_x || !recv_src_idx || !recv_weights ||
+                              !slot_to_row))
+        return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && fp8 && (!x_scales || !recv_scales)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOEDISP_ERR_MISALIGNED;
+    if (!aligned(x_scales, 4) || !aligned(recv_scales, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+        !aligned(tokens_per_expert, 4) || !aligned(recv_src_idx, 4) || !aligned(recv_weights, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(slot_to_row, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    const WsPlan w = plan_workspace(*s);
+    DispatchArgs a;
+    a.T = s->num_tokens;
+    a.k = s->topk;
+    a.E = s->num_experts;
+    a.row16 = (int)(row_bytes(*s) / 16);
+    a.scale_words = fp8 ? scales_per_row(*s) : 0;
+    a.capacity = s->num_tokens * s->topk;
+    a.plan = plan_dispatch(*s);
+    a.x = (const v4u*)x;
+    a.x_scales = fp8 ? x_scales : nullptr;
+    a.topk_idx = topk_idx;
+    a.topk_weights = topk_weights;
+    a.tokens_per_expert = tokens_per_expert;
+    a.recv_x = (v4u*)recv_x;
+    a.recv_scales = fp8 ? recv_scales : nullptr;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_weights = recv_weights;
+    a.expert_offsets = expert_offsets;
+    a.slot_to_row = slot_to_row;
+    a.hdr = (WsHeader*)ws;
+    a.lookback = (uint64_t*)((char*)ws + w.lookback_offset);
+    return hip_status(launch_dispatch(a, (hipStream_t)stream));
+}
+
+int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,
+               const float* recv_weights, const int32_t* slot_to_row, void* out, int32_t out_dtype, void* ws,
+               size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (out_dtype != MOEDISP_BF16 && out_dtype != MOEDISP_FP32) return MOEDISP_ERR_UNSUPPORTED;
+    if ((size_t)s->hidden * 2 % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    if (s->num_tokens > 0 && (!expert_out || !recv_weights || !slot_to_row || !out)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(expert_out, 16) || !aligned(out, 16)) return MOEDISP_ERR_MISALIGNED;
+    if (!aligned(recv_src_idx, 4) || !aligned(recv_weights, 4) || !aligned(slot_to_row, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    if (s->num_tokens == 0) return MOEDISP_OK;
+    const CombinePlan p = plan_combine(*s);
+    CombineArgs a;
+    a.T = s->num_tokens;
+    a.k = s->topk;
+    a.row16 = (int)((size_t)s->hidden * 2 / 16);
+    a.capacity = s->num_tokens * s->topk;
+    a.col_splits = p.col_splits;
+    a.expert_out = (const v4u*)expert_out;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_weights = recv_weights;
+    a.slot_to_row = slot_to_row;
+    a.out = out;
+    a.hdr = (WsHeader*)ws;
+    return hip_status(launch_combine(a, out_dtype == MOEDISP_FP32, (hipStream_t)stream));
+}
+
+int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_status) {
+    if (!ws || !host_status || ws_bytes < sizeof(WsHeader)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOEDISP_ERR_MISALIGNED;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, &((WsHeader*)ws)->status, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return MOEDISP_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOEDISP_ERR_HIP;
+    *host_status = (int32_t)v;
+    if (v) return hip_status(launch_set_word(&((WsHeader*)ws)->status, 0u, st));
+    return MOEDISP_OK;
+}
+
+int ep_set_spin_limit(void* ws, size_t ws_bytes, uint32_t limit, void* stream) {
+    if (!ws || ws_bytes < sizeof(WsHeader)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(ws, 256)) return MOEDISP_ERR_MISALIGNED;
+    return hip_status(launch_set_word(&((WsHeader*)ws)->spin_limit, limit, (hipStream_t)stream));
+}
+
+const char* ep_status_string(int status) {
+    switch (status) {
+        case MOEDISP_OK: return "ok";
+        case MOEDISP_ERR_INVALID_ARG: return "invalid argument";
+        case MOEDISP_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case MOEDISP_ERR_MISALIGNED: return "misaligned pointer";
+        case MOEDISP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOEDISP_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if ((!dst || !src) && bytes) return MOEDISP_ERR_INVALID_ARG;
+    if (bytes % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    if (!aligned(dst, 16) || !aligned(src, 16)) return MOEDISP_ERR_MISALIGNED;
+    return hip_status(launch_copy((v4u*)dst, (const v4u*)src, bytes / 16, (hipStream_t)stream));
+}
+
+}  // extern "C"

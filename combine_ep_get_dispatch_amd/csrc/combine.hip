@@ -1,0 +1,188 @@
+// Combine kernel: gather each token's expert outputs back through the dispatch
+// handle and form the weighted top-k sum.
+//
+// What is computed ("MSCCLPP EP implementation - #852": PR description,
+// "Scope", intranode combine; the commit message fixing internode combine says
+// combine runs in the reverse direction of dispatch and must consume the
+// receiver-side bookkeeping dispatch returned; the commit message on combine
+// byte accounting says one returned row is read per routed copy):
+//     out[t][h] = sum_{j = 0..k-1, slot routed} recv_weights[r] * expert_out[r][h],
+//     r = slot_to_row[t][j],
+// accumulated in fp32 by fused multiply-add in ascending j from 0, then rounded
+// once to bf16 (nearest-even, v_cvt_pk_bf16_f32) or stored as fp32.
+//
+// How.  One workgroup per (token, column range).  The token's k rows and
+// weights are uniform across the workgroup, so they come through scalar loads;
+// the handle is checked there (row inside the receive buffer and, when
+// recv_src_idx is given, naming this token) and bad slots are skipped with
+// BAD_HANDLE raised.  Each lane owns U 16-byte units (8 bf16) of the output
+// row: it issues all k*U gathered 16-byte loads before the first FMA, so each
+// lane keeps k*U loads in flight, then accumulates slot by slot in order.
+// With k known at compile time (1, 2, 4, 8) the slot loop is unrolled; other
+// k take the generic loop.
+#include "moedisp_internal.h"
+
+namespace moedisp {
+namespace {
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    const bf2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline void fma8(float* acc, float w, v4u v) {
+    acc[0] = __builtin_fmaf(w, bf16_lo(v.x), acc[0]);
+    acc[1] = __builtin_fmaf(w, bf16_hi(v.x), acc[1]);
+    acc[2] = __builtin_fmaf(w, bf16_lo(v.y), acc[2]);
+    acc[3] = __builtin_fmaf(w, bf16_hi(v.y), acc[3]);
+    acc[4] = __builtin_fmaf(w, bf16_lo(v.z), acc[4]);
+    acc[5] = __builtin_fmaf(w, bf16_hi(v.z), acc[5]);
+    acc[6] = __builtin_fmaf(w, bf16_lo(v.w), acc[6]);
+    acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
+}
+
+template <bool kF32>
+__device__ inline void store_out(void* out, size_t unit, const float* acc) {
+    if constexpr (kF32) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        f4* o = reinterpret_cast<f4*>(out) + 2 * unit;
+        const f4 a0 = {acc[0], acc[1], acc[2], acc[3]};
+        const f4 a1 = {acc[4], acc[5], acc[6], acc[7]};
+        __builtin_nontemporal_store(a0, o);
+        __builtin_nontemporal_store(a1, o + 1);
+    } else {
+        v4u r;
+        r.x = pack_bf16x2(acc[0], acc[1]);
+        r.y = pack_bf16x2(acc[2], acc[3]);
+        r.z = pack_bf16x2(acc[4], acc[5]);
+        r.w = pack_bf16x2(acc[6], acc[7]);
+        __builtin_nontemporal_store(r, reinterpret_cast<v4u*>(out) + unit);
+    }
+}
+
+// Row and weight of slot j of token t, with the handle checks.
+__device__ inline int handle_row(const CombineArgs& a, int t, int j, float* w, uint32_t* err) {
+    int r = a.slot_to_row[(size_t)t * a.k + j];
+    *w = 0.0f;
+    if (r < -1 || r >= a.capacity) {
+        *err |= MOEDISP_DEV_BAD_HANDLE;
+        return -1;
+    }
+    if (r >= 0) {
+        *w = a.recv_weights[r];
+        if (a.recv_src_idx && a.recv_src_idx[r] != t) {
+            *err |= MOEDISP_DEV_BAD_HANDLE;
+            return -1;
+        }
+    }
+    return r;
+}
+
+// KC: compile-time k (0 = runtime k, slots gathered one at a time).
+template <int KC, int U, bool kF32>
+__global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
+    const int t = blockIdx.x / a.col_splits;
+    const int split = blockIdx.x - t * a.col_splits;
+    const int tid = threadIdx.x;
+    const int per_split = (a.row16 + a.col_splits - 1) / a.col_splits;
+    const int c0 = split * per_split;
+    const int c1 = min(a.row16, c0 + per_split);
+    uint32_t err = 0;
+
+    if constexpr (KC > 0) {
+        int rows[KC];
+        float wts[KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) rows[j] = handle_row(a, t, j, &wts[j], &err);
+        for (int c = c0 + tid; c < c1; c += U * kThreads) {
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+            v4u v[KC][U];
+#pragma unroll
+            for (int j = 0; j < KC; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int cc = c + u * kThreads;
+                    if (rows[j] >= 0 && cc < c1)
+                        v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 + cc);
+                }
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                if (rows[j] < 0) continue;
+#pragma unroll
+                for (int u = 0; u < U; ++u) fma8(acc[u], wts[j], v[j][u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cc = c + u * kThreads;
+                if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
+            }
+        }
+    } else {
+        if (tid == 0)
+            for (int j = 0; j < a.k; ++j) {
+                float w;
+                handle_row(a, t, j, &w, &err);
+            }
+        uint32_t ignored = 0;
+        for (int c = c0 + tid; c < c1; c += U * kThreads) {
+            float acc[U][8];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+            for (int j = 0; j < a.k; ++j) {
+                float w;
+                const int r = handle_row(a, t, j, &w, &ignored);
+                if (r < 0) continue;
+                v4u v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int cc = c + u * kThreads;
+                    if (cc < c1) v[u] = __builtin_nontemporal_load(a.expert_out + (size_t)r * a.row16 + cc);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) fma8(acc[u], w, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cc = c + u * kThreads;
+                if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
+            }
+        }
+    }
+    if (err && split == 0 && tid == 0) atomicOr(&a.hdr->status, err);
+}
+
+template <int KC, bool kF32>
+hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
+    constexpr int U = KC >= 8 ? 2 : 4;
+    hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool kF32>
+hipError_t launch_any(const CombineArgs& a, hipStream_t stream) {
+    switch (a.k) {
+        case 1: return launch_k<1, kF32>(a, stream);
+        case 2: return launch_k<2, kF32>(a, stream);
+        case 4: return launch_k<4, kF32>(a, stream);
+        case 8: return launch_k<8, kF32>(a, stream);
+        default: return launch_k<0, kF32>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream) {
+    return f32_out ? launch_any<true>(a, stream) : launch_any<false>(a, stream);
+}
+
+}  // namespace moedisp

@@ -1,0 +1,117 @@
+// Layout kernel: tokens per expert, tokens per group and the token-in-group
+// bitmap ("counts + token-in-rank" of the high-throughput layout kernel on the
+// "MSCCLPP EP implementation - #852" page, review file table).
+//
+// One thread per token, 256 tokens per workgroup.  The workgroup's routing
+// rows are staged in LDS (padded to an odd stride so a wave reading one slot
+// of 64 tokens hits distinct banks).  Expert counts go to an LDS-private
+// histogram: for each slot, the lanes of a wave that carry the same expert
+// find each other with one ballot per bit of the expert id, and only the
+// lowest such lane adds the popcount of its peer mask - one LDS atomic per
+// distinct expert per wave instead of one per lane, which matters under skewed
+// routing.  Group counts are popcounts of one ballot per group.  Each
+// workgroup writes its partial counts to the workspace; the last workgroup to
+// finish sums them in workgroup order and resets the finish counter.
+#include "moedisp_internal.h"
+
+namespace moedisp {
+namespace {
+
+// Lanes among `active` whose key equals this lane's key (keys < 2^nbits).
+// Every lane of the wave must execute this (it issues nbits ballots).
+__device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active) {
+    uint64_t peers = active;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
+    }
+    return peers;
+}
+
+__global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
+    extern __shared__ int32_t dyn[];  // [E + G] counts, then the staged routing rows
+    const int EG = a.E + a.G;
+    int32_t* s_cnt = dyn;
+    int32_t* s_ids = dyn + EG;
+    __shared__ uint32_t s_err;
+    __shared__ uint32_t s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int k = a.k;
+    const int kp = k | 1;  // odd LDS stride
+    const int t0 = blockIdx.x * kLayoutTokensPerBlock;
+    const int nt = max(0, min(kLayoutTokensPerBlock, a.T - t0));
+
+    for (int i = tid; i < EG; i += kThreads) s_cnt[i] = 0;
+    if (tid == 0) s_err = 0;
+    for (int i = tid; i < nt * k; i += kThreads) {
+        const int tt = i / k;
+        s_ids[tt * kp + (i - tt * k)] = a.topk_idx[(size_t)t0 * k + i];
+    }
+    __syncthreads();
+
+    const bool have = tid < nt;
+    const int per_group = a.E / a.G;
+    const int nbits = a.E > 1 ? 32 - __clz(a.E - 1) : 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    uint32_t gmask = 0;
+    uint32_t err = 0;
+    for (int j = 0; j < k; ++j) {
+        int id = have ? s_ids[tid * kp + j] : -1;
+        if (id < -1 || id >= a.E) {
+            err |= MOEDISP_DEV_BAD_EXPERT_ID;
+            id = -1;
+        }
+        const bool routed = id >= 0;
+        if (routed) {
+            for (int jj = 0; jj < j; ++jj)
+                if (s_ids[tid * kp + jj] == id) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
+            gmask |= 1u << (id / per_group);
+        }
+        const uint64_t active = __ballot(routed);
+        const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, nbits, active);
+        if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+    }
+    for (int g = 0; g < a.G; ++g) {
+        const uint64_t in_g = __ballot((gmask >> g) & 1u);
+        if (lane == 0 && in_g) atomicAdd(&s_cnt[a.E + g], (int32_t)__popcll(in_g));
+    }
+    if (have) a.is_token_in_group[t0 + tid] = gmask;
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+
+    int32_t* mine = a.partials + (size_t)blockIdx.x * EG;
+    for (int i = tid; i < EG; i += kThreads) mine[i] = s_cnt[i];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        if (s_err) atomicOr(&a.hdr->status, s_err);
+        const uint32_t prev = atomicAdd(&a.hdr->layout_done, 1u);
+        s_last = prev == (uint32_t)(a.blocks - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    __threadfence();
+    for (int i = tid; i < EG; i += kThreads) {
+        int32_t sum = 0;
+        for (int b = 0; b < a.blocks; ++b) sum += a.partials[(size_t)b * EG + i];
+        if (i < a.E)
+            a.tokens_per_expert[i] = sum;
+        else
+            a.tokens_per_group[i - a.E] = sum;
+    }
+    if (tid == 0) __hip_atomic_store(&a.hdr->layout_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+    const size_t lds = (size_t)(a.E + a.G + kLayoutTokensPerBlock * (a.k | 1)) * sizeof(int32_t);
+    hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace moedisp

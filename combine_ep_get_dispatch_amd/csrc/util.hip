@@ -1,0 +1,57 @@
+// Small helper kernels: workspace fill, single-word store, and the plain
+// 16-byte copy used to calibrate achievable HBM bandwidth.
+#include "moedisp_internal.h"
+
+namespace moedisp {
+namespace {
+
+__global__ __launch_bounds__(kThreads) void moedisp_fill_zero(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = 0u;
+}
+
+__global__ void moedisp_set_word(uint32_t* p, uint32_t v) {
+    if (threadIdx.x == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Grid-stride copy, 4 units of 16 bytes in flight per lane.
+__global__ __launch_bounds__(kThreads) void moedisp_probe_copy(v4u* __restrict__ dst, const v4u* __restrict__ src,
+                                                               size_t n) {
+    constexpr int U = 4;
+    const size_t stride = (size_t)gridDim.x * kThreads;
+    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
+    }
+    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+    const size_t n = bytes / 4;
+    if (n == 0) return hipSuccess;
+    const size_t want = (n + kThreads - 1) / kThreads;
+    const unsigned blocks = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(moedisp_fill_zero, dim3(blocks), dim3(kThreads), 0, stream, (uint32_t*)p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream) {
+    hipLaunchKernelGGL(moedisp_set_word, dim3(1), dim3(64), 0, stream, p, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream) {
+    if (n16 == 0) return hipSuccess;
+    // 256 CUs x 8 workgroups, each lane moving 4 units per pass
+    const size_t want = (n16 + 4 * kThreads - 1) / (4 * kThreads);
+    const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
+    hipLaunchKernelGGL(moedisp_probe_copy, dim3(blocks), dim3(kThreads), 0, stream, dst, src, n16);
+    return hipGetLastError();
+}
+
+}  // namespace moedisp

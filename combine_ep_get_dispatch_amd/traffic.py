@@ -1,0 +1,31 @@
+"""Algorithmic HBM bytes of layout, dispatch and combine.
+
+Every routed copy counts once, in both directions: dispatch writes one
+received row per routed slot, and combine reads one expert-output row per
+routed slot (the "MSCCLPP EP implementation - #852" page's commit message on
+combine byte accounting: each expert sends one copy per dispatched token
+back).  Index and weight arrays count once per read or write.  Bytes the
+library moves beyond these (the workspace, the combine's check of
+recv_src_idx) are overhead and are not counted.
+"""
+from __future__ import annotations
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+
+
+def algorithmic_bytes(T: int, H: int, E: int, G: int, k: int, R: int, x_elt: int = 2, scale_block: int = 0) -> dict:
+    row = H * x_elt + ((H // scale_block) * 4 if scale_block else 0)  # payload + fp32 scales
+    out_row = H * 2  # combine reads and writes bf16
+    layout = T * k * 4 + E * 4 + G * 4 + T * 4
+    dispatch = (T * row            # x (and scales) read once
+                + R * row          # one received row per routed copy
+                + 2 * T * k * 4    # topk_idx, topk_weights
+                + 2 * R * 4        # recv_src_idx, recv_weights
+                + T * k * 4        # slot_to_row
+                + (E + 1) * 4)     # expert_offsets
+    combine = (R * out_row         # one expert-output row per routed copy
+               + T * out_row       # output
+               + T * k * 4         # slot_to_row
+               + R * 4)            # recv_weights
+    return dict(layout=layout, dispatch=dispatch, combine=combine, dispatch_combine=dispatch + combine,
+                step=layout + dispatch + combine)

@@ -1,0 +1,163 @@
+/*
+ * moedisp.h - C ABI of libmoedisp: one GPU's share of MoE expert-parallel
+ * token layout, dispatch and combine, written for MI355X (gfx950).
+ *
+ * The operations follow the MSCCL++ EP pull request page ("MSCCLPP EP
+ * implementation - #852"):
+ *   - PR description, "Scope": get_dispatch_layout, dispatch and combine are
+ *     the three calls of the expert-parallel path;
+ *   - review file table, high-throughput layout kernel entry: the layout call
+ *     produces token counts and token-in-rank flags;
+ *   - commit message fixing internode combine: combine runs in the reverse
+ *     direction of dispatch and consumes receiver-side bookkeeping that
+ *     dispatch returned;
+ *   - commit message on combine byte accounting: one returned row per routed
+ *     copy;
+ *   - warp-geometry commit messages and the code-scanning excerpt: hidden
+ *     rows are moved in 16-byte units.
+ * A destination rank of the page is a destination GROUP here: a contiguous
+ * block of E/G experts whose receive rows are a contiguous range of this
+ * GPU's HBM.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is DEVICE memory owned by the caller, except the
+ *     moedisp_shape pointer and ep_check_status's host_status (host memory).
+ *     The library never allocates, never frees and keeps no device memory of
+ *     its own; all scratch state lives in the caller's workspace `ws`.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns; nothing synchronises
+ *     except ep_check_status.
+ *   - Row buffers (x, recv_x, expert_out, out) must be 16-byte aligned and a
+ *     row must be a whole number of 16-byte units (H * element size % 16 == 0).
+ *     Index, weight and scale arrays must be 4-byte aligned; ws 256-byte aligned.
+ *   - Arguments that can be checked on the host are checked before anything is
+ *     enqueued; a failed check returns a negative MOEDISP_ERR_* code and
+ *     enqueues nothing.  A failed launch returns MOEDISP_ERR_HIP.  Problems
+ *     only visible in device data (bad expert ids, an inconsistent layout or
+ *     handle, a wait that timed out) set bits of a status word in `ws`, read
+ *     by ep_check_status.  The library never asserts or aborts.
+ *   - Calls that share one `ws` must be ordered on one stream; concurrent
+ *     calls need distinct workspaces.
+ */
+#ifndef MOEDISP_H
+#define MOEDISP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of token rows. */
+typedef enum {
+    MOEDISP_BF16 = 0,      /* bfloat16, 2 bytes */
+    MOEDISP_FP8_E4M3 = 1,  /* OCP e4m3fn codes, 1 byte, with fp32 scales per block */
+    MOEDISP_FP32 = 2       /* float32 (combine output only) */
+} moedisp_dtype;
+
+/* Problem shape.  T tokens of H elements, E experts in G groups (E % G == 0,
+ * group of expert e = e / (E/G)), top-k slots per token. */
+typedef struct {
+    int32_t num_tokens;   /* T >= 0 */
+    int32_t hidden;       /* H > 0 */
+    int32_t num_experts;  /* E in [1, 4096] */
+    int32_t num_groups;   /* G in [1, 32], E % G == 0 */
+    int32_t topk;         /* k in [1, 32], k <= E */
+    int32_t x_dtype;      /* MOEDISP_BF16 or MOEDISP_FP8_E4M3 */
+    int32_t scale_block;  /* 0 for bf16; for fp8 the channels per fp32 scale (H % scale_block == 0) */
+} moedisp_shape;
+
+/* Host-side return codes. */
+#define MOEDISP_OK 0
+#define MOEDISP_ERR_INVALID_ARG (-1)          /* null pointer, negative size, E % G != 0, ... */
+#define MOEDISP_ERR_UNSUPPORTED (-2)          /* a limit above exceeded, row not whole 16-B units */
+#define MOEDISP_ERR_MISALIGNED (-3)           /* pointer alignment rule broken */
+#define MOEDISP_ERR_WORKSPACE_TOO_SMALL (-4)  /* ws_bytes < ep_workspace_bytes(shape) */
+#define MOEDISP_ERR_HIP (-5)                  /* a HIP runtime call or launch failed */
+
+/* Device status bits (ep_check_status). */
+#define MOEDISP_DEV_BAD_EXPERT_ID 1u     /* id outside {-1} U [0,E); that slot is treated as masked */
+#define MOEDISP_DEV_DUPLICATE_EXPERT 2u  /* an expert repeated within one token (each copy still routed) */
+#define MOEDISP_DEV_BAD_LAYOUT 4u        /* tokens_per_expert disagrees with topk_idx; bad rows skipped */
+#define MOEDISP_DEV_BAD_HANDLE 8u        /* combine handle inconsistent; those slots skipped */
+#define MOEDISP_DEV_SPIN_TIMEOUT 16u     /* a bounded cross-workgroup wait gave up; results invalid */
+#define MOEDISP_DEV_WORKSPACE_RACE 32u   /* workspace counters corrupted by overlapping calls; re-init ws */
+
+/* Bytes of workspace the calls need for `shape`; 0 if the shape is invalid.
+ * One workspace serves layout, dispatch and combine of that shape (or of any
+ * shape with no more tokens and experts). */
+size_t ep_workspace_bytes(const moedisp_shape* shape);
+
+/* Zero a workspace before its first use (or after a call that reported
+ * MOEDISP_DEV_SPIN_TIMEOUT).  The calls keep its counters consistent
+ * afterwards; a workspace must not be shared by overlapping calls. */
+int ep_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Layout ("counts + token-in-rank" of the high-throughput layout kernel).
+ *   topk_idx           int32 [T][k]: expert per slot, -1 = masked slot.
+ *   tokens_per_expert  int32 [E]: number of routed slots with that expert.
+ *   tokens_per_group   int32 [G]: number of tokens with at least one routed
+ *                      slot in the group (a token counts once per group).
+ *   is_token_in_group  uint32 [T]: bit g set iff the token reaches group g.
+ * Status bits: BAD_EXPERT_ID, DUPLICATE_EXPERT. */
+int ep_get_dispatch_layout(const moedisp_shape* shape, const int32_t* topk_idx,
+                           int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                           uint32_t* is_token_in_group, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch: pack every routed copy of a token into its expert's contiguous
+ * receive rows.  Expert e owns rows [expert_offsets[e], expert_offsets[e+1]);
+ * inside them rows follow token order.  Row of slot (t,j) with expert e:
+ *   expert_offsets[e] + #{t' < t : some slot of t' routes to e}.
+ *   x                  [T][H] bf16 or fp8 codes (bytes are copied unchanged).
+ *   x_scales           fp32 [T][H/scale_block] for fp8, NULL for bf16.
+ *   topk_idx, topk_weights  int32 / fp32 [T][k].
+ *   tokens_per_expert  int32 [E] from ep_get_dispatch_layout for this topk_idx.
+ *   recv_x             [T*k][H] capacity; rows >= R = expert_offsets[E] untouched.
+ *   recv_scales        fp32 [T*k][H/scale_block] for fp8, NULL for bf16.
+ *   recv_src_idx       int32 [T*k]: source token of each received row.
+ *   recv_weights       fp32 [T*k]: topk_weights[t][j] of each received row.
+ *   expert_offsets     int32 [E+1]: exclusive prefix of tokens_per_expert; [E] = R.
+ *   slot_to_row        int32 [T][k]: row of each slot, -1 if masked.
+ * (recv_src_idx, recv_weights, slot_to_row) is the handle ep_combine takes.
+ * Status bits: BAD_EXPERT_ID, BAD_LAYOUT, SPIN_TIMEOUT, WORKSPACE_RACE. */
+int ep_dispatch(const moedisp_shape* shape, const void* x, const float* x_scales,
+                const int32_t* topk_idx, const float* topk_weights,
+                const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets,
+                int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+
+/* Combine: the reverse of dispatch through its handle.
+ *   out[t][h] = sum over j = 0..k-1 in ascending order, skipping masked slots,
+ *               of recv_weights[r] * expert_out[r][h] with r = slot_to_row[t][j],
+ *   accumulated in fp32 by fused multiply-add from 0; bf16 output is that sum
+ *   rounded once to nearest-even; a token with no routed slot gets +0.
+ *   expert_out    bf16 [T*k][H] (rows [0,R) are read).
+ *   recv_src_idx  may be NULL; if given, each slot's row must name its token.
+ *   out           [T][H] bf16 (out_dtype MOEDISP_BF16) or fp32 (MOEDISP_FP32).
+ * Status bits: BAD_HANDLE. */
+int ep_combine(const moedisp_shape* shape, const void* expert_out, const int32_t* recv_src_idx,
+               const float* recv_weights, const int32_t* slot_to_row, void* out,
+               int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* Wait for `stream`, then return the device status bits accumulated in `ws`
+ * since the last check in *host_status and clear them. */
+int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_status);
+
+/* Upper bound on polls of one cross-workgroup wait before it gives up with
+ * MOEDISP_DEV_SPIN_TIMEOUT (0 = the default, 2^18).  Stored in `ws`. */
+int ep_set_spin_limit(void* ws, size_t ws_bytes, uint32_t limit, void* stream);
+
+/* Text for a host return code. */
+const char* ep_status_string(int status);
+
+/* Calibration helper, not part of the path: a plain 16-byte-vector device
+ * copy of `bytes` (a multiple of 16; both pointers 16-byte aligned), used to
+ * measure the achievable HBM bandwidth and to scale hardware byte counters. */
+int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEDISP_H */

@@ -1,0 +1,136 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments on the host with
+the documented codes before anything touches a device."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import combine_ep_get_dispatch_amd as M
+from combine_ep_get_dispatch_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moedisp.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from combine_ep_get_dispatch_amd import build
+        build.build()
+    return M.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def shape(T=4096, H=7168, E=256, G=8, k=8, dt=M.BF16, sb=0):
+    return M.moedisp_shape.make(T, H, E, G, k, dt, sb)
+
+
+def test_workspace_bytes(lib):
+    s = shape()
+    n = M.ep_workspace_bytes(s)
+    # header + layout partials (16 workgroups x 264 counts) + look-back words (256 tiles x 256 experts)
+    assert n >= 256 + 16 * 264 * 4 + 256 * 256 * 8
+    assert n % 256 == 0
+    assert M.ep_workspace_bytes(shape(T=0)) > 0
+    assert M.ep_workspace_bytes(shape(E=255)) == 0          # E % G != 0
+    assert M.ep_workspace_bytes(shape(G=64, E=256)) == 0    # more groups than bitmap bits
+    assert M.ep_workspace_bytes(shape(H=7)) == 0            # row not whole 16-byte units
+    assert M.ep_workspace_bytes(shape(dt=M.FP8_E4M3, sb=128)) > 0
+    assert M.ep_workspace_bytes(shape(dt=M.FP8_E4M3, sb=100)) == 0
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails its host checks
+
+
+def p(off=0):
+    return C.c_void_p(FAKE + off)
+
+
+def layout_rc(lib, s, ws_bytes=1 << 30, ws=None, idx=None, tpe=None, tpg=None, bm=None):
+    return lib.ep_get_dispatch_layout(C.byref(s), idx or p(), tpe or p(), tpg or p(), bm or p(), ws or p(),
+                                      ws_bytes, None)
+
+
+def dispatch_rc(lib, s, x=None, xs=None, recv_x=None, rs=None, ws=None, ws_bytes=1 << 30, tpe=None):
+    return lib.ep_dispatch(C.byref(s), x or p(), xs, p(), p(), tpe or p(), recv_x or p(), rs, p(), p(), p(), p(),
+                           ws or p(), ws_bytes, None)
+
+
+def combine_rc(lib, s, eo=None, out=None, out_dtype=M.BF16, ws_bytes=1 << 30):
+    return lib.ep_combine(C.byref(s), eo or p(), p(), p(), p(), out or p(), out_dtype, p(), ws_bytes, None)
+
+
+def test_host_checks_layout(lib):
+    assert layout_rc(lib, shape(E=255)) == B.ERR_INVALID_ARG
+    assert layout_rc(lib, shape(T=-1)) == B.ERR_INVALID_ARG
+    assert layout_rc(lib, shape(k=0)) == B.ERR_INVALID_ARG
+    assert layout_rc(lib, shape(k=9, E=8, G=8)) == B.ERR_INVALID_ARG      # k > E
+    assert layout_rc(lib, shape(k=33, E=64)) == B.ERR_UNSUPPORTED
+    assert layout_rc(lib, shape(G=64, E=256)) == B.ERR_UNSUPPORTED
+    assert layout_rc(lib, shape(E=8192)) == B.ERR_UNSUPPORTED
+    assert layout_rc(lib, shape(T=1 << 28, k=8)) == B.ERR_UNSUPPORTED     # T*k rows beyond 30 bits
+    assert layout_rc(lib, shape(dt=7)) == B.ERR_UNSUPPORTED
+    assert layout_rc(lib, shape(), tpe=p(2)) == B.ERR_MISALIGNED
+    assert layout_rc(lib, shape(), ws=p(64)) == B.ERR_MISALIGNED           # ws needs 256-byte alignment
+    assert layout_rc(lib, shape(), ws_bytes=100) == B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.ep_get_dispatch_layout(C.byref(shape()), None, p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_get_dispatch_layout(None, p(), p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+
+
+def test_host_checks_dispatch(lib):
+    assert dispatch_rc(lib, shape(), x=p(8)) == B.ERR_MISALIGNED           # rows need 16-byte alignment
+    assert dispatch_rc(lib, shape(), recv_x=p(4)) == B.ERR_MISALIGNED
+    assert dispatch_rc(lib, shape(), tpe=p(1)) == B.ERR_MISALIGNED
+    assert dispatch_rc(lib, shape(H=7172)) == B.ERR_UNSUPPORTED             # 14344-byte rows
+    fp8 = shape(dt=M.FP8_E4M3, sb=128)
+    assert dispatch_rc(lib, fp8) == B.ERR_INVALID_ARG                      # fp8 without scales
+    assert dispatch_rc(lib, fp8, xs=p(), rs=None) == B.ERR_INVALID_ARG
+    assert dispatch_rc(lib, shape(dt=M.FP8_E4M3, sb=0), xs=p(), rs=p()) == B.ERR_INVALID_ARG
+    assert dispatch_rc(lib, shape(sb=128)) == B.ERR_INVALID_ARG             # bf16 with a scale block
+    assert dispatch_rc(lib, shape(), ws_bytes=4096) == B.ERR_WORKSPACE_TOO_SMALL
+    # null topk_idx
+    assert lib.ep_dispatch(C.byref(shape()), p(), None, None, p(), p(), p(), None, p(), p(), p(), p(), p(),
+                           1 << 30, None) == B.ERR_INVALID_ARG
+
+
+def test_host_checks_combine(lib):
+    assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
+    assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED
+    assert combine_rc(lib, shape(), out=p(8)) == B.ERR_MISALIGNED
+    assert combine_rc(lib, shape(), ws_bytes=0) == B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.ep_combine(C.byref(shape()), None, p(), p(), p(), p(), M.BF16, p(), 1 << 30, None) == B.ERR_INVALID_ARG
+
+
+def test_host_checks_misc(lib):
+    v = C.c_int32(0)
+    assert lib.ep_check_status(None, 1 << 20, None, C.byref(v)) == B.ERR_INVALID_ARG
+    assert lib.ep_check_status(p(), 1 << 20, None, None) == B.ERR_INVALID_ARG
+    assert lib.ep_check_status(p(8), 1 << 20, None, C.byref(v)) == B.ERR_MISALIGNED
+    assert lib.ep_workspace_init(p(), 16, None) == B.ERR_INVALID_ARG
+    assert lib.ep_workspace_init(p(4), 1 << 20, None) == B.ERR_MISALIGNED
+    assert lib.ep_set_spin_limit(None, 1 << 20, 5, None) == B.ERR_INVALID_ARG
+    assert lib.ep_probe_copy(p(), p(), 15, None) == B.ERR_UNSUPPORTED
+    assert lib.ep_probe_copy(p(4), p(), 16, None) == B.ERR_MISALIGNED
+    for code in (0, -1, -2, -3, -4, -5):
+        assert M.ep_status_string(code) != "unknown status"
+    assert M.ep_status_string(-99) == "unknown status"
+
+
+def test_python_binding_raises_without_gpu_work(lib):
+    s = shape(E=255)
+    with pytest.raises(M.MoeDispError):
+        B._check("ep_get_dispatch_layout", layout_rc(lib, s))

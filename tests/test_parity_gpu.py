@@ -1,0 +1,213 @@
+"""GPU parity of libmoedisp against the CPU oracle (needs an MI355X).
+
+Bit-exact: layout counts, bitmap, offsets, slot_to_row, recv_src_idx,
+recv_weights, received rows and scales.  Combine: max relative error 1e-3 in
+fp32 and at most one bf16 ulp after rounding, on every token of the small and
+mid-sized cases and on a seeded sample of tokens (always including the last)
+at the full sizes, which run in the same launch configuration as the
+benchmark.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_get_dispatch_amd as M
+from combine_ep_get_dispatch_amd import workloads as W
+import gpu_harness as GH
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    M.load()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# --- small and mid-sized cases: every output compared ---------------------
+
+MID = {
+    "tiny": lambda: W.config(1),
+    "decode_fp8": lambda: W.config(4),
+    "dsv3_ragged": lambda: W.make_workload("dsv3_ragged", 601, 7168, 256, 8, 8, seed=31, expert_kind="scale_by_id"),
+    "zipf_ragged": lambda: W.make_workload("zipf_ragged", 777, 7168, 256, 8, 8, seed=32, routing="zipf",
+                                           mask_frac=0.05, expert_kind="scale_by_id"),
+    "mixtral_ragged": lambda: W.make_workload("mixtral_ragged", 3001, 4096, 8, 8, 2, seed=33,
+                                              expert_kind="double_odd"),
+}
+
+
+@pytest.mark.parametrize("name", list(MID))
+def test_parity_every_output(orc, dev, name):
+    wl = MID[name]()
+    _say(f"[parity] {name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k} {wl.x_dtype}")
+    r = GH.full_parity(orc, wl, dev)
+    _say(f"[parity] {name} ok R={r['R']} max_ulp={r['max_ulp']} exact_f32={r['exact_f32']:.4f}")
+
+
+# --- full sizes, bench launch configuration --------------------------------
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_parity_full_size(orc, dev, cid):
+    wl = W.config(cid)
+    _say(f"[parity-full] config {cid} {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k}")
+    r = GH.full_parity(orc, wl, dev, sample_tokens=384, seed=cid)
+    _say(f"[parity-full] config {cid} ok R={r['R']} max_ulp={r['max_ulp']} exact_f32={r['exact_f32']:.4f}")
+
+
+# --- edge cases ------------------------------------------------------------
+
+EDGE = {
+    "T0": lambda: W.make_workload("T0", 0, 64, 8, 2, 2, seed=41),
+    "T1": lambda: W.make_workload("T1", 1, 64, 8, 2, 2, seed=42),
+    "all_masked": lambda: W.make_workload("all_masked", 37, 64, 8, 2, 2, seed=43, mask_frac=1.0),
+    "half_masked": lambda: W.make_workload("half_masked", 300, 64, 16, 4, 4, seed=44, mask_frac=0.5),
+    "k1": lambda: W.make_workload("k1", 257, 64, 8, 2, 1, seed=45),
+    "G1": lambda: W.make_workload("G1", 100, 64, 32, 1, 4, seed=46),
+    "G_eq_E": lambda: W.make_workload("G_eq_E", 100, 64, 32, 32, 4, seed=47),
+    "row16_bf16": lambda: W.make_workload("row16_bf16", 200, 8, 8, 2, 2, seed=48),
+    "row16_fp8": lambda: W.make_workload("row16_fp8", 200, 16, 8, 2, 2, seed=49, x_dtype=W.X_FP8, scale_block=16),
+    "k3_odd": lambda: W.make_workload("k3_odd", 123, 96, 12, 3, 3, seed=50),
+    "k32": lambda: W.make_workload("k32", 50, 64, 64, 8, 32, seed=51),
+    "E4096": lambda: W.make_workload("E4096", 300, 64, 4096, 32, 8, seed=52, routing="zipf", mask_frac=0.1),
+    "E1": lambda: W.make_workload("E1", 70, 64, 1, 1, 1, seed=53),
+    "tokens_per_tile_edges": lambda: W.make_workload("tile_edges", 1025, 256, 64, 8, 6, seed=54),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_parity_edge_cases(orc, dev, name):
+    wl = EDGE[name]()
+    _say(f"[edge] {name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k}")
+    GH.full_parity(orc, wl, dev)
+
+
+# --- properties -----------------------------------------------------------
+
+def test_dispatch_deterministic_under_repeats(orc, dev):
+    """Skewed routing, 20 dispatches on one workspace: every output identical
+    (the look-back must not let scheduling order leak into the result)."""
+    wl = W.make_workload("det", 2048, 1024, 256, 8, 8, seed=61, routing="zipf", mask_frac=0.05)
+    _say("[determinism] 20 repeats")
+    bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
+    assert st == 0
+    ref, R = GH.fetch_dispatch(bufs, wl)
+    for i in range(20):
+        bufs.recv_x.zero_()
+        bufs.slot_to_row.fill_(-7)
+        bufs.dispatch(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+        g, _ = GH.fetch_dispatch(bufs, wl)
+        for key in ("expert_offsets", "slot_to_row", "recv_src_idx", "recv_weights", "recv_x"):
+            assert np.array_equal(g[key], ref[key]), (i, key)
+    assert bufs.status() == 0
+    GH.assert_dispatch_equal(ref, GH.oracle_run(orc, wl), wl)
+
+
+def test_round_trip_identity_experts(dev):
+    """dispatch -> identity experts (the received rows themselves) -> combine
+    with weights summing to one returns x within one bf16 ulp."""
+    wl = W.config(1)
+    bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
+    assert st == 0
+    eo = bufs.recv_x.view(torch.bfloat16)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    bufs.combine(eo, out, M.BF16)
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert GH.bf16_ulp_distance(got, wl.x).max() <= 1
+
+
+def test_workspace_reuse_across_shapes(orc, dev):
+    """One workspace serves a large call, then smaller and different ones;
+    the epoch-tagged look-back words of earlier calls must not leak."""
+    big = W.make_workload("ws_big", 1500, 512, 64, 8, 4, seed=71)
+    shape = GH.shape_of(big)
+    bufs = M.EpBuffers(shape, dev)
+    for wl in [big, W.make_workload("ws_small", 333, 512, 64, 8, 4, seed=72), big,
+               W.make_workload("ws_fewer_experts", 700, 512, 16, 4, 4, seed=73)]:
+        sub = GH.shape_of(wl)
+        inputs = GH.GpuInputs(wl, dev)
+        b = M.EpBuffers(sub, dev)
+        b.ws = bufs.ws  # shared workspace, large enough for every shape here
+        b.layout(inputs.topk_idx)
+        b.dispatch(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+        assert b.status() == 0
+        g, _ = GH.fetch_dispatch(b, wl)
+        GH.assert_dispatch_equal(g, GH.oracle_run(orc, wl), wl)
+
+
+# --- device-detected errors -------------------------------------------------
+
+def test_bad_and_duplicate_expert_ids_match_oracle(orc, dev):
+    wl = W.make_workload("bad_ids", 400, 64, 16, 4, 4, seed=81)
+    idx = wl.topk_idx
+    idx[3, 1] = 16      # out of range
+    idx[10, 2] = -5     # negative, not -1
+    idx[20, 3] = idx[20, 0]  # repeat within a token
+    o = GH.oracle_run(orc, wl)
+    assert o["status"] == (M.binding.DEV_BAD_EXPERT_ID | M.binding.DEV_DUPLICATE_EXPERT)
+    bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
+    assert st == o["status"]
+    g, _ = GH.fetch_dispatch(bufs, wl)
+    GH.assert_dispatch_equal(g, o, wl)
+
+
+def test_inconsistent_layout_is_reported(dev):
+    wl = W.make_workload("bad_layout", 300, 64, 16, 4, 4, seed=82)
+    bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
+    assert st == 0
+    bufs.tokens_per_expert[0] += 5
+    bufs.tokens_per_expert[3] -= 1
+    bufs.dispatch(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+    assert bufs.status() & M.binding.DEV_BAD_LAYOUT
+    s2r = bufs.slot_to_row.cpu().numpy()
+    assert s2r.max() < wl.T * wl.k  # every written row stayed inside the buffer
+
+
+def test_bad_handle_is_reported_and_skipped(dev):
+    wl = W.make_workload("bad_handle", 64, 64, 8, 2, 2, seed=83)
+    bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
+    assert st == 0
+    bufs.slot_to_row[5, 0] = wl.T * wl.k + 100   # outside the receive buffer
+    r = int(bufs.slot_to_row[9, 1].item())
+    bufs.recv_src_idx[r] = 0                     # row no longer names token 9
+    eo = bufs.recv_x.view(torch.bfloat16)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    bufs.combine(eo, out, M.FP32)
+    assert bufs.status() & M.binding.DEV_BAD_HANDLE
+
+
+def test_forced_spin_timeout_terminates(dev):
+    """A spin limit of one poll makes some cross-workgroup waits give up; the
+    kernel must still drain and report SPIN_TIMEOUT (plus BAD_LAYOUT for the
+    rows that then fall outside their segment), or, if no wait ever had to
+    poll twice, finish cleanly.  Either way the grid exits and a re-zeroed
+    workspace works again."""
+    wl = W.make_workload("spin", 4096, 256, 256, 8, 8, seed=84)
+    shape = GH.shape_of(wl)
+    bufs = M.EpBuffers(shape, dev)
+    inputs = GH.GpuInputs(wl, dev)
+    M.ep_set_spin_limit(bufs.ws, 1)
+    bufs.layout(inputs.topk_idx)
+    bufs.dispatch(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+    st = bufs.status()
+    allowed = M.binding.DEV_SPIN_TIMEOUT | M.binding.DEV_BAD_LAYOUT
+    assert st & ~allowed == 0, st
+    assert not (st & M.binding.DEV_BAD_LAYOUT) or (st & M.binding.DEV_SPIN_TIMEOUT), st
+    M.ep_set_spin_limit(bufs.ws, 0)
+    M.ep_workspace_init(bufs.ws)
+    bufs.dispatch(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+    assert bufs.status() == 0
+
+
+def test_probe_copy(dev):
+    n = 64 << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    M.ep_probe_copy(dst, src, n)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
