@@ -35,11 +35,9 @@ DEV_BAD_EXPERT_ID = 1
 DEV_DUPLICATE_EXPERT = 2
 DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
-DEV_SPIN_TIMEOUT = 16
-DEV_WORKSPACE_RACE = 32
 
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
-           "ep_check_status", "ep_set_spin_limit", "ep_status_string", "ep_probe_copy")
+           "ep_check_status", "ep_status_string", "ep_probe_copy")
 
 
 class MoeDispError(RuntimeError):
@@ -86,8 +84,6 @@ def load(path: str = LIB_PATH):
     L.ep_combine.restype = C.c_int
     L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
     L.ep_check_status.restype = C.c_int
-    L.ep_set_spin_limit.argtypes = [P, C.c_size_t, C.c_uint32, P]
-    L.ep_set_spin_limit.restype = C.c_int
     L.ep_status_string.argtypes = [C.c_int]
     L.ep_status_string.restype = C.c_char_p
     L.ep_probe_copy.argtypes = [P, P, C.c_size_t, P]
@@ -149,11 +145,6 @@ def ep_check_status(ws, stream=None) -> int:
     _check("ep_check_status", load().ep_check_status(_p(ws), ws.numel() * ws.element_size(), _s(stream),
                                                      C.byref(v)))
     return int(v.value)
-
-
-def ep_set_spin_limit(ws, limit: int, stream=None):
-    _check("ep_set_spin_limit", load().ep_set_spin_limit(_p(ws), ws.numel() * ws.element_size(), int(limit),
-                                                         _s(stream)))
 
 
 def ep_probe_copy(dst, src, nbytes: int, stream=None):

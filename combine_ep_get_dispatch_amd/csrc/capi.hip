@@ -40,21 +40,38 @@ static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 DispatchPlan plan_dispatch(const moedisp_shape& s) {
     DispatchPlan p;
-    const long long write_per_token = (long long)s.topk * (long long)row_bytes(s);
-    // tokens per workgroup: aim for >= 32 KiB of row stores per workgroup
+    const int T = s.num_tokens, k = s.topk;
+    // copy: >= 64 KiB of row stores per workgroup
+    const long long write_per_token = (long long)k * (long long)row_bytes(s);
     int bt = 1;
-    while (bt < kMaxBlockTokens && write_per_token * bt < 32 * 1024) bt *= 2;
+    while (bt < kMaxBlockTokens && write_per_token * bt < 64 * 1024 && 2 * bt * k <= kMaxDispatchThreads) bt *= 2;
+    // count tiles: 16 tokens (at least bt), doubled until there are at most
+    // kMaxTiles (a slot's row sums one count per earlier tile)
+    int tt = 16;
+    while (tt < bt) tt *= 2;
+    while ((long long)tt * kMaxTiles < T && 2 * tt * k <= kMaxTileSlots) tt *= 2;
+    p.tile_tokens = tt;
+    p.tiles = T > 0 ? ceil_div(T, tt) : 1;
+    p.tile_stride = (p.tiles + 3) / 4 * 4;
     const int row16 = (int)(row_bytes(s) / 16);
     // split rows across workgroups while the grid is small (decode-sized T)
     int splits = 1;
-    const long long token_blocks = ceil_div(s.num_tokens, bt);
+    const long long token_blocks = ceil_div(T, bt);
     while (token_blocks * splits < 1024 && row16 / (splits * 2) >= kThreads / 2) splits *= 2;
     p.block_tokens = bt;
-    p.tile_tokens = bt > 16 ? bt : 16;
     p.col_splits = splits;
-    p.parts = (p.tile_tokens / p.block_tokens) * splits;
-    p.tiles = s.num_tokens > 0 ? ceil_div(s.num_tokens, p.tile_tokens) : 1;
-    p.blocks = p.tiles * p.parts;
+    // at least one workgroup, so that workgroup 0 runs the total check
+    p.blocks = token_blocks > 0 ? (int)(token_blocks * splits) : 1;
+    // lanes: whole waves covering one pass of the column range, and at least
+    // one lane per slot of the workgroup
+    p.units_per_lane = 4;
+    const int units = (row16 + splits - 1) / splits;
+    int threads = ((units + p.units_per_lane - 1) / p.units_per_lane + 63) / 64 * 64;
+    const int slot_lanes = (bt * k + 63) / 64 * 64;
+    if (threads < slot_lanes) threads = slot_lanes;
+    if (threads < kThreads) threads = kThreads;
+    if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
+    p.threads = threads;
     return p;
 }
 
@@ -65,6 +82,14 @@ CombinePlan plan_combine(const moedisp_shape& s) {
     while ((long long)s.num_tokens * splits < 1024 && row16 / (splits * 2) >= kThreads) splits *= 2;
     p.col_splits = splits;
     p.blocks = s.num_tokens * splits;
+    // lanes per workgroup: whole waves, enough for one pass of `units_per_lane`
+    // 16-byte units per lane over the workgroup's column range
+    const int units = (row16 + splits - 1) / splits;
+    const int per_lane = combine_units_per_lane(s.topk);
+    int threads = ((units + per_lane - 1) / per_lane + 63) / 64 * 64;
+    if (threads > kMaxCombineThreads) threads = kMaxCombineThreads;
+    if (threads < 64) threads = 64;
+    p.threads = threads;
     return p;
 }
 
@@ -76,9 +101,9 @@ WsPlan plan_workspace(const moedisp_shape& s) {
     const DispatchPlan d = plan_dispatch(s);
     w.partial_offset = sizeof(WsHeader);
     const size_t partial_bytes = (size_t)w.layout_blocks * (s.num_experts + s.num_groups) * sizeof(int32_t);
-    w.lookback_offset = align256(w.partial_offset + partial_bytes);
-    const size_t look_bytes = (size_t)d.tiles * s.num_experts * sizeof(uint64_t);
-    w.total = align256(w.lookback_offset + look_bytes);
+    w.counts_offset = align256(w.partial_offset + partial_bytes);
+    const size_t count_bytes = (size_t)d.tile_stride * s.num_experts * sizeof(int32_t);
+    w.total = align256(w.counts_offset + count_bytes);
     return w;
 }
 
@@ -174,7 +199,7 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
     a.expert_offsets = expert_offsets;
     a.slot_to_row = slot_to_row;
     a.hdr = (WsHeader*)ws;
-    a.lookback = (uint64_t*)((char*)ws + w.lookback_offset);
+    a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
     return hip_status(launch_dispatch(a, (hipStream_t)stream));
 }
 
@@ -198,6 +223,7 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     a.row16 = (int)((size_t)s->hidden * 2 / 16);
     a.capacity = s->num_tokens * s->topk;
     a.col_splits = p.col_splits;
+    a.threads = p.threads;
     a.expert_out = (const v4u*)expert_out;
     a.recv_src_idx = recv_src_idx;
     a.recv_weights = recv_weights;
@@ -218,12 +244,6 @@ int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_statu
     *host_status = (int32_t)v;
     if (v) return hip_status(launch_set_word(&((WsHeader*)ws)->status, 0u, st));
     return MOEDISP_OK;
-}
-
-int ep_set_spin_limit(void* ws, size_t ws_bytes, uint32_t limit, void* stream) {
-    if (!ws || ws_bytes < sizeof(WsHeader)) return MOEDISP_ERR_INVALID_ARG;
-    if (!aligned(ws, 256)) return MOEDISP_ERR_MISALIGNED;
-    return hip_status(launch_set_word(&((WsHeader*)ws)->spin_limit, limit, (hipStream_t)stream));
 }
 
 const char* ep_status_string(int status) {

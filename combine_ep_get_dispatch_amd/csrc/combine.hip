@@ -84,10 +84,11 @@ __device__ inline int handle_row(const CombineArgs& a, int t, int j, float* w, u
 
 // KC: compile-time k (0 = runtime k, slots gathered one at a time).
 template <int KC, int U, bool kF32>
-__global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
+__global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArgs a) {
     const int t = blockIdx.x / a.col_splits;
     const int split = blockIdx.x - t * a.col_splits;
     const int tid = threadIdx.x;
+    const int nth = blockDim.x;
     const int per_split = (a.row16 + a.col_splits - 1) / a.col_splits;
     const int c0 = split * per_split;
     const int c1 = min(a.row16, c0 + per_split);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
         float wts[KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j) rows[j] = handle_row(a, t, j, &wts[j], &err);
-        for (int c = c0 + tid; c < c1; c += U * kThreads) {
+        for (int c = c0 + tid; c < c1; c += U * nth) {
             float acc[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
             for (int j = 0; j < KC; ++j)
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * kThreads;
+                    const int cc = c + u * nth;
                     if (rows[j] >= 0 && cc < c1)
                         v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 + cc);
                 }
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int cc = c + u * kThreads;
+                const int cc = c + u * nth;
                 if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
             }
         }
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
                 handle_row(a, t, j, &w, &err);
             }
         uint32_t ignored = 0;
-        for (int c = c0 + tid; c < c1; c += U * kThreads) {
+        for (int c = c0 + tid; c < c1; c += U * nth) {
             float acc[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
                 v4u v[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * kThreads;
+                    const int cc = c + u * nth;
                     if (cc < c1) v[u] = __builtin_nontemporal_load(a.expert_out + (size_t)r * a.row16 + cc);
                 }
 #pragma unroll
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int cc = c + u * kThreads;
+                const int cc = c + u * nth;
                 if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
             }
         }
@@ -163,8 +164,8 @@ __global__ __launch_bounds__(kThreads) void moedisp_combine(CombineArgs a) {
 
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
-    constexpr int U = KC >= 8 ? 2 : 4;
-    hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(kThreads), 0, stream, a);
+    constexpr int U = (KC == 1 || KC == 2 || KC == 4) ? 4 : 2;  // = combine_units_per_lane(k)
+    hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(a.threads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -1,5 +1,5 @@
-// Dispatch kernel: row offsets by a single-pass scan with decoupled look-back,
-// fused with the row scatter.
+// Dispatch: per-tile expert counts (count kernel), then receive rows and the
+// row scatter (scatter kernel).
 //
 // What is computed ("MSCCLPP EP implementation - #852": PR description,
 // "Scope", intranode dispatch; commit message fixing internode combine for the
@@ -10,55 +10,44 @@
 // bytes are copied there.  Rows move in 16-byte units (the page's warp-geometry
 // commits and code-scanning excerpt count hidden rows in int4 units).
 //
-// How.  Tokens form look-back tiles of `tile_tokens`.  Workgroups take a ticket
-// from a workspace counter when they start, so a ticket's predecessors are
-// already running; ticket -> (tile, part).  Part 0 of each tile ("publisher")
-// builds the tile's per-expert histogram in LDS, publishes it as an aggregate
-// word per expert, walks back over predecessor tiles (eight words per poll)
-// until it meets an inclusive prefix, and publishes its own inclusive prefix.
-// Tile 0 seeds the chain with the exclusive scan of tokens_per_expert, so
-// every published prefix already includes the expert's base offset.  The other
-// parts of a tile wait for that tile's prefix of the experts they need.  Within
-// a tile, a slot's rank is the number of earlier slots in the tile with the
-// same expert, counted from the LDS copy of the tile's routing: no atomics
-// decide any order, so the result is deterministic.
-//
-// Each workgroup then copies its tokens: every lane loads U 16-byte units of
-// the source row once and stores them to each of the token's k destination
-// rows (one load, k coalesced stores per unit).  Look-back words carry the
-// call's epoch so words left by earlier calls read as "not ready"; the last
-// workgroup to finish advances the epoch and resets the ticket counters.
-// Every wait is bounded; a wait that gives up raises SPIN_TIMEOUT and the
-// workgroup continues, so the grid always drains.
+// The device-wide scan is a reduce-then-scan split across the two kernels,
+// with the kernel boundary as its only synchronisation:
+//  - count kernel, one workgroup per tile of `tile_tokens` tokens: counts the
+//    tile's slots per expert in LDS and stores them expert-major (one
+//    expert's counts over the tiles are contiguous).  Tile 0 also stores
+//    expert_offsets, the exclusive scan of tokens_per_expert.
+//  - scatter kernel, one workgroup per `block_tokens` tokens (and column
+//    range): for each of its slots with expert e, the row is
+//      expert_offsets[e] + (counts of e in the earlier tiles, summed by
+//      several lanes with 16-byte loads from the L2-resident count table)
+//      + (the number of earlier slots of its own tile with expert e, counted
+//      from an LDS copy of the tile's routing).
+//    Every workgroup does this small prefix sum for itself, so no workgroup
+//    ever waits for another: on a multi-XCD part a cross-workgroup wait (a
+//    chained or decoupled look-back) costs a cross-XCD round trip per hop,
+//    and while the copy saturates HBM those polls queue behind the stores.
+//    No atomics decide any order, so the result is deterministic.
+// The scatter then streams: each lane loads U 16-byte units of the source row
+// once (the first pass is issued before the row computation) and stores them,
+// non-temporally, to each of the token's k destination rows.  Workgroups of
+// column range 0 write the handle (slot_to_row, recv_src_idx, recv_weights)
+// and fp8 scales.  Rows outside their expert's segment (or the buffer) are not
+// written and raise BAD_LAYOUT; workgroup 0 also checks that the routed slots
+// add up to the sum of tokens_per_expert.
 #include "moedisp_internal.h"
 
 namespace moedisp {
 namespace {
-
-constexpr int kLookWindow = 8;
-
-__device__ inline uint64_t pack_word(uint32_t epoch, uint32_t flag, uint32_t value) {
-    return ((uint64_t)epoch << 32) | ((uint64_t)flag << 30) | (uint64_t)(value & kValueMask);
-}
-__device__ inline uint32_t word_epoch(uint64_t w) { return (uint32_t)(w >> 32); }
-__device__ inline uint32_t word_flag(uint64_t w) { return (uint32_t)(w >> 30) & 3u; }
-__device__ inline uint32_t word_value(uint64_t w) { return (uint32_t)w & kValueMask; }
-
-__device__ inline uint64_t load_word(const uint64_t* p) {
-    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void store_word(uint64_t* p, uint64_t v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Exclusive scan of in[0..n) into out (LDS), by the whole workgroup.  Returns
 // the total; sets *bad if an entry is negative.
 __device__ long long block_exclusive_scan(const int32_t* __restrict__ in, int n, int32_t* out,
                                           long long* s_wave, bool* bad) {
     const int tid = threadIdx.x;
+    const int nth = blockDim.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int per = (n + kThreads - 1) / kThreads;
+    const int per = (n + nth - 1) / nth;
     const int lo = min(n, tid * per);
     const int hi = min(n, lo + per);
     long long sum = 0;
@@ -76,7 +65,7 @@ __device__ long long block_exclusive_scan(const int32_t* __restrict__ in, int n,
     __syncthreads();
     long long run = incl - sum;
     long long total = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
+    for (int w = 0; w < nth / 64; ++w) {
         if (w < wave) run += s_wave[w];
         total += s_wave[w];
     }
@@ -88,169 +77,138 @@ __device__ long long block_exclusive_scan(const int32_t* __restrict__ in, int n,
     return total;
 }
 
-template <bool kNT>
-__device__ inline void store16(v4u* p, v4u v) {
-    if constexpr (kNT)
-        __builtin_nontemporal_store(v, p);
-    else
-        *p = v;
-}
-
-template <int U, bool kNT>
-__global__ __launch_bounds__(kThreads) void moedisp_dispatch(DispatchArgs a) {
-    extern __shared__ int32_t dyn[];  // hist[E], excl[E], off[E]
+__global__ __launch_bounds__(kThreads) void moedisp_count(DispatchArgs a) {
+    const DispatchPlan& P = a.plan;
+    extern __shared__ int32_t dyn[];  // hist[E]
     int32_t* s_hist = dyn;
-    int32_t* s_excl = dyn + a.E;
-    int32_t* s_off = dyn + 2 * a.E;
-    __shared__ int32_t s_ids[kMaxTileTokens * kMaxTopk];
-    __shared__ int32_t s_rows[kMaxBlockTokens * kMaxTopk];
     __shared__ long long s_wave[kThreads / 64];
-    __shared__ uint32_t s_ticket, s_epoch, s_limit, s_err;
-
+    __shared__ uint32_t s_err;
     const int tid = threadIdx.x;
     const int k = a.k;
     const int E = a.E;
-    const DispatchPlan& P = a.plan;
+    const int tile = blockIdx.x;
+    const int tile_t0 = tile * P.tile_tokens;
+    const int tile_slots = max(0, min(P.tile_tokens, a.T - tile_t0)) * k;
 
+    for (int e = tid; e < E; e += kThreads) s_hist[e] = 0;
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+    uint32_t err = 0;
+    for (int s = tid; s < tile_slots; s += kThreads) {
+        const int id = a.topk_idx[(size_t)tile_t0 * k + s];
+        if (id >= 0 && id < E)
+            atomicAdd(&s_hist[id], 1);
+        else if (id != -1)
+            err |= MOEDISP_DEV_BAD_EXPERT_ID;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kThreads) a.tile_counts[(size_t)e * P.tile_stride + tile] = s_hist[e];
+    if (tile == 0) {
+        __syncthreads();  // s_hist is reused as the scan output
+        bool bad = false;
+        const long long total = block_exclusive_scan(a.tokens_per_expert, E, s_hist, s_wave, &bad);
+        if (bad || total > a.capacity) err |= MOEDISP_DEV_BAD_LAYOUT;
+        for (int e = tid; e < E; e += kThreads) a.expert_offsets[e] = s_hist[e];
+        if (tid == 0) a.expert_offsets[E] = (int32_t)total;
+    }
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
+}
+
+// U: 16-byte units per lane per pass.
+template <int U>
+__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchArgs a) {
+    const DispatchPlan& P = a.plan;
+    extern __shared__ int32_t dyn[];  // routing of the tile up to this workgroup's last slot
+    int32_t* s_ids = dyn;
+    __shared__ int32_t s_pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
+    __shared__ int32_t s_base[kMaxBlockSlots];  // expert_offsets[e]
+    __shared__ int32_t s_len[kMaxBlockSlots];   // tokens_per_expert[e]
+    __shared__ int32_t s_rows[kMaxBlockSlots];
+    __shared__ int32_t s_routed;
+    __shared__ uint32_t s_err;
+
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    const int k = a.k;
+    const int E = a.E;
+    const int tok = blockIdx.x / P.col_splits;
+    const int split = blockIdx.x - tok * P.col_splits;
+    const int blk_t0 = tok * P.block_tokens;
+    const int blk_nt = max(0, min(P.block_tokens, a.T - blk_t0));
+    const int blk_slots = blk_nt * k;
+    const int tile = blk_t0 / P.tile_tokens;  // tile_tokens is a multiple of block_tokens
+    const int tile_t0 = tile * P.tile_tokens;
+    const int first = (blk_t0 - tile_t0) * k;  // slots of the tile before this workgroup's
+    const int per_split = (a.row16 + P.col_splits - 1) / P.col_splits;
+    const int c0 = split * per_split;
+    const int c1 = min(a.row16, c0 + per_split);
+
+    // first pass of source units: independent of the rows, so issued first
+    v4u pre[U];
+    if (blk_nt > 0) {
+        const v4u* src = a.x + (size_t)blk_t0 * a.row16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c0 + tid + u * nth;
+            if (cc < c1) pre[u] = src[cc];
+        }
+    }
+    for (int i = tid; i < first + blk_slots; i += nth) {
+        const int id = a.topk_idx[(size_t)tile_t0 * k + i];
+        s_ids[i] = (id >= 0 && id < E) ? id : -1;
+    }
+    for (int q = tid; q < blk_slots; q += nth) s_pre[q] = 0;
     if (tid == 0) {
-        s_ticket = atomicAdd(&a.hdr->dispatch_ticket, 1u);
-        s_epoch = __hip_atomic_load(&a.hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-        const uint32_t lim = __hip_atomic_load(&a.hdr->spin_limit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_limit = lim ? lim : kDefaultSpinLimit;
+        s_routed = 0;
         s_err = 0;
     }
     __syncthreads();
-    const uint32_t ticket = s_ticket;
-    const uint32_t epoch = s_epoch;
-    const uint32_t limit = s_limit;
-    if (ticket >= (uint32_t)a.plan.blocks) {
-        // counters left by an overlapping call on this workspace: touch nothing
-        if (tid == 0) atomicOr(&a.hdr->status, MOEDISP_DEV_WORKSPACE_RACE);
-        return;
-    }
-    const int tile = (int)(ticket / (uint32_t)P.parts);
-    const int part = (int)(ticket % (uint32_t)P.parts);
-    const int split = part % P.col_splits;
-    const int tile_t0 = tile * P.tile_tokens;
-    const int tile_nt = max(0, min(P.tile_tokens, a.T - tile_t0));
-    const int tile_slots = tile_nt * k;
-    const int blk_t0 = tile_t0 + (part / P.col_splits) * P.block_tokens;
-    const int blk_nt = max(0, min(P.block_tokens, a.T - blk_t0));
-    const int blk_slots = blk_nt * k;
-    const bool publisher = part == 0;
-    uint32_t err = 0;
 
-    // routing of the whole tile -> LDS; ids outside {-1} U [0,E) become -1
-    for (int s = tid; s < tile_slots; s += kThreads) {
-        int id = a.topk_idx[(size_t)tile_t0 * k + s];
-        if (id < -1 || id >= E) {
-            err |= MOEDISP_DEV_BAD_EXPERT_ID;
-            id = -1;
+    // counts of each slot's expert in the earlier tiles: L lanes per slot,
+    // 16-byte loads of the expert's contiguous count column
+    if (blk_slots > 0) {
+        const int L = nth / blk_slots;  // >= 1: the plan keeps blk_slots <= threads
+        if (tid < L * blk_slots) {
+            const int q = tid / L;
+            const int l = tid - q * L;
+            const int e = s_ids[first + q];
+            if (e >= 0) {
+                const int32_t* col = a.tile_counts + (size_t)e * P.tile_stride;  // 16-byte aligned
+                const int n4 = tile >> 2;
+                int32_t sum = 0;
+                for (int c = l; c < n4; c += 4 * L) {
+                    int4 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        v[u] = (c + u * L < n4) ? reinterpret_cast<const int4*>(col)[c + u * L] : make_int4(0, 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
+                }
+                if (l == 0) {
+                    for (int j = n4 * 4; j < tile; ++j) sum += col[j];
+                    s_base[q] = a.expert_offsets[e];
+                    s_len[q] = a.tokens_per_expert[e];
+                }
+                if (sum) atomicAdd(&s_pre[q], sum);
+            }
         }
-        s_ids[s] = id;
     }
-    if (publisher)
-        for (int e = tid; e < E; e += kThreads) s_hist[e] = 0;
     __syncthreads();
 
-    if (publisher) {
-        for (int s = tid; s < tile_slots; s += kThreads) {
-            const int id = s_ids[s];
-            if (id >= 0) atomicAdd(&s_hist[id], 1);
-        }
-        __syncthreads();
-        uint64_t* mine = a.lookback + (size_t)tile * E;
-        if (tile == 0) {
-            bool bad = false;
-            const long long total = block_exclusive_scan(a.tokens_per_expert, E, s_excl, s_wave, &bad);
-            if (bad || total > a.capacity) err |= MOEDISP_DEV_BAD_LAYOUT;
-            for (int e = tid; e < E; e += kThreads) {
-                store_word(mine + e, pack_word(epoch, kFlagPrefix, (uint32_t)(s_excl[e] + s_hist[e])));
-                a.expert_offsets[e] = s_excl[e];
-            }
-            if (tid == 0) a.expert_offsets[E] = (int32_t)total;
-        } else {
-            for (int e = tid; e < E; e += kThreads)
-                store_word(mine + e, pack_word(epoch, kFlagAggregate, (uint32_t)s_hist[e]));
-            for (int e = tid; e < E; e += kThreads) {
-                uint32_t acc = 0;
-                int j = tile - 1;
-                uint32_t polls = 0;
-                while (true) {
-                    uint64_t w[kLookWindow];
-#pragma unroll
-                    for (int q = 0; q < kLookWindow; ++q)
-                        w[q] = (j - q >= 0) ? load_word(a.lookback + (size_t)(j - q) * E + e) : 0ull;
-                    int q = 0;
-                    bool done = false;
-                    for (; q < kLookWindow && j - q >= 0; ++q) {
-                        if (word_epoch(w[q]) != epoch || word_flag(w[q]) == 0u) break;
-                        acc += word_value(w[q]);
-                        if (word_flag(w[q]) == kFlagPrefix) {
-                            done = true;
-                            break;
-                        }
-                    }
-                    if (done) break;
-                    j -= q;
-                    if (j < 0) {  // tile 0 always publishes a prefix; cannot happen
-                        err |= MOEDISP_DEV_BAD_LAYOUT;
-                        break;
-                    }
-                    if (q == 0) {
-                        if (++polls > limit) {
-                            err |= MOEDISP_DEV_SPIN_TIMEOUT;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                    }
-                }
-                s_excl[e] = (int32_t)acc;
-                store_word(mine + e, pack_word(epoch, kFlagPrefix, acc + (uint32_t)s_hist[e]));
-            }
-        }
-        if (tile == P.tiles - 1) {
-            // the last tile's inclusive prefix must land on expert_offsets[e+1]
-            bool bad = false;
-            block_exclusive_scan(a.tokens_per_expert, E, s_off, s_wave, &bad);
-            for (int e = tid; e < E; e += kThreads)
-                if ((long long)s_excl[e] + s_hist[e] != (long long)s_off[e] + a.tokens_per_expert[e])
-                    err |= MOEDISP_DEV_BAD_LAYOUT;
-        }
-        __syncthreads();
-    }
-
     // rows of this workgroup's slots
-    for (int q = tid; q < blk_slots; q += kThreads) {
-        const int s = (blk_t0 - tile_t0) * k + q;  // slot within the tile
+    uint32_t err = 0;
+    for (int q = tid; q < blk_slots; q += nth) {
+        const int s = first + q;
         const int e = s_ids[s];
         int row = -1;
         if (e >= 0) {
-            int before = 0, in_tile = 0;
-            for (int u = 0; u < tile_slots; ++u) {
-                const int v = s_ids[u];
-                in_tile += v == e;
-                before += (v == e) & (u < s);
-            }
-            long long base;
-            if (publisher) {
-                base = s_excl[e];
-            } else {
-                const uint64_t* p = a.lookback + (size_t)tile * E + e;
-                uint32_t polls = 0;
-                uint64_t w = load_word(p);
-                while (word_epoch(w) != epoch || word_flag(w) != kFlagPrefix) {
-                    if (++polls > limit) {
-                        err |= MOEDISP_DEV_SPIN_TIMEOUT;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                    w = load_word(p);
-                }
-                base = (long long)word_value(w) - in_tile;
-            }
-            const long long r = base + before;
-            if (r < 0 || r >= a.capacity)
+            int before = 0;
+            for (int u = 0; u < s; ++u) before += s_ids[u] == e;
+            const long long base = s_base[q];
+            const long long r = base + s_pre[q] + before;
+            if (r < 0 || r < base || r >= base + s_len[q] || r >= a.capacity)
                 err |= MOEDISP_DEV_BAD_LAYOUT;
             else
                 row = (int)r;
@@ -261,19 +219,18 @@ __global__ __launch_bounds__(kThreads) void moedisp_dispatch(DispatchArgs a) {
 
     // handle: slot -> row, row -> source token and weight, fp8 scales
     if (split == 0) {
-        for (int q = tid; q < blk_slots; q += kThreads) {
-            const int t = blk_t0 + q / k;
+        for (int q = tid; q < blk_slots; q += nth) {
             const size_t slot = (size_t)blk_t0 * k + q;
             const int row = s_rows[q];
             a.slot_to_row[slot] = row;
             if (row >= 0) {
-                a.recv_src_idx[row] = t;
+                a.recv_src_idx[row] = blk_t0 + q / k;
                 a.recv_weights[row] = a.topk_weights[slot];
             }
         }
         if (a.scale_words) {
             const int n = blk_slots * a.scale_words;
-            for (int i = tid; i < n; i += kThreads) {
+            for (int i = tid; i < n; i += nth) {
                 const int q = i / a.scale_words;
                 const int c = i - q * a.scale_words;
                 const int row = s_rows[q];
@@ -285,18 +242,20 @@ __global__ __launch_bounds__(kThreads) void moedisp_dispatch(DispatchArgs a) {
     }
 
     // row scatter: each 16-byte unit is loaded once and stored k times
-    const int per_split = (a.row16 + P.col_splits - 1) / P.col_splits;
-    const int c0 = split * per_split;
-    const int c1 = min(a.row16, c0 + per_split);
     for (int tt = 0; tt < blk_nt; ++tt) {
         const v4u* src = a.x + (size_t)(blk_t0 + tt) * a.row16;
         const int32_t* rows = s_rows + tt * k;
-        for (int c = c0 + tid; c < c1; c += U * kThreads) {
+        for (int c = c0 + tid; c < c1; c += U * nth) {
             v4u v[U];
+            if (tt == 0 && c == c0 + tid) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int cc = c + u * kThreads;
-                if (cc < c1) v[u] = src[cc];
+                for (int u = 0; u < U; ++u) v[u] = pre[u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int cc = c + u * nth;
+                    if (cc < c1) v[u] = src[cc];
+                }
             }
             for (int j = 0; j < k; ++j) {
                 const int r = rows[j];
@@ -304,32 +263,47 @@ __global__ __launch_bounds__(kThreads) void moedisp_dispatch(DispatchArgs a) {
                 v4u* dst = a.recv_x + (size_t)r * a.row16;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * kThreads;
-                    if (cc < c1) store16<kNT>(dst + cc, v[u]);
+                    const int cc = c + u * nth;
+                    if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
                 }
             }
         }
     }
 
+    // workgroup 0: the routed slots must add up to the layout's total
+    if (blockIdx.x == 0) {
+        const int n = a.T * k;
+        int32_t routed = 0;
+        for (int i0 = tid; i0 < n; i0 += 8 * nth) {
+            int32_t v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nth < n) ? a.topk_idx[i0 + u * nth] : -1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) routed += (v[u] >= 0 && v[u] < E);
+        }
+        if (routed) atomicAdd(&s_routed, routed);
+        __syncthreads();
+        if (tid == 0 && s_routed != a.expert_offsets[E]) err |= MOEDISP_DEV_BAD_LAYOUT;
+    }
     if (err) atomicOr(&s_err, err);
     __syncthreads();
-    if (tid == 0) {
-        if (s_err) atomicOr(&a.hdr->status, s_err);
-        __threadfence();
-        const uint32_t prev = atomicAdd(&a.hdr->dispatch_done, 1u);
-        if (prev == (uint32_t)(P.blocks - 1)) {
-            __hip_atomic_store(&a.hdr->epoch, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.hdr->dispatch_ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.hdr->dispatch_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
-    const size_t lds = (size_t)3 * a.E * sizeof(int32_t);
-    hipLaunchKernelGGL((moedisp_dispatch<4, true>), dim3(a.plan.blocks), dim3(kThreads), lds, stream, a);
+    const DispatchPlan& p = a.plan;
+    hipLaunchKernelGGL(moedisp_count, dim3(p.tiles), dim3(kThreads), (size_t)a.E * sizeof(int32_t), stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
+    const dim3 grid(p.blocks), block(p.threads);
+    switch (p.units_per_lane) {
+        case 1: hipLaunchKernelGGL((moedisp_scatter<1>), grid, block, lds, stream, a); break;
+        case 2: hipLaunchKernelGGL((moedisp_scatter<2>), grid, block, lds, stream, a); break;
+        default: hipLaunchKernelGGL((moedisp_scatter<4>), grid, block, lds, stream, a); break;
+    }
     return hipGetLastError();
 }
 

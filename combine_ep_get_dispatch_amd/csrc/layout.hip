@@ -46,9 +46,24 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
 
     for (int i = tid; i < EG; i += kThreads) s_cnt[i] = 0;
     if (tid == 0) s_err = 0;
-    for (int i = tid; i < nt * k; i += kThreads) {
-        const int tt = i / k;
-        s_ids[tt * kp + (i - tt * k)] = a.topk_idx[(size_t)t0 * k + i];
+    // stage the routing rows: 8 independent coalesced loads in flight per lane
+    constexpr int kStage = 8;
+    const int n = nt * k;
+    for (int i0 = 0; i0 < n; i0 += kStage * kThreads) {
+        int32_t v[kStage];
+#pragma unroll
+        for (int q = 0; q < kStage; ++q) {
+            const int i = i0 + q * kThreads + tid;
+            v[q] = i < n ? a.topk_idx[(size_t)t0 * k + i] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kStage; ++q) {
+            const int i = i0 + q * kThreads + tid;
+            if (i < n) {
+                const int tt = i / k;
+                s_ids[tt * kp + (i - tt * k)] = v[q];
+            }
+        }
     }
     __syncthreads();
 
@@ -95,9 +110,18 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
     if (!s_last) return;
 
     __threadfence();
+    // sum the partials in workgroup order, 16 independent loads in flight
+    constexpr int kBatch = 16;
     for (int i = tid; i < EG; i += kThreads) {
         int32_t sum = 0;
-        for (int b = 0; b < a.blocks; ++b) sum += a.partials[(size_t)b * EG + i];
+        for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
+            int32_t v[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                v[q] = (b0 + q < a.blocks) ? a.partials[(size_t)(b0 + q) * EG + i] : 0;
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) sum += v[q];
+        }
         if (i < a.E)
             a.tokens_per_expert[i] = sum;
         else

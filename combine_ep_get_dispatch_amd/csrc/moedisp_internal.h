@@ -18,49 +18,54 @@ constexpr int kLayoutTokensPerBlock = 256; // layout: one token per thread
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGroups = 32;
-constexpr int kMaxTileTokens = 32;         // dispatch look-back tile
+constexpr int kMaxTileSlots = 4096;        // dispatch tile: tile_tokens * k routing ids in LDS
+constexpr int kMaxTiles = 256;             // dispatch aims for at most this many tiles
 constexpr int kMaxBlockTokens = 16;        // dispatch tokens copied per workgroup
-constexpr uint32_t kDefaultSpinLimit = 1u << 18;
-
-// Look-back words: [63:32] epoch of the dispatch call, [31:30] flag, [29:0] value.
-constexpr uint32_t kFlagAggregate = 1u;  // value = this tile's count for the expert
-constexpr uint32_t kFlagPrefix = 2u;     // value = inclusive prefix through this tile
-constexpr uint32_t kValueMask = (1u << 30) - 1u;
+constexpr int kMaxBlockSlots = 512;        // >= kMaxBlockTokens * kMaxTopk
 
 // First 256 bytes of the workspace.
 struct WsHeader {
     uint32_t status;           // MOEDISP_DEV_* bits, or-ed by kernels
     uint32_t layout_done;      // layout workgroups finished (the last one reduces)
-    uint32_t dispatch_ticket;  // dispatch workgroup order (taken at start)
-    uint32_t dispatch_done;    // dispatch workgroups finished
-    uint32_t epoch;            // dispatch calls completed; tags look-back words
-    uint32_t spin_limit;       // 0 = kDefaultSpinLimit
-    uint32_t reserved[58];
+    uint32_t reserved[62];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
-// How one dispatch launch splits work.  Tokens are grouped in look-back
-// tiles of `tile_tokens`; each tile is served by `parts` workgroups: every
-// workgroup copies `block_tokens` consecutive tokens of the tile, restricted
-// to one of `col_splits` equal column ranges of the row.
+// How one dispatch splits work.  The count kernel runs one workgroup per tile
+// of `tile_tokens` tokens and stores per-tile expert counts (expert-major,
+// `tile_stride` >= tiles ints per expert, a multiple of 4).  The scatter kernel
+// runs `blocks` workgroups of `threads` lanes: each computes the rows of and
+// copies `block_tokens` consecutive tokens (inside one tile), restricted to
+// one of `col_splits` equal column ranges of the row, `units_per_lane`
+// 16-byte units per lane and pass.
 struct DispatchPlan {
     int tile_tokens;
+    int tiles;
+    int tile_stride;
     int block_tokens;
     int col_splits;
-    int parts;
-    int tiles;
     int blocks;
+    int threads;
+    int units_per_lane;  // 1, 2 or 4
 };
+
+constexpr int kMaxDispatchThreads = 1024;
 
 struct CombinePlan {
     int col_splits;
     int blocks;
+    int threads;
 };
+
+constexpr int kMaxCombineThreads = 1024;
+// 16-byte units each combine lane owns per pass (k loads in flight per unit);
+// k = 1, 2, 4 have unrolled kernels with 4 units, every other k uses 2
+inline int combine_units_per_lane(int k) { return (k == 1 || k == 2 || k == 4) ? 4 : 2; }
 
 struct WsPlan {
     int layout_blocks;
     size_t partial_offset;   // int32 [layout_blocks][E + G]
-    size_t lookback_offset;  // uint64 [tiles][E]
+    size_t counts_offset;    // int32 [E][tile_stride]: per-tile expert counts of the dispatch
     size_t total;
 };
 
@@ -104,7 +109,7 @@ struct DispatchArgs {
     int32_t* expert_offsets;
     int32_t* slot_to_row;
     WsHeader* hdr;
-    uint64_t* lookback;
+    int32_t* tile_counts;
 };
 
 struct CombineArgs {
@@ -112,6 +117,7 @@ struct CombineArgs {
     int row16;
     int capacity;
     int col_splits;
+    int threads;
     const v4u* expert_out;
     const int32_t* recv_src_idx;
     const float* recv_weights;

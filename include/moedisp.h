@@ -34,8 +34,8 @@
  *     enqueued; a failed check returns a negative MOEDISP_ERR_* code and
  *     enqueues nothing.  A failed launch returns MOEDISP_ERR_HIP.  Problems
  *     only visible in device data (bad expert ids, an inconsistent layout or
- *     handle, a wait that timed out) set bits of a status word in `ws`, read
- *     by ep_check_status.  The library never asserts or aborts.
+ *     handle) set bits of a status word in `ws`, read by ep_check_status.
+ *     The library never asserts or aborts.
  *   - Calls that share one `ws` must be ordered on one stream; concurrent
  *     calls need distinct workspaces.
  */
@@ -81,17 +81,14 @@ typedef struct {
 #define MOEDISP_DEV_DUPLICATE_EXPERT 2u  /* an expert repeated within one token (each copy still routed) */
 #define MOEDISP_DEV_BAD_LAYOUT 4u        /* tokens_per_expert disagrees with topk_idx; bad rows skipped */
 #define MOEDISP_DEV_BAD_HANDLE 8u        /* combine handle inconsistent; those slots skipped */
-#define MOEDISP_DEV_SPIN_TIMEOUT 16u     /* a bounded cross-workgroup wait gave up; results invalid */
-#define MOEDISP_DEV_WORKSPACE_RACE 32u   /* workspace counters corrupted by overlapping calls; re-init ws */
 
 /* Bytes of workspace the calls need for `shape`; 0 if the shape is invalid.
  * One workspace serves layout, dispatch and combine of that shape (or of any
  * shape with no more tokens and experts). */
 size_t ep_workspace_bytes(const moedisp_shape* shape);
 
-/* Zero a workspace before its first use (or after a call that reported
- * MOEDISP_DEV_SPIN_TIMEOUT).  The calls keep its counters consistent
- * afterwards; a workspace must not be shared by overlapping calls. */
+/* Zero a workspace before its first use.  The calls keep its counters
+ * consistent afterwards; a workspace must not be shared by overlapping calls. */
 int ep_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Layout ("counts + token-in-rank" of the high-throughput layout kernel).
@@ -120,7 +117,7 @@ int ep_get_dispatch_layout(const moedisp_shape* shape, const int32_t* topk_idx,
  *   expert_offsets     int32 [E+1]: exclusive prefix of tokens_per_expert; [E] = R.
  *   slot_to_row        int32 [T][k]: row of each slot, -1 if masked.
  * (recv_src_idx, recv_weights, slot_to_row) is the handle ep_combine takes.
- * Status bits: BAD_EXPERT_ID, BAD_LAYOUT, SPIN_TIMEOUT, WORKSPACE_RACE. */
+ * Status bits: BAD_EXPERT_ID, BAD_LAYOUT. */
 int ep_dispatch(const moedisp_shape* shape, const void* x, const float* x_scales,
                 const int32_t* topk_idx, const float* topk_weights,
                 const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
@@ -143,10 +140,6 @@ int ep_combine(const moedisp_shape* shape, const void* expert_out, const int32_t
 /* Wait for `stream`, then return the device status bits accumulated in `ws`
  * since the last check in *host_status and clear them. */
 int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_status);
-
-/* Upper bound on polls of one cross-workgroup wait before it gives up with
- * MOEDISP_DEV_SPIN_TIMEOUT (0 = the default, 2^18).  Stored in `ws`. */
-int ep_set_spin_limit(void* ws, size_t ws_bytes, uint32_t limit, void* stream);
 
 /* Text for a host return code. */
 const char* ep_status_string(int status);
