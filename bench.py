@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of one GPU's share of MoE EP layout -> dispatch -> combine.
 
-One step = ep_get_dispatch_layout + ep_dispatch + ep_combine (bf16 out) over
-one batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168
-bf16, E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
+One step = ep_get_dispatch_layout + ep_dispatch (called as its two phases,
+ep_dispatch_notify and ep_dispatch_scatter) + ep_combine (bf16 out) over one
+batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168 bf16,
+E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
 stand-in expert outputs are resident in HBM before the timed region; the
 timed region is exactly K steps between two device synchronisations.  HIP
-events on the launch stream time each call (one kernel each) inside that
-region; the dominant kernel's algorithmic bytes over its mean duration give
-the roofline entry.  The CPU oracle, timed on a bounded sample of the same
-workload on the host, is the reported baseline.
+events on the launch stream between the calls time each kernel (every call
+is one kernel) inside that region; the dominant kernel's algorithmic bytes
+over its mean duration give the roofline entry, with the HBM bytes measured
+by rocprofv3 counters (profiles/hbm_traffic.json) when they were taken on the
+current kernel sources.  The CPU oracle, timed on a bounded sample of the
+same workload on the host, is the reported baseline.
 
 Prints one JSON line.  `--gpus` above 1 is refused: this build runs one GPU.
 """
@@ -78,23 +81,29 @@ def run_gpu(cid, steps, warmup, dev):
 
     stream = torch.cuda.current_stream()
 
+    # one step = layout, dispatch (its two phases: notify = count kernel,
+    # scatter = scatter kernel), combine; events between the calls time each
+    # kernel on the launch stream
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         bufs.layout(idx, stream)
         if ev is not None:
             ev[1].record(stream)
-        bufs.dispatch(x, xs, idx, w, stream)
+        bufs.dispatch_notify(idx, stream)
         if ev is not None:
             ev[2].record(stream)
-        bufs.combine(eo, out, M.BF16, True, stream)
+        bufs.dispatch_scatter(x, xs, idx, w, stream)
         if ev is not None:
             ev[3].record(stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+        if ev is not None:
+            ev[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -107,8 +116,10 @@ def run_gpu(cid, steps, warmup, dev):
 
     elapsed = t1 - t0
     lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
-    dis = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    sct = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
+    dis = ntf + sct
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
     ms_step = elapsed / steps * 1e3
@@ -118,6 +129,7 @@ def run_gpu(cid, steps, warmup, dev):
         ms_per_step=ms_step, tokens_per_s=wl.T / (ms_step * 1e-3),
         step_gbps=B["step"] / (ms_step * 1e-3) / 1e9,
         layout_us=float(lay.mean()), dispatch_us=float(dis.mean()), combine_us=float(com.mean()),
+        notify_us=float(ntf.mean()), scatter_us=float(sct.mean()),
         dispatch_us_min=float(dis.min()), combine_us_min=float(com.min()),
         dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
         combine_gbps=B["combine"] / (com.mean() * 1e-6) / 1e9,
@@ -232,12 +244,21 @@ def main():
     if probe:
         log(f"[bench] probe copy {probe:.0f} GB/s")
 
-    # dominant kernel: the longer of dispatch and combine
-    if main_res["dispatch_us"] >= main_res["combine_us"]:
-        dom, dom_us, dom_bytes = "moedisp_dispatch", main_res["dispatch_us"], main_res["bytes"]["dispatch"]
+    # dominant kernel: the longer of the scatter kernel (which moves all of the
+    # dispatch's row bytes) and the combine kernel
+    B = main_res["bytes"]
+    if main_res["scatter_us"] >= main_res["combine_us"]:
+        dom, dom_us = "moedisp_scatter", main_res["scatter_us"]
+        dom_bytes = B["dispatch"] - B["notify"]
     else:
-        dom, dom_us, dom_bytes = "moedisp_combine", main_res["combine_us"], main_res["bytes"]["combine"]
+        dom, dom_us, dom_bytes = "moedisp_combine", main_res["combine_us"], B["combine"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    from combine_ep_get_dispatch_amd.profiling import load_traffic
+    measured = load_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.json"))
+    traffic = None
+    if measured and dom in measured["kernels"] and measured.get("workload") == main_res["workload"]:
+        kt = measured["kernels"][dom]
+        traffic = kt["fetch_bytes"] + kt["write_bytes"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -266,11 +287,13 @@ def main():
                              "tokens_per_s": main_res["dc_tokens_per_s"], "gbps": main_res["dc_gbps"],
                              "frac": main_res["dc_frac"]},
         "phases_us": {"layout": main_res["layout_us"], "dispatch": main_res["dispatch_us"],
+                      "dispatch_notify": main_res["notify_us"], "dispatch_scatter": main_res["scatter_us"],
                       "combine": main_res["combine_us"], "dispatch_min": main_res["dispatch_us_min"],
                       "combine_min": main_res["combine_us_min"]},
         "phases_gbps": {"dispatch": main_res["dispatch_gbps"], "combine": main_res["combine_gbps"]},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
+                     "kernel_us": dom_us},
         "probe_copy_gbps": probe,
         "other_workloads": others,
         "cpu_baseline": cpu,

@@ -36,8 +36,9 @@ DEV_DUPLICATE_EXPERT = 2
 DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
 
-EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch", "ep_combine",
-           "ep_check_status", "ep_status_string", "ep_probe_copy")
+EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch",
+           "ep_dispatch_notify", "ep_dispatch_scatter", "ep_combine", "ep_check_status", "ep_status_string",
+           "ep_probe_copy")
 
 
 class MoeDispError(RuntimeError):
@@ -80,6 +81,10 @@ def load(path: str = LIB_PATH):
     L.ep_get_dispatch_layout.restype = C.c_int
     L.ep_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch.restype = C.c_int
+    L.ep_dispatch_notify.argtypes = [S, P, P, P, P, C.c_size_t, P]
+    L.ep_dispatch_notify.restype = C.c_int
+    L.ep_dispatch_scatter.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_dispatch_scatter.restype = C.c_int
     L.ep_combine.argtypes = [S, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
     L.ep_combine.restype = C.c_int
     L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
@@ -129,6 +134,20 @@ def ep_get_dispatch_layout(shape, topk_idx, tokens_per_expert, tokens_per_group,
 def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales, recv_src_idx,
                 recv_weights, expert_offsets, slot_to_row, ws, stream=None):
     _check("ep_dispatch", load().ep_dispatch(
+        C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
+        _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
+        ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_dispatch_notify(shape, topk_idx, tokens_per_expert, expert_offsets, ws, stream=None):
+    _check("ep_dispatch_notify", load().ep_dispatch_notify(
+        C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(expert_offsets), _p(ws),
+        ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_dispatch_scatter(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                        recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
+    _check("ep_dispatch_scatter", load().ep_dispatch_scatter(
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
         _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
         ws.numel() * ws.element_size(), _s(stream)))
@@ -185,6 +204,14 @@ class EpBuffers:
         ep_dispatch(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,
                     self.recv_scales, self.recv_src_idx, self.recv_weights, self.expert_offsets, self.slot_to_row,
                     self.ws, stream)
+
+    def dispatch_notify(self, topk_idx, stream=None):
+        ep_dispatch_notify(self.shape, topk_idx, self.tokens_per_expert, self.expert_offsets, self.ws, stream)
+
+    def dispatch_scatter(self, x, x_scales, topk_idx, topk_weights, stream=None):
+        ep_dispatch_scatter(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,
+                            self.recv_scales, self.recv_src_idx, self.recv_weights, self.expert_offsets,
+                            self.slot_to_row, self.ws, stream)
 
     def combine(self, expert_out, out, out_dtype=BF16, check_src=True, stream=None):
         ep_combine(self.shape, expert_out, self.recv_src_idx if check_src else None, self.recv_weights,

@@ -160,18 +160,22 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
     return hip_status(launch_layout(a, (hipStream_t)stream));
 }
 
-int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
-                const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
-                int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row,
-                void* ws, size_t ws_bytes, void* stream) {
+// Checks shared by the dispatch calls; fills the launch arguments.  Pointers
+// a phase does not use may be passed as NULL-equivalents by the caller of that
+// phase only through the phase-specific wrappers below.
+static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                         const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x,
+                         float* recv_scales, int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
+                         int32_t* slot_to_row, void* ws, size_t ws_bytes, bool scatter, DispatchArgs* a) {
     int st = check_shape(s);
     if (st) return st;
     const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
     if (!tokens_per_expert || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
-    if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !recv_x || !recv_src_idx || !recv_weights ||
-                              !slot_to_row))
+    if (s->num_tokens > 0 && !topk_idx) return MOEDISP_ERR_INVALID_ARG;
+    if (scatter && s->num_tokens > 0 &&
+        (!x || !topk_weights || !recv_x || !recv_src_idx || !recv_weights || !slot_to_row))
         return MOEDISP_ERR_INVALID_ARG;
-    if (s->num_tokens > 0 && fp8 && (!x_scales || !recv_scales)) return MOEDISP_ERR_INVALID_ARG;
+    if (scatter && s->num_tokens > 0 && fp8 && (!x_scales || !recv_scales)) return MOEDISP_ERR_INVALID_ARG;
     if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOEDISP_ERR_MISALIGNED;
     if (!aligned(x_scales, 4) || !aligned(recv_scales, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
         !aligned(tokens_per_expert, 4) || !aligned(recv_src_idx, 4) || !aligned(recv_weights, 4) ||
@@ -179,28 +183,60 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
         return MOEDISP_ERR_MISALIGNED;
     if ((st = check_ws(s, ws, ws_bytes))) return st;
     const WsPlan w = plan_workspace(*s);
+    a->T = s->num_tokens;
+    a->k = s->topk;
+    a->E = s->num_experts;
+    a->row16 = (int)(row_bytes(*s) / 16);
+    a->scale_words = fp8 ? scales_per_row(*s) : 0;
+    a->capacity = s->num_tokens * s->topk;
+    a->plan = plan_dispatch(*s);
+    a->x = (const v4u*)x;
+    a->x_scales = fp8 ? x_scales : nullptr;
+    a->topk_idx = topk_idx;
+    a->topk_weights = topk_weights;
+    a->tokens_per_expert = tokens_per_expert;
+    a->recv_x = (v4u*)recv_x;
+    a->recv_scales = fp8 ? recv_scales : nullptr;
+    a->recv_src_idx = recv_src_idx;
+    a->recv_weights = recv_weights;
+    a->expert_offsets = const_cast<int32_t*>(expert_offsets);
+    a->slot_to_row = slot_to_row;
+    a->hdr = (WsHeader*)ws;
+    a->tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    return MOEDISP_OK;
+}
+
+int ep_dispatch_notify(const moedisp_shape* s, const int32_t* topk_idx, const int32_t* tokens_per_expert,
+                       int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
-    a.T = s->num_tokens;
-    a.k = s->topk;
-    a.E = s->num_experts;
-    a.row16 = (int)(row_bytes(*s) / 16);
-    a.scale_words = fp8 ? scales_per_row(*s) : 0;
-    a.capacity = s->num_tokens * s->topk;
-    a.plan = plan_dispatch(*s);
-    a.x = (const v4u*)x;
-    a.x_scales = fp8 ? x_scales : nullptr;
-    a.topk_idx = topk_idx;
-    a.topk_weights = topk_weights;
-    a.tokens_per_expert = tokens_per_expert;
-    a.recv_x = (v4u*)recv_x;
-    a.recv_scales = fp8 ? recv_scales : nullptr;
-    a.recv_src_idx = recv_src_idx;
-    a.recv_weights = recv_weights;
-    a.expert_offsets = expert_offsets;
-    a.slot_to_row = slot_to_row;
-    a.hdr = (WsHeader*)ws;
-    a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
-    return hip_status(launch_dispatch(a, (hipStream_t)stream));
+    const int st = dispatch_args(s, nullptr, nullptr, topk_idx, nullptr, tokens_per_expert, nullptr, nullptr, nullptr,
+                                 nullptr, expert_offsets, nullptr, ws, ws_bytes, false, &a);
+    if (st) return st;
+    return hip_status(launch_dispatch_notify(a, (hipStream_t)stream));
+}
+
+int ep_dispatch_scatter(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                        const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                        int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
+                        int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
+    DispatchArgs a;
+    const int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                                 recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a);
+    if (st) return st;
+    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+}
+
+int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row,
+                void* ws, size_t ws_bytes, void* stream) {
+    DispatchArgs a;
+    const int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                                 recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a);
+    if (st) return st;
+    const hipError_t e = launch_dispatch_notify(a, (hipStream_t)stream);
+    if (e != hipSuccess) return MOEDISP_ERR_HIP;
+    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
 }
 
 int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,

@@ -292,11 +292,13 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
 
 }  // namespace
 
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream) {
+hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(moedisp_count, dim3(a.plan.tiles), dim3(kThreads), (size_t)a.E * sizeof(int32_t), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream) {
     const DispatchPlan& p = a.plan;
-    hipLaunchKernelGGL(moedisp_count, dim3(p.tiles), dim3(kThreads), (size_t)a.E * sizeof(int32_t), stream, a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
     const dim3 grid(p.blocks), block(p.threads);
     switch (p.units_per_lane) {

@@ -127,7 +127,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
-hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream);

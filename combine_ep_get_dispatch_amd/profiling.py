@@ -1,0 +1,96 @@
+"""HBM traffic of the kernels from rocprofv3 hardware counters.
+
+Two counter runs of the same benchmark command (one with FETCH_SIZE, one with
+WRITE_SIZE; rocprofv3 reports both in KiB per kernel dispatch) give the bytes
+each kernel moved between L2 and the memory side.  Each is scaled by what the
+same counter reads for the library's plain copy kernel (ep_probe_copy) of a
+known size in the same run, so the figures are in bytes.  The result is stored
+with a hash of the kernel sources; the benchmark reports it only while the
+sources still match, i.e. only for the kernels the counters were taken on.
+
+    python -m combine_ep_get_dispatch_amd.profiling FETCH_DIR WRITE_DIR OUT_JSON PROBE_BYTES WORKLOAD
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+KERNELS = ("moedisp_layout", "moedisp_count", "moedisp_scatter", "moedisp_combine", "moedisp_probe_copy")
+
+
+def source_hash() -> str:
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "moedisp.h")]
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def short_name(kernel_name: str) -> str:
+    for k in KERNELS:
+        if k in kernel_name:
+            return k
+    return ""
+
+
+def read_counter(run_dir: str, counter: str) -> dict:
+    """{kernel: [per-dispatch value in KiB, ...]} from a rocprofv3 --pmc csv run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    out = defaultdict(list)
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                k = short_name(row.get("Kernel_Name", ""))
+                if k:
+                    out[k].append(float(row["Counter_Value"]))
+    return out
+
+
+def summarise(fetch_dir: str, write_dir: str, probe_bytes: int, workload: str) -> dict:
+    fetch = read_counter(fetch_dir, "FETCH_SIZE")
+    write = read_counter(write_dir, "WRITE_SIZE")
+    med = lambda v: sorted(v)[len(v) // 2]
+    f_probe, w_probe = med(fetch["moedisp_probe_copy"]), med(write["moedisp_probe_copy"])
+    f_scale = probe_bytes / f_probe   # bytes per counter unit
+    w_scale = probe_bytes / w_probe
+    kernels = {}
+    for k in KERNELS:
+        if k in fetch and k in write:
+            kernels[k] = {"fetch_bytes": med(fetch[k]) * f_scale, "write_bytes": med(write[k]) * w_scale,
+                          "fetch_kib_raw": med(fetch[k]), "write_kib_raw": med(write[k]),
+                          "dispatches": [len(fetch[k]), len(write[k])]}
+    return {"source_sha256": source_hash(), "workload": workload, "probe_bytes": probe_bytes,
+            "calibration": {"fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale},
+            "kernels": kernels}
+
+
+def load_traffic(path: str):
+    """Per-kernel traffic if it was measured on the current kernel sources, else None."""
+    try:
+        with open(path) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return d if d.get("source_sha256") == source_hash() else None
+
+
+if __name__ == "__main__":
+    fetch_dir, write_dir, out, probe, workload = sys.argv[1], sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5]
+    res = summarise(fetch_dir, write_dir, probe, workload)
+    with open(out, "w") as fh:
+        json.dump(res, fh, indent=1)
+    print(json.dumps(res, indent=1))

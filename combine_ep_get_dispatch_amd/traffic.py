@@ -27,5 +27,8 @@ def algorithmic_bytes(T: int, H: int, E: int, G: int, k: int, R: int, x_elt: int
                + T * out_row       # output
                + T * k * 4         # slot_to_row
                + R * 4)            # recv_weights
-    return dict(layout=layout, dispatch=dispatch, combine=combine, dispatch_combine=dispatch + combine,
-                step=layout + dispatch + combine)
+    # the notify phase of dispatch reads topk_idx and writes expert_offsets;
+    # the scatter phase moves everything else
+    notify = T * k * 4 + (E + 1) * 4
+    return dict(layout=layout, dispatch=dispatch, notify=notify, combine=combine,
+                dispatch_combine=dispatch + combine, step=layout + dispatch + combine)

@@ -124,6 +124,23 @@ int ep_dispatch(const moedisp_shape* shape, const void* x, const float* x_scales
                 int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets,
                 int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
 
+/* The two phases of ep_dispatch, for callers that time or schedule them
+ * apart (the page's high-throughput path likewise separates notify_dispatch,
+ * which exchanges counts, from dispatch, which moves rows).
+ * ep_dispatch_notify: per-tile expert counts of topk_idx (kept in `ws`) and
+ *   expert_offsets[E+1] (exclusive scan of tokens_per_expert).
+ * ep_dispatch_scatter: everything else ep_dispatch writes; it reads the counts
+ *   and expert_offsets that ep_dispatch_notify left for the same topk_idx and
+ *   tokens_per_expert in the same `ws` (stream-ordered before it).
+ * Arguments, layouts and status bits as for ep_dispatch. */
+int ep_dispatch_notify(const moedisp_shape* shape, const int32_t* topk_idx, const int32_t* tokens_per_expert,
+                       int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
+int ep_dispatch_scatter(const moedisp_shape* shape, const void* x, const float* x_scales,
+                        const int32_t* topk_idx, const float* topk_weights,
+                        const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                        int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
+                        int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+
 /* Combine: the reverse of dispatch through its handle.
  *   out[t][h] = sum over j = 0..k-1 in ascending order, skipping masked slots,
  *               of recv_weights[r] * expert_out[r][h] with r = slot_to_row[t][j],

@@ -107,6 +107,21 @@ def test_host_checks_dispatch(lib):
                            1 << 30, None) == B.ERR_INVALID_ARG
 
 
+def test_host_checks_dispatch_phases(lib):
+    s = shape()
+    # notify: null topk_idx, null expert_offsets, misaligned offsets, small ws
+    assert lib.ep_dispatch_notify(C.byref(s), None, p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_notify(C.byref(s), p(), p(), None, p(), 1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_notify(C.byref(s), p(), p(), p(2), p(), 1 << 30, None) == B.ERR_MISALIGNED
+    assert lib.ep_dispatch_notify(C.byref(s), p(), p(), p(), p(), 64, None) == B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.ep_dispatch_notify(C.byref(shape(E=255)), p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+    # scatter: null row buffers, misaligned rows
+    assert lib.ep_dispatch_scatter(C.byref(s), None, None, p(), p(), p(), p(), None, p(), p(), p(), p(), p(),
+                                   1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_scatter(C.byref(s), p(8), None, p(), p(), p(), p(), None, p(), p(), p(), p(), p(),
+                                   1 << 30, None) == B.ERR_MISALIGNED
+
+
 def test_host_checks_combine(lib):
     assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
     assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED

@@ -108,6 +108,21 @@ def test_dispatch_deterministic_under_repeats(orc, dev):
     GH.assert_dispatch_equal(ref, GH.oracle_run(orc, wl), wl)
 
 
+def test_notify_then_scatter_equals_dispatch(orc, dev):
+    """The two phases called apart give exactly what ep_dispatch gives."""
+    for wl in (W.make_workload("phases_bf16", 700, 512, 64, 8, 4, seed=91, routing="zipf", mask_frac=0.1),
+               W.make_workload("phases_fp8", 90, 1024, 32, 8, 8, seed=92, x_dtype=W.X_FP8, scale_block=128)):
+        shape = GH.shape_of(wl)
+        inputs = GH.GpuInputs(wl, dev)
+        b = M.EpBuffers(shape, dev)
+        b.layout(inputs.topk_idx)
+        b.dispatch_notify(inputs.topk_idx)
+        b.dispatch_scatter(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+        assert b.status() == 0
+        g, _ = GH.fetch_dispatch(b, wl)
+        GH.assert_dispatch_equal(g, GH.oracle_run(orc, wl), wl)
+
+
 def test_round_trip_identity_experts(dev):
     """dispatch -> identity experts (the received rows themselves) -> combine
     with weights summing to one returns x within one bf16 ulp."""
