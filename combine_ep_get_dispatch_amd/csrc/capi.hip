@@ -64,7 +64,8 @@ DispatchPlan plan_dispatch(const moedisp_shape& s) {
     p.blocks = token_blocks > 0 ? (int)(token_blocks * splits) : 1;
     // lanes: whole waves covering one pass of the column range, and at least
     // one lane per slot of the workgroup
-    p.units_per_lane = 4;
+    // one 16-byte unit per lane and pass (up to 1024 lanes; wider rows loop)
+    p.units_per_lane = 1;
     const int units = (row16 + splits - 1) / splits;
     int threads = ((units + p.units_per_lane - 1) / p.units_per_lane + 63) / 64 * 64;
     const int slot_lanes = (bt * k + 63) / 64 * 64;
@@ -150,6 +151,17 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
     a.k = s->topk;
     a.E = s->num_experts;
     a.G = s->num_groups;
+    a.id_bits = 0;
+    while ((1 << a.id_bits) < a.E) ++a.id_bits;
+    const uint32_t per_group = (uint32_t)(a.E / a.G);
+    a.pg_shift = -1;
+    a.pg_magic = 0;
+    if ((per_group & (per_group - 1)) == 0) {
+        a.pg_shift = 0;
+        while ((1u << a.pg_shift) < per_group) ++a.pg_shift;
+    } else {
+        a.pg_magic = (uint32_t)((1ull << 32) / per_group + 1);
+    }
     a.topk_idx = topk_idx;
     a.tokens_per_expert = tokens_per_expert;
     a.tokens_per_group = tokens_per_group;

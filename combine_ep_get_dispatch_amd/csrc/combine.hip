@@ -16,8 +16,9 @@
 // the handle is checked there (row inside the receive buffer and, when
 // recv_src_idx is given, naming this token) and bad slots are skipped with
 // BAD_HANDLE raised.  Each lane owns U 16-byte units (8 bf16) of the output
-// row: it issues all k*U gathered 16-byte loads before the first FMA, so each
-// lane keeps k*U loads in flight, then accumulates slot by slot in order.
+// row (U = 1 for k = 8: 896 lanes cover a 7168-wide row in one pass): it
+// issues all k*U gathered 16-byte loads before the first FMA, so each lane
+// keeps k*U loads in flight, then accumulates slot by slot in order.
 // With k known at compile time (1, 2, 4, 8) the slot loop is unrolled; other
 // k take the generic loop.
 #include "moedisp_internal.h"
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
-    constexpr int U = (KC == 1 || KC == 2 || KC == 4) ? 4 : 2;  // = combine_units_per_lane(k)
+    constexpr int U = (KC == 1 || KC == 2 || KC == 4) ? 2 : 1;  // = combine_units_per_lane(k)
     hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(a.threads), 0, stream, a);
     return hipGetLastError();
 }

@@ -28,7 +28,8 @@
 //    and while the copy saturates HBM those polls queue behind the stores.
 //    No atomics decide any order, so the result is deterministic.
 // The scatter then streams: each lane loads U 16-byte units of the source row
-// once (the first pass is issued before the row computation) and stores them,
+// (U = 1 by default, up to 1024 lanes per workgroup) once - the first pass is
+// issued before the row computation - and stores them,
 // non-temporally, to each of the token's k destination rows.  Workgroups of
 // column range 0 write the handle (slot_to_row, recv_src_idx, recv_weights)
 // and fp8 scales.  Rows outside their expert's segment (or the buffer) are not

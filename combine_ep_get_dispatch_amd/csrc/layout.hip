@@ -17,11 +17,14 @@
 namespace moedisp {
 namespace {
 
-// Lanes among `active` whose key equals this lane's key (keys < 2^nbits).
-// Every lane of the wave must execute this (it issues nbits ballots).
+// Lanes among `active` whose key equals this lane's key (keys < 2^nbits,
+// nbits <= 12).  Every lane of the wave must execute this (it issues nbits
+// ballots).
 __device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active) {
     uint64_t peers = active;
-    for (int b = 0; b < nbits; ++b) {
+#pragma unroll
+    for (int b = 0; b < 12; ++b) {
+        if (b >= nbits) break;  // nbits is uniform
         const bool bit = (key >> b) & 1u;
         const uint64_t ones = __ballot(bit);
         peers &= bit ? ones : ~ones;
@@ -29,6 +32,14 @@ __device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active)
     return peers;
 }
 
+// Group of expert id: id / (E/G) by a shift (power-of-two group sizes) or by
+// a multiply-high with a host-computed reciprocal (exact for id, E <= 4096).
+__device__ inline uint32_t group_of(uint32_t id, const LayoutArgs& a) {
+    return a.pg_shift >= 0 ? id >> a.pg_shift : __umulhi(id, a.pg_magic);
+}
+
+// KMAX: compile-time bound on k; a token's routing row lives in registers.
+template <int KMAX>
 __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
     extern __shared__ int32_t dyn[];  // [E + G] counts, then the staged routing rows
     const int EG = a.E + a.G;
@@ -68,25 +79,32 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
     __syncthreads();
 
     const bool have = tid < nt;
-    const int per_group = a.E / a.G;
-    const int nbits = a.E > 1 ? 32 - __clz(a.E - 1) : 0;
     const uint64_t below = (1ull << lane) - 1ull;
     uint32_t gmask = 0;
     uint32_t err = 0;
-    for (int j = 0; j < k; ++j) {
-        int id = have ? s_ids[tid * kp + j] : -1;
+    int ids[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        int id = (have && j < k) ? s_ids[tid * kp + j] : -1;
         if (id < -1 || id >= a.E) {
             err |= MOEDISP_DEV_BAD_EXPERT_ID;
             id = -1;
         }
+        ids[j] = id;
+    }
+#pragma unroll
+    for (int j = 1; j < KMAX; ++j)
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj)
+            if (ids[j] >= 0 && ids[j] == ids[jj]) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (j >= k) break;  // k is uniform
+        const int id = ids[j];
         const bool routed = id >= 0;
-        if (routed) {
-            for (int jj = 0; jj < j; ++jj)
-                if (s_ids[tid * kp + jj] == id) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
-            gmask |= 1u << (id / per_group);
-        }
+        if (routed) gmask |= 1u << group_of((uint32_t)id, a);
         const uint64_t active = __ballot(routed);
-        const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, nbits, active);
+        const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
         if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
     }
     for (int g = 0; g < a.G; ++g) {
@@ -134,7 +152,12 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)(a.E + a.G + kLayoutTokensPerBlock * (a.k | 1)) * sizeof(int32_t);
-    hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kThreads), lds, stream, a);
+    if (a.k <= 8)
+        hipLaunchKernelGGL((moedisp_layout<8>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
+    else if (a.k <= 16)
+        hipLaunchKernelGGL((moedisp_layout<16>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL((moedisp_layout<kMaxTopk>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 

@@ -59,8 +59,8 @@ struct CombinePlan {
 
 constexpr int kMaxCombineThreads = 1024;
 // 16-byte units each combine lane owns per pass (k loads in flight per unit);
-// k = 1, 2, 4 have unrolled kernels with 4 units, every other k uses 2
-inline int combine_units_per_lane(int k) { return (k == 1 || k == 2 || k == 4) ? 4 : 2; }
+// k = 1, 2, 4 have unrolled kernels with 2 units, every other k uses 1
+inline int combine_units_per_lane(int k) { return (k == 1 || k == 2 || k == 4) ? 2 : 1; }
 
 struct WsPlan {
     int layout_blocks;
@@ -82,6 +82,9 @@ inline int scales_per_row(const moedisp_shape& s) {
 
 struct LayoutArgs {
     int T, k, E, G;
+    int id_bits;        // bits of an expert id (ceil(log2 E))
+    int pg_shift;       // log2(E/G) if E/G is a power of two, else -1
+    uint32_t pg_magic;  // floor(2^32 / (E/G)) + 1 otherwise
     const int32_t* topk_idx;
     int32_t* tokens_per_expert;
     int32_t* tokens_per_group;

@@ -77,6 +77,10 @@ EDGE = {
     "E4096": lambda: W.make_workload("E4096", 300, 64, 4096, 32, 8, seed=52, routing="zipf", mask_frac=0.1),
     "E1": lambda: W.make_workload("E1", 70, 64, 1, 1, 1, seed=53),
     "tokens_per_tile_edges": lambda: W.make_workload("tile_edges", 1025, 256, 64, 8, 6, seed=54),
+    "groups_of_3": lambda: W.make_workload("groups_of_3", 300, 64, 24, 8, 4, seed=55),
+    "groups_of_6_zipf": lambda: W.make_workload("groups_of_6", 513, 64, 12, 2, 3, seed=56, routing="zipf",
+                                                mask_frac=0.2),
+    "groups_of_96": lambda: W.make_workload("groups_of_96", 200, 64, 3072, 32, 8, seed=57, routing="zipf"),
 }
 
 
