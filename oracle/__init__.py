@@ -19,6 +19,10 @@ LIB = os.path.join(_HERE, "liboracle.so")
 ERR_BAD_EXPERT = 1
 ERR_DUP_EXPERT = 2
 
+# scale formats of the quantise-on-dispatch oracle
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+
 GCC_FLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
              "-Wall", "-Wextra"]
 
@@ -64,6 +68,17 @@ class Oracle:
         L.oracle_dispatch.restype = C.c_int
         L.oracle_combine.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, P, P, P, P, P]
         L.oracle_combine.restype = C.c_int
+        L.oracle_f32_to_e4m3_array.argtypes = [P, P, C.c_int64]
+        L.oracle_f32_to_e4m3_array.restype = None
+        L.oracle_e4m3_to_double_array.argtypes = [P, P, C.c_int64]
+        L.oracle_e4m3_to_double_array.restype = None
+        L.oracle_ue8m0_exponent.argtypes = [C.c_float]
+        L.oracle_ue8m0_exponent.restype = C.c_int
+        L.oracle_quant_rows.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, P, P, P]
+        L.oracle_quant_rows.restype = C.c_int
+        L.oracle_dispatch_quant.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                            P, P, P, P, P, P, P, P, P]
+        L.oracle_dispatch_quant.restype = C.c_int
         self.L = L
         self.path = path
 
@@ -128,6 +143,59 @@ class Oracle:
         return of, ob
 
 
+    # -- quantise-on-dispatch ------------------------------------------------
+
+    def f32_to_e4m3(self, a) -> np.ndarray:
+        a = _c(a, np.float32)
+        out = np.empty(a.shape, np.uint8)
+        self.L.oracle_f32_to_e4m3_array(_p(a), _p(out), a.size)
+        return out
+
+    def e4m3_to_f64(self, codes) -> np.ndarray:
+        c = _c(codes, np.uint8)
+        out = np.empty(c.shape, np.float64)
+        self.L.oracle_e4m3_to_double_array(_p(c), _p(out), c.size)
+        return out
+
+    def ue8m0_exponent(self, amax: float) -> int:
+        return int(self.L.oracle_ue8m0_exponent(float(amax)))
+
+    def quant_rows(self, x_bf16, block: int, fmt: int):
+        """x_bf16: uint16 [T][H].  Returns (codes uint8 [T][H], scales): scales
+        float32 [T][H/block] for fmt SCALE_FP32, uint8 exponent bytes for
+        SCALE_UE8M0."""
+        x = _c(x_bf16, np.uint16)
+        T, H = x.shape
+        q = np.zeros((T, H), np.uint8)
+        sc = np.zeros((T, H // block), np.float32 if fmt == SCALE_FP32 else np.uint8)
+        if self.L.oracle_quant_rows(T, H, block, fmt, _p(x), _p(q), _p(sc)) < 0:
+            raise ValueError("oracle_quant_rows: bad arguments")
+        return q, sc
+
+    def dispatch_quant(self, x_bf16, topk_idx, topk_weights, E: int, block: int, fmt: int):
+        """Quantise-on-dispatch.  Returns the dict of dispatch() with recv_x
+        holding E4M3 codes uint8 [T*k][H] and recv_scales [T*k][H/block]
+        (float32, or uint8 for UE8M0)."""
+        x = _c(x_bf16, np.uint16)
+        idx = _c(topk_idx, np.int32)
+        T, k = idx.shape
+        H = x.shape[1]
+        cap = T * k
+        rq = np.zeros((cap, H), np.uint8)
+        rs = np.zeros((cap, H // block), np.float32 if fmt == SCALE_FP32 else np.uint8)
+        src = np.full(cap, -1, np.int32)
+        rw = np.zeros(cap, np.float32)
+        off = np.zeros(E + 1, np.int32)
+        s2r = np.zeros((T, k), np.int32)
+        w = _c(topk_weights, np.float32)
+        st = self.L.oracle_dispatch_quant(T, k, E, H, block, fmt, _p(x), _p(idx), _p(w), _p(rq), _p(rs),
+                                          _p(src), _p(rw), _p(off), _p(s2r))
+        if st < 0:
+            raise ValueError("oracle_dispatch_quant: bad arguments")
+        return dict(recv_x=rq, recv_scales=rs, recv_src_idx=src, recv_weights=rw,
+                    expert_offsets=off, slot_to_row=s2r, status=st)
+
+
 _default = None
 
 
@@ -155,3 +223,11 @@ def dispatch(x, x_scales, topk_idx, topk_weights, E):
 
 def combine(expert_out_bf16, recv_weights, slot_to_row, want_f32=True, want_bf16=True):
     return get().combine(expert_out_bf16, recv_weights, slot_to_row, want_f32, want_bf16)
+
+
+def quant_rows(x_bf16, block, fmt):
+    return get().quant_rows(x_bf16, block, fmt)
+
+
+def dispatch_quant(x_bf16, topk_idx, topk_weights, E, block, fmt):
+    return get().dispatch_quant(x_bf16, topk_idx, topk_weights, E, block, fmt)

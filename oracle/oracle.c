@@ -35,6 +35,24 @@
  *     multiply-add, then rounds once to bf16 (nearest, ties to even); a token
  *     whose every slot is masked gets +0.
  *
+ * Quantise-on-dispatch (same page: the commit messages that give the
+ * low-latency dispatch E4M3 payloads with FP32 scales per 32 elements, then
+ * UE8M0 scale bytes per 32 elements, and that keep tiny nonzero MXFP8 blocks
+ * alive at UE8M0 code zero; the review file table's FP8 E4M3 quantization
+ * helpers for that dispatch).  The page prints no formula; the readings are:
+ *   - payload codes are OCP E4M3 ("e4m3fn": bias 7, 3 fraction bits, no
+ *     infinity, largest finite 448);
+ *   - a block is B consecutive channels of one token; amax is the largest
+ *     |x| in it;
+ *   - FP32 scales: scale = amax / 448 rounded to binary32 (1 for an all-zero
+ *     block); each element is x / scale rounded to binary32, then to the
+ *     nearest E4M3 value, ties to even, magnitudes beyond 448 saturating;
+ *   - UE8M0 scales: scale = 2^s with s the smallest integer for which
+ *     448 * 2^s >= amax, clamped to [-127, 127] (s = 0 for an all-zero
+ *     block); the scale byte is s + 127; each element is x * 2^-s rounded to
+ *     binary32 (exact unless far below the E4M3 range), then to E4M3 as above.
+ *     Clamping at -127 (code zero) keeps tiny nonzero blocks nonzero.
+ *
  * Error codes (bit mask, same meaning as the library's device status bits):
  *   1  an expert id outside {-1} U [0,E)      (slot treated as masked)
  *   2  an expert id repeated within one token  (each copy is its own slot)
@@ -250,4 +268,140 @@ int oracle_combine(int T, int k, int H, int64_t R, const uint16_t* expert_out,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* E4M3 (OCP e4m3fn) codes                                                   */
+/* Code bits: sign, 4 exponent bits e, 3 fraction bits f.                    */
+/*   e >= 1: (1 + f/8) * 2^(e-7);  e = 0: (f/8) * 2^-6;  e = 15, f = 7: NaN. */
+/* ------------------------------------------------------------------------ */
+
+double oracle_e4m3_to_double(uint8_t c)
+{
+    int e = (c >> 3) & 15, f = c & 7;
+    double mag;
+    if (e == 15 && f == 7) return NAN;
+    if (e == 0)
+        mag = ldexp(f / 8.0, -6);
+    else
+        mag = ldexp(1.0 + f / 8.0, e - 7);
+    return (c & 0x80) ? -mag : mag;
+}
+
+/* Nearest E4M3 value, ties to the even code, |v| beyond 448 saturating to
+ * +-448.  The E4M3 grid near |v| in [2^p, 2^(p+1)) is spaced 2^(p-3); below
+ * 2^-6 (subnormals) it stays 2^-9.  |v| is divided by the spacing (exact), rounded
+ * to an integer by rint() (nearest-even) and scaled back; the encoding of the
+ * result then follows from the definition above.  The sign is kept, so a
+ * negative value that rounds to zero gives the code 0x80.  NaN gives 0x7F
+ * with its sign. */
+uint8_t oracle_f32_to_e4m3(float v)
+{
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return (uint8_t)(sign | 0x7F);
+    double a = fabs((double)v);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7E);
+    if (a == 0.0) return sign;
+    int p;
+    frexp(a, &p);                 /* a in [2^(p-1), 2^p) */
+    int lo = p - 1;               /* a in [2^lo, 2^(lo+1)) */
+    if (lo < -6) lo = -6;         /* subnormal range keeps the 2^-9 spacing */
+    double spacing = ldexp(1.0, lo - 3);
+    double r = rint(a / spacing) * spacing;
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6)) return (uint8_t)(sign | (uint8_t)(r / ldexp(1.0, -9)));
+    int q;
+    frexp(r, &q);                 /* r in [2^(q-1), 2^q) */
+    int ex = q - 1;
+    int f = (int)((r / ldexp(1.0, ex) - 1.0) * 8.0);
+    return (uint8_t)(sign | (uint8_t)(((ex + 7) << 3) | f));
+}
+
+void oracle_f32_to_e4m3_array(const float* in, uint8_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e4m3(in[i]);
+}
+
+void oracle_e4m3_to_double_array(const uint8_t* in, double* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_to_double(in[i]);
+}
+
+/* UE8M0 exponent of a block: the smallest s in [-127, 127] with
+ * 448 * 2^s >= amax; 0 for amax == 0.  amax is a finite binary32 >= 0. */
+int oracle_ue8m0_exponent(float amax)
+{
+    if (amax == 0.0f) return 0;
+    int s = -127;
+    while (s < 127 && ldexp(448.0, s) < (double)amax) ++s;
+    return s;
+}
+
+#define ORACLE_SCALE_FP32 0
+#define ORACLE_SCALE_UE8M0 1
+
+/* Quantise T rows of H bf16 values in blocks of B channels.
+ * q: E4M3 codes [T][H].  scales: fp32 [T][H/B] (fmt 0) or UE8M0 bytes
+ * [T][H/B] (fmt 1).  Returns 0, or -1 for bad arguments. */
+int oracle_quant_rows(int T, int H, int B, int fmt, const uint16_t* x, uint8_t* q, uint8_t* scales)
+{
+    if (T < 0 || H <= 0 || B <= 0 || H % B != 0) return -1;
+    if (fmt != ORACLE_SCALE_FP32 && fmt != ORACLE_SCALE_UE8M0) return -1;
+    int nb = H / B;
+    for (int t = 0; t < T; ++t) {
+        for (int b = 0; b < nb; ++b) {
+            const uint16_t* xb = x + (int64_t)t * H + (int64_t)b * B;
+            uint8_t* qb = q + (int64_t)t * H + (int64_t)b * B;
+            float amax = 0.0f;
+            for (int i = 0; i < B; ++i) {
+                float m = fabsf((float)oracle_bf16_to_double(xb[i]));
+                if (m > amax) amax = m;
+            }
+            if (fmt == ORACLE_SCALE_FP32) {
+                float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+                for (int i = 0; i < B; ++i) {
+                    float v = (float)oracle_bf16_to_double(xb[i]) / scale;
+                    qb[i] = oracle_f32_to_e4m3(v);
+                }
+                memcpy(scales + ((int64_t)t * nb + b) * 4, &scale, 4);
+            } else {
+                int sx = oracle_ue8m0_exponent(amax);
+                for (int i = 0; i < B; ++i) {
+                    float v = ldexpf((float)oracle_bf16_to_double(xb[i]), -sx);
+                    qb[i] = oracle_f32_to_e4m3(v);
+                }
+                scales[(int64_t)t * nb + b] = (uint8_t)(sx + 127);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Dispatch with quantisation: every token row is quantised once (as
+ * oracle_quant_rows), then the codes and the token's scales are dispatched
+ * exactly as oracle_dispatch moves rows and scales.  recv_q [T*k][H] codes,
+ * recv_scales [T*k][H/B] fp32 or bytes; other outputs and the status as for
+ * oracle_dispatch. */
+int oracle_dispatch_quant(int T, int k, int E, int H, int B, int fmt,
+                          const uint16_t* x, const int32_t* topk_idx, const float* topk_weights,
+                          uint8_t* recv_q, uint8_t* recv_scales,
+                          int32_t* recv_src_idx, float* recv_weights,
+                          int32_t* expert_offsets, int32_t* slot_to_row)
+{
+    if (T < 0 || H <= 0 || B <= 0 || H % B != 0) return -1;
+    int64_t scale_bytes = (int64_t)(H / B) * (fmt == ORACLE_SCALE_FP32 ? 4 : 1);
+    uint8_t* q = (uint8_t*)malloc((size_t)T * H + 1);
+    uint8_t* sc = (uint8_t*)malloc((size_t)(T * scale_bytes) + 1);
+    if (!q || !sc) {
+        free(q);
+        free(sc);
+        return -1;
+    }
+    int st = oracle_quant_rows(T, H, B, fmt, x, q, sc);
+    if (st == 0)
+        st = oracle_dispatch(T, k, E, H, scale_bytes, q, sc, topk_idx, topk_weights, recv_q, recv_scales,
+                             recv_src_idx, recv_weights, expert_offsets, slot_to_row);
+    free(q);
+    free(sc);
+    return st;
 }

@@ -322,6 +322,200 @@ def check_error_status(orc):
     assert st2 == 1, "a negative id other than -1 is a bad id"
 
 
+# ---------------------------------------------------------------------------
+# quantise-on-dispatch: E4M3 codes, FP32 and UE8M0 block scales
+# ---------------------------------------------------------------------------
+
+SCALE_FP32, SCALE_UE8M0 = 0, 1
+
+
+def torch_e4m3_values() -> np.ndarray:
+    """Value of every E4M3 code from torch's float8_e4m3fn type (a library
+    decoding, independent of the oracle)."""
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
+def torch_e4m3_codes(v: np.ndarray) -> np.ndarray:
+    """torch's float -> float8_e4m3fn cast (nearest-even; only used in range)."""
+    t = torch.from_numpy(np.ascontiguousarray(v, np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e4m3_half_spacing(v: np.ndarray) -> np.ndarray:
+    """Half the E4M3 grid spacing at |v| (<= 448): 2^(p-4) in [2^p, 2^(p+1)),
+    2^-10 below 2^-6."""
+    a = np.abs(np.asarray(v, np.float64))
+    p = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return 2.0 ** (p - 4)
+
+
+def check_e4m3_codes(orc):
+    """Decoding of all 256 codes equals torch's; encoding every finite value
+    gives its code back; 0x7F and 0xFF are the NaNs; 448 is the largest."""
+    codes = np.arange(256, dtype=np.uint8)
+    dec = orc.e4m3_to_f64(codes)
+    ref = torch_e4m3_values()
+    nan = np.isnan(ref)
+    assert np.flatnonzero(nan).tolist() == [0x7F, 0xFF]
+    assert np.array_equal(np.isnan(dec), nan)
+    assert np.array_equal(dec[~nan], ref[~nan]), "E4M3 decoding differs from float8_e4m3fn"
+    assert np.array_equal(np.signbit(dec[~nan]), codes[~nan] >= 0x80)
+    assert dec[0x7E] == 448.0 and dec[0x01] == 2.0 ** -9 and dec[0x08] == 2.0 ** -6
+    assert np.array_equal(orc.f32_to_e4m3(dec[~nan].astype(np.float32)), codes[~nan]), "encode(decode(c)) != c"
+
+
+def check_e4m3_rounding(orc):
+    """Nearest-even rounding against torch's cast on random values, exact
+    midpoints and their neighbours; saturation beyond 448."""
+    rng = np.random.default_rng(31)
+    mag = 2.0 ** rng.uniform(-13, np.log2(448.0), 30000)
+    v = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    v = v[np.abs(v) <= 448.0]
+    assert np.array_equal(orc.f32_to_e4m3(v), torch_e4m3_codes(v)), "rounding differs from the library cast"
+    vals = np.unique(torch_e4m3_values()[:0x7F])            # 0 .. 448, ascending
+    mid = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)     # exact in binary32
+    for sgn in (1.0, -1.0):
+        m = (sgn * mid).astype(np.float32)
+        c = orc.f32_to_e4m3(m)
+        assert np.all((c & 1) == 0), "a tie must round to the even code"
+        assert np.array_equal(c, torch_e4m3_codes(m))
+        up = np.nextafter(np.abs(m), np.float32(np.inf)).astype(np.float32) * np.float32(sgn)
+        dn = np.nextafter(np.abs(m), np.float32(0)).astype(np.float32) * np.float32(sgn)
+        cu, cd = orc.f32_to_e4m3(up), orc.f32_to_e4m3(dn)
+        assert np.array_equal(np.abs(orc.e4m3_to_f64(cu)), vals[1:]), "above a midpoint rounds up"
+        assert np.array_equal(np.abs(orc.e4m3_to_f64(cd)), vals[:-1]), "below a midpoint rounds down"
+    big = np.array([448.5, 463.9, 464.0, 480.0, 1e6, 3e38, np.inf], np.float32)
+    assert np.all(orc.f32_to_e4m3(big) == 0x7E) and np.all(orc.f32_to_e4m3(-big) == 0xFE), "saturation"
+    assert orc.f32_to_e4m3(np.array([0.0, -0.0, 2.0 ** -11, -2.0 ** -11], np.float32)).tolist() == \
+        [0x00, 0x80, 0x00, 0x80], "signed zeros"
+
+
+def quant_test_rows(seed=41, B=32, nblk=24):
+    """bf16 rows with normal blocks, all-zero blocks, signed-zero blocks, tiny
+    (subnormal) blocks, huge blocks and one dominant element per block."""
+    rng = np.random.default_rng(seed)
+    T, H = 6, B * nblk
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    xb = x.reshape(T, nblk, B)
+    xb[0, 1] = 0.0
+    xb[0, 2] = -0.0
+    xb[1, 3] *= 2.0 ** -130                     # bf16 subnormals
+    xb[1, 4] = 0.0
+    xb[1, 4, 5] = 2.0 ** -133                   # one tiny nonzero element
+    xb[2, 5] *= 1e30
+    xb[2, 6] *= 1e-20
+    xb[3, :, 0] = rng.choice([-1, 1], nblk) * 2.0 ** rng.integers(-20, 20, nblk)
+    xb[4] *= 448.0
+    xb[5] = rng.integers(-4, 5, (nblk, B)) * 0.125    # many ties of the grid
+    return torch_bf16_bits(x)
+
+
+def check_quant_fp32(orc, B=32):
+    x = quant_test_rows(B=B)
+    T, H = x.shape
+    q, sc = orc.quant_rows(x, B, SCALE_FP32)
+    xf = bf16_to_f64(x).reshape(T, H // B, B)
+    amax = np.abs(xf).max(axis=-1)
+    s = sc.astype(np.float64)
+    zero = amax == 0
+    assert np.all(s[zero] == 1.0), "an all-zero block has scale 1"
+    assert np.all(np.abs(s[~zero] * 448.0 - amax[~zero]) <= amax[~zero] * 2.0 ** -24 + 2.0 ** -149 * 448), \
+        "scale is amax/448 to binary32 precision"
+    dec = orc.e4m3_to_f64(q).reshape(xf.shape)
+    assert not np.isnan(dec).any()
+    v = xf / s[..., None]                        # exact quotient
+    err = np.abs(dec - np.clip(v, -448, 448))
+    bound = e4m3_half_spacing(np.clip(v, -448, 448)) + np.abs(v) * 2.0 ** -23
+    assert np.all(err <= bound), "codes are the nearest E4M3 values of x/scale"
+    arg = np.abs(xf).argmax(axis=-1)
+    top = np.take_along_axis(q.reshape(xf.shape), arg[..., None], -1)[..., 0]
+    normal_scale = s >= 2.0 ** -126
+    assert np.all((top[~zero & normal_scale] & 0x7F) == 0x7E), "the block's largest element maps to +-448"
+    assert np.array_equal(np.signbit(dec), np.signbit(xf)), "signs (zeros included) are kept"
+    # blocks are independent: changing one block changes only its scale and codes
+    x2 = x.copy()
+    x2[0, 7 * B + 3] = torch_bf16_bits(np.array([1e4], np.float32))[0]
+    q2, sc2 = orc.quant_rows(x2, B, SCALE_FP32)
+    diff_blocks = np.flatnonzero((q2 != q).reshape(T, -1, B).any(-1).ravel() | (sc2 != sc).ravel())
+    assert diff_blocks.tolist() == [7], "only the changed block may change"
+
+
+def check_quant_ue8m0(orc, B=32):
+    x = quant_test_rows(B=B)
+    T, H = x.shape
+    q, sc = orc.quant_rows(x, B, SCALE_UE8M0)
+    xf = bf16_to_f64(x).reshape(T, H // B, B)
+    amax = np.abs(xf).max(axis=-1)
+    s = sc.astype(np.int64) - 127
+    zero = amax == 0
+    assert np.all(s[zero] == 0), "an all-zero block has scale 2^0"
+    nz = ~zero
+    assert np.all(448.0 * np.ldexp(1.0, s[nz]) >= amax[nz]), "no element needs saturation"
+    assert np.all((s[nz] == -127) | (448.0 * np.ldexp(1.0, s[nz] - 1) < amax[nz])), "s is the smallest such"
+    dec = orc.e4m3_to_f64(q).reshape(xf.shape)
+    v = xf * np.ldexp(1.0, -s)[..., None]        # exact
+    assert np.all(np.abs(dec - v) <= e4m3_half_spacing(v) * (1 + 2.0 ** -20)), "nearest E4M3 of x * 2^-s"
+    assert np.array_equal(np.signbit(dec), np.signbit(xf))
+    tiny = amax[1, 3:5]
+    assert np.all(s[1, 3:5] == -127) and np.all(tiny > 0)
+    assert np.all(q.reshape(xf.shape)[1, 4, 5] == 0x08), "a tiny nonzero block stays nonzero at code zero"
+    # exponent choice over every positive finite bf16 amax
+    a_bits = np.arange(1, 0x7F80, dtype=np.uint16)
+    rows = np.zeros((a_bits.size, B), np.uint16)
+    rows[:, 0] = a_bits
+    _, sb = orc.quant_rows(rows, B, SCALE_UE8M0)
+    a = bf16_to_f64(a_bits)
+    ss = sb[:, 0].astype(np.int64) - 127
+    assert np.all(448.0 * np.ldexp(1.0, ss) >= a)
+    assert np.all((ss == -127) | (448.0 * np.ldexp(1.0, ss - 1) < a))
+
+
+def check_quant_example(orc, path=os.path.join(GOLDEN, "quant_example.json")):
+    with open(path) as f:
+        g = json.load(f)
+    def val(s):
+        if "^" in s:
+            base, ex = s.split("^")
+            return (-1.0 if base.startswith("-") else 1.0) * 2.0 ** int(ex)
+        return float(s)
+    x = torch_bf16_bits(np.array([[val(v) for v in g["x"]]], np.float32))
+    assert np.array_equal(bf16_to_f64(x)[0], [val(v) for v in g["x"]]), "example values are exact in bf16"
+    q, sc = orc.quant_rows(x, g["B"], SCALE_FP32)
+    assert q[0].tolist() == g["codes_fp32"]
+    assert sc[0].astype(np.float64).tolist() == [m * 2.0 ** p for m, p in g["scales_fp32"]]
+    q, sc = orc.quant_rows(x, g["B"], SCALE_UE8M0)
+    assert q[0].tolist() == g["codes_ue8m0"]
+    assert sc[0].tolist() == g["scales_ue8m0"]
+
+
+def check_dispatch_quant(orc, wl, B, fmt):
+    """Quantise-on-dispatch = the token's quantised row and scales, moved by
+    the (separately pinned) dispatch: same handle as the bf16 dispatch, and
+    every received row holds its source token's codes and scales."""
+    d = orc.dispatch_quant(wl.x, wl.topk_idx, wl.topk_weights, wl.E, B, fmt)
+    ref = orc.dispatch(wl.x, None, wl.topk_idx, wl.topk_weights, wl.E)
+    for key in ("expert_offsets", "slot_to_row", "recv_src_idx", "recv_weights"):
+        assert np.array_equal(d[key], ref[key]), key
+    q, sc = orc.quant_rows(wl.x, B, fmt)
+    R = wl.num_routed
+    src = d["recv_src_idx"][:R]
+    assert np.array_equal(d["recv_x"][:R], q[src])
+    assert np.array_equal(d["recv_scales"][:R].view(np.uint8), sc[src].view(np.uint8))
+    assert d["status"] == ref["status"]
+
+
+def check_quant_all(orc):
+    check_e4m3_codes(orc)
+    check_e4m3_rounding(orc)
+    check_quant_fp32(orc, 32)
+    check_quant_fp32(orc, 128)
+    check_quant_ue8m0(orc, 32)
+    check_quant_example(orc)
+    wl = W.make_workload("quant_mid", 200, 256, 32, 4, 4, seed=25, mask_frac=0.1)
+    check_dispatch_quant(orc, wl, 128, SCALE_FP32)
+    check_dispatch_quant(orc, wl, 32, SCALE_UE8M0)
+
+
 ALL_BASIC = [check_bf16_rounding, check_bruteforce, check_combine_exact_dyadic, check_combine_k1_inverse,
              check_worked_example, check_error_status]
 
@@ -343,6 +537,7 @@ def run_all(orc):
     """Every pin in one go (used by the mutation test)."""
     for chk in ALL_BASIC:
         chk(orc)
+    check_quant_all(orc)
     for wl in small_configs():
         check_layout_invariants(orc, wl)
         check_dispatch_invariants(orc, wl)

@@ -47,6 +47,50 @@ MUTANTS = {
     "bf16_spacing": ("double spacing = ldexp(1.0, p - 8);", "double spacing = ldexp(1.0, p - 9);"),
     # bf16 rounding: subnormal spacing wrong
     "bf16_subnormal": ("if (p < -125) p = -125;", "if (p < -126) p = -126;"),
+    # E4M3: truncation instead of nearest-even
+    "e4m3_truncate": ("double r = rint(a / spacing) * spacing;", "double r = floor(a / spacing) * spacing;"),
+    # E4M3: ties away from zero instead of to even
+    "e4m3_ties_away": ("double r = rint(a / spacing) * spacing;", "double r = round(a / spacing) * spacing;"),
+    # E4M3: exponent bias 8 in the decoder
+    "e4m3_bias": ("mag = ldexp(1.0 + f / 8.0, e - 7);", "mag = ldexp(1.0 + f / 8.0, e - 8);"),
+    # E4M3: two fraction bits kept instead of three
+    "e4m3_spacing": ("double spacing = ldexp(1.0, lo - 3);", "double spacing = ldexp(1.0, lo - 2);"),
+    # E4M3: subnormal range ends one binade too low
+    "e4m3_subnormal": ("if (lo < -6) lo = -6;", "if (lo < -7) lo = -7;"),
+    # E4M3: overflow gives NaN instead of saturating
+    "e4m3_no_saturation": ("if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
+                           "if (a >= 464.0) return (uint8_t)(sign | 0x7F);"),
+    # E4M3: sign dropped
+    "e4m3_sign": ("uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = v < 0 ? 0x80 : 0x00;"),
+    # FP32 scales: wrong format maximum
+    "scale_max_240": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                      "float scale = amax > 0.0f ? amax / 240.0f : 1.0f;"),
+    # FP32 scales: all-zero block gets scale 0
+    "scale_zero_block": ("float scale = amax > 0.0f ? amax / 448.0f : 1.0f;",
+                         "float scale = amax > 0.0f ? amax / 448.0f : 0.0f;"),
+    # amax of signed values instead of magnitudes
+    "amax_signed": ("float m = fabsf((float)oracle_bf16_to_double(xb[i]));",
+                    "float m = (float)oracle_bf16_to_double(xb[i]);"),
+    # FP32 scales: multiply instead of divide
+    "scale_multiply": ("float v = (float)oracle_bf16_to_double(xb[i]) / scale;",
+                       "float v = (float)oracle_bf16_to_double(xb[i]) * scale;"),
+    # UE8M0: one binade too large (<= instead of <)
+    "ue8m0_off_by_one": ("while (s < 127 && ldexp(448.0, s) < (double)amax) ++s;",
+                         "while (s < 127 && ldexp(448.0, s) <= (double)amax) ++s;"),
+    # UE8M0: no clamp at code zero (tiny blocks flushed)
+    "ue8m0_no_low_clamp": ("    int s = -127;\n", "    int s = -150;\n"),
+    # UE8M0: scaling in the wrong direction
+    "ue8m0_direction": ("float v = ldexpf((float)oracle_bf16_to_double(xb[i]), -sx);",
+                        "float v = ldexpf((float)oracle_bf16_to_double(xb[i]), sx);"),
+    # UE8M0: bias 128 in the scale byte
+    "ue8m0_bias": ("scales[(int64_t)t * nb + b] = (uint8_t)(sx + 127);",
+                   "scales[(int64_t)t * nb + b] = (uint8_t)(sx + 128);"),
+    # quantiser: block offset forgotten (every block reads the first)
+    "quant_block_offset": ("const uint16_t* xb = x + (int64_t)t * H + (int64_t)b * B;",
+                           "const uint16_t* xb = x + (int64_t)t * H;"),
+    # quantised dispatch: the scales are not moved with the rows
+    "quant_scales_dropped": ("st = oracle_dispatch(T, k, E, H, scale_bytes, q, sc, topk_idx",
+                             "st = oracle_dispatch(T, k, E, H, scale_bytes, q, NULL, topk_idx"),
 }
 
 

@@ -73,3 +73,30 @@ def test_full_size_dispatch_invariants(orc):
     wl = W.config(2)
     K.check_layout_invariants(orc, wl)
     K.check_dispatch_invariants(orc, wl)
+
+
+def test_e4m3_codes_match_library_decoding(orc):
+    K.check_e4m3_codes(orc)
+
+
+def test_e4m3_rounding_ties_and_saturation(orc):
+    K.check_e4m3_rounding(orc)
+
+
+@pytest.mark.parametrize("B", [32, 128])
+def test_quant_fp32_scales(orc, B):
+    K.check_quant_fp32(orc, B)
+
+
+def test_quant_ue8m0_scales(orc):
+    K.check_quant_ue8m0(orc, 32)
+
+
+def test_quant_worked_example(orc):
+    K.check_quant_example(orc)
+
+
+@pytest.mark.parametrize("B,fmt", [(32, K.SCALE_FP32), (128, K.SCALE_FP32), (32, K.SCALE_UE8M0)])
+def test_dispatch_quant_is_quantise_then_dispatch(orc, B, fmt):
+    wl = W.make_workload("quant_mid", 300, 256, 64, 8, 6, seed=26, routing="zipf", mask_frac=0.05)
+    K.check_dispatch_quant(orc, wl, B, fmt)
