@@ -143,6 +143,52 @@ def run_gpu(cid, steps, warmup, dev):
     return res
 
 
+def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
+    """Time quantise-on-dispatch (notify + quantising scatter) on config `cid`."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    from combine_ep_get_dispatch_amd import workloads as W
+    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS, algorithmic_bytes_quant
+
+    wl = W.config(cid)
+    bufs = M.EpBuffers(shape_of(M, W, wl), dev).enable_quant(block, fmt)
+    x, _, idx, w = make_inputs(wl, dev)
+    bufs.layout(idx)
+    bufs.dispatch_quant(x, idx, w)
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} on quantised config {cid}")
+    R = int(bufs.expert_offsets[-1].item())
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        bufs.dispatch_notify(idx, stream)
+        bufs.dispatch_scatter_quant(x, idx, w, stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        bufs.dispatch_notify(idx, stream)
+        evs[i][1].record(stream)
+        bufs.dispatch_scatter_quant(x, idx, w, stream)
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    if bufs.status():
+        raise RuntimeError(f"device status after quantised steps on config {cid}")
+    ntf = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    sct = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    B = algorithmic_bytes_quant(wl.T, wl.H, wl.E, wl.k, R, block, 4 if fmt == M.SCALE_FP32 else 1)
+    dis = ntf + sct
+    res = dict(workload=wl.name, block=block, scale_fmt="fp32" if fmt == M.SCALE_FP32 else "ue8m0", R=R,
+               notify_us=float(ntf.mean()), scatter_us=float(sct.mean()), dispatch_us=float(dis.mean()),
+               dispatch_tokens_per_s=wl.T / (dis.mean() * 1e-6),
+               dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
+               scatter_gbps=B["scatter"] / (sct.mean() * 1e-6) / 1e9, bytes=B)
+    res["scatter_frac"] = res["scatter_gbps"] / HBM_PEAK_GBPS
+    del bufs, x, idx, w
+    torch.cuda.empty_cache()
+    return res
+
+
 def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
     """Achievable HBM copy bandwidth (read + write bytes) with the library's
     plain 16-byte copy kernel."""
@@ -211,6 +257,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-quant", action="store_true", help="skip the quantise-on-dispatch timings")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -240,6 +287,13 @@ def main():
                                                        "tokens_per_s", "dc_tokens_per_s", "dc_gbps", "dc_frac",
                                                        "layout_us", "dispatch_us", "combine_us",
                                                        "dispatch_gbps", "combine_gbps")}
+    quant = {}
+    if not args.no_quant:
+        import combine_ep_get_dispatch_amd as M
+        for block, fmt, tag in ((128, M.SCALE_FP32, "fp32_b128"), (32, M.SCALE_UE8M0, "ue8m0_b32")):
+            log(f"[bench] quantised dispatch {tag}")
+            quant[tag] = run_gpu_quant(args.config, block, fmt, max(20, args.steps // 4),
+                                       max(5, args.warmup // 4), dev)
     probe = None if args.no_probe else probe_copy_gbps(dev)
     if probe:
         log(f"[bench] probe copy {probe:.0f} GB/s")
@@ -253,11 +307,11 @@ def main():
     else:
         dom, dom_us, dom_bytes = "moedisp_combine", main_res["combine_us"], B["combine"]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    from combine_ep_get_dispatch_amd.profiling import load_traffic
+    from combine_ep_get_dispatch_amd.profiling import kernel_traffic, load_traffic
     measured = load_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     traffic = None
-    if measured and dom in measured["kernels"] and measured.get("workload") == main_res["workload"]:
-        kt = measured["kernels"][dom]
+    kt = kernel_traffic(measured, dom) if measured and measured.get("workload") == main_res["workload"] else None
+    if kt:
         traffic = kt["fetch_bytes"] + kt["write_bytes"]
 
     cpu = None
@@ -296,6 +350,7 @@ def main():
                      "kernel_us": dom_us},
         "probe_copy_gbps": probe,
         "other_workloads": others,
+        "quant_dispatch": quant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

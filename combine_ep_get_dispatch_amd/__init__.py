@@ -4,12 +4,14 @@ The product is the C library libmoedisp.so (include/moedisp.h); this package
 holds its HIP sources (csrc/), its build script, the Python binding and the
 seeded synthetic workloads.
 """
-from .binding import (BF16, FP8_E4M3, FP32, EpBuffers, MoeDispError, ep_check_status, ep_combine, ep_dispatch,
-                      ep_dispatch_notify, ep_dispatch_scatter,
+from .binding import (BF16, FP8_E4M3, FP32, SCALE_FP32, SCALE_UE8M0, EpBuffers, MoeDispError, ep_check_status,
+                      ep_combine, ep_dispatch, ep_dispatch_notify, ep_dispatch_quant, ep_dispatch_scatter,
+                      ep_dispatch_scatter_quant,
                       ep_get_dispatch_layout, ep_probe_copy, ep_status_string,
                       ep_workspace_bytes, ep_workspace_init, load, moedisp_shape)
 
-__all__ = ["BF16", "FP8_E4M3", "FP32", "EpBuffers", "MoeDispError", "ep_check_status", "ep_combine", "ep_dispatch",
-           "ep_dispatch_notify", "ep_dispatch_scatter",
+__all__ = ["BF16", "FP8_E4M3", "FP32", "SCALE_FP32", "SCALE_UE8M0", "EpBuffers", "MoeDispError", "ep_check_status",
+           "ep_combine", "ep_dispatch", "ep_dispatch_notify", "ep_dispatch_quant", "ep_dispatch_scatter",
+           "ep_dispatch_scatter_quant",
            "ep_get_dispatch_layout", "ep_probe_copy", "ep_status_string",
            "ep_workspace_bytes", "ep_workspace_init", "load", "moedisp_shape"]

@@ -22,6 +22,10 @@ BF16 = 0
 FP8_E4M3 = 1
 FP32 = 2
 
+# scale formats of quantise-on-dispatch (moedisp_scale_fmt)
+SCALE_FP32 = 0
+SCALE_UE8M0 = 1
+
 # host return codes
 OK = 0
 ERR_INVALID_ARG = -1
@@ -37,8 +41,8 @@ DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
 
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch",
-           "ep_dispatch_notify", "ep_dispatch_scatter", "ep_combine", "ep_check_status", "ep_status_string",
-           "ep_probe_copy")
+           "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
+           "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy")
 
 
 class MoeDispError(RuntimeError):
@@ -85,6 +89,11 @@ def load(path: str = LIB_PATH):
     L.ep_dispatch_notify.restype = C.c_int
     L.ep_dispatch_scatter.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch_scatter.restype = C.c_int
+    L.ep_dispatch_quant.argtypes = [S, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_dispatch_quant.restype = C.c_int
+    L.ep_dispatch_scatter_quant.argtypes = [S, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P, P,
+                                            C.c_size_t, P]
+    L.ep_dispatch_scatter_quant.restype = C.c_int
     L.ep_combine.argtypes = [S, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
     L.ep_combine.restype = C.c_int
     L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
@@ -153,6 +162,23 @@ def ep_dispatch_scatter(shape, x, x_scales, topk_idx, topk_weights, tokens_per_e
         ws.numel() * ws.element_size(), _s(stream)))
 
 
+def ep_dispatch_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
+                      recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
+    _check("ep_dispatch_quant", load().ep_dispatch_quant(
+        C.byref(shape), int(quant_block), int(scale_fmt), _p(x), _p(topk_idx), _p(topk_weights),
+        _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
+        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_dispatch_scatter_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
+                              recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws,
+                              stream=None):
+    _check("ep_dispatch_scatter_quant", load().ep_dispatch_scatter_quant(
+        C.byref(shape), int(quant_block), int(scale_fmt), _p(x), _p(topk_idx), _p(topk_weights),
+        _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
+        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
 def ep_combine(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, out, out_dtype, ws, stream=None):
     _check("ep_combine", load().ep_combine(
         C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(out),
@@ -212,6 +238,27 @@ class EpBuffers:
         ep_dispatch_scatter(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,
                             self.recv_scales, self.recv_src_idx, self.recv_weights, self.expert_offsets,
                             self.slot_to_row, self.ws, stream)
+
+    def enable_quant(self, quant_block: int, scale_fmt: int):
+        """Receive buffers of quantise-on-dispatch: E4M3 codes [T*k][H] and one
+        scale per block of `quant_block` channels (float32 or uint8)."""
+        T, H, k = self.shape.num_tokens, self.shape.hidden, self.shape.topk
+        self.quant_block, self.scale_fmt = int(quant_block), int(scale_fmt)
+        nsc = H // self.quant_block if H % self.quant_block == 0 else 0
+        self.recv_q = torch.empty((T * k, H), dtype=torch.uint8, device=self.device)
+        sdt = torch.float32 if scale_fmt == SCALE_FP32 else torch.uint8
+        self.recv_qscales = torch.empty((T * k, nsc), dtype=sdt, device=self.device)
+        return self
+
+    def dispatch_quant(self, x, topk_idx, topk_weights, stream=None):
+        ep_dispatch_quant(self.shape, self.quant_block, self.scale_fmt, x, topk_idx, topk_weights,
+                          self.tokens_per_expert, self.recv_q, self.recv_qscales, self.recv_src_idx,
+                          self.recv_weights, self.expert_offsets, self.slot_to_row, self.ws, stream)
+
+    def dispatch_scatter_quant(self, x, topk_idx, topk_weights, stream=None):
+        ep_dispatch_scatter_quant(self.shape, self.quant_block, self.scale_fmt, x, topk_idx, topk_weights,
+                                  self.tokens_per_expert, self.recv_q, self.recv_qscales, self.recv_src_idx,
+                                  self.recv_weights, self.expert_offsets, self.slot_to_row, self.ws, stream)
 
     def combine(self, expert_out, out, out_dtype=BF16, check_src=True, stream=None):
         ep_combine(self.shape, expert_out, self.recv_src_idx if check_src else None, self.recv_weights,

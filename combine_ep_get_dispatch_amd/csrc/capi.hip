@@ -38,42 +38,56 @@ static int check_shape(const moedisp_shape* s) {
 
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-DispatchPlan plan_dispatch(const moedisp_shape& s) {
+// Scatter plan for rows of `units` lane units whose k copies write
+// `write_per_token` bytes; column ranges are whole multiples of `align` units.
+static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_token, int units, int align) {
     DispatchPlan p;
     const int T = s.num_tokens, k = s.topk;
     // copy: >= 64 KiB of row stores per workgroup
-    const long long write_per_token = (long long)k * (long long)row_bytes(s);
     int bt = 1;
     while (bt < kMaxBlockTokens && write_per_token * bt < 64 * 1024 && 2 * bt * k <= kMaxDispatchThreads) bt *= 2;
-    // count tiles: 16 tokens (at least bt), doubled until there are at most
-    // kMaxTiles (a slot's row sums one count per earlier tile)
+    // count tiles: 16 tokens (>= bt, as bt <= 16), doubled until there are at
+    // most kMaxTiles (a slot's row sums one count per earlier tile); this
+    // depends only on T and k
     int tt = 16;
     while (tt < bt) tt *= 2;
     while ((long long)tt * kMaxTiles < T && 2 * tt * k <= kMaxTileSlots) tt *= 2;
     p.tile_tokens = tt;
     p.tiles = T > 0 ? ceil_div(T, tt) : 1;
     p.tile_stride = (p.tiles + 3) / 4 * 4;
-    const int row16 = (int)(row_bytes(s) / 16);
     // split rows across workgroups while the grid is small (decode-sized T)
     int splits = 1;
     const long long token_blocks = ceil_div(T, bt);
-    while (token_blocks * splits < 1024 && row16 / (splits * 2) >= kThreads / 2) splits *= 2;
+    while (token_blocks * splits < 1024 && units / (splits * 2) >= kThreads / 2) splits *= 2;
+    int per = ceil_div(units, splits);
+    per = ceil_div(per, align) * align;
+    p.split_units = per;
+    p.col_splits = ceil_div(units, per);
     p.block_tokens = bt;
-    p.col_splits = splits;
     // at least one workgroup, so that workgroup 0 runs the total check
-    p.blocks = token_blocks > 0 ? (int)(token_blocks * splits) : 1;
-    // lanes: whole waves covering one pass of the column range, and at least
-    // one lane per slot of the workgroup
-    // one 16-byte unit per lane and pass (up to 1024 lanes; wider rows loop)
+    p.blocks = token_blocks > 0 ? (int)(token_blocks * p.col_splits) : 1;
+    // lanes: whole waves covering one pass of the column range (one unit per
+    // lane and pass, up to 1024 lanes; wider rows loop), and at least one
+    // lane per slot of the workgroup
     p.units_per_lane = 1;
-    const int units = (row16 + splits - 1) / splits;
-    int threads = ((units + p.units_per_lane - 1) / p.units_per_lane + 63) / 64 * 64;
+    int threads = (per + 63) / 64 * 64;
     const int slot_lanes = (bt * k + 63) / 64 * 64;
     if (threads < slot_lanes) threads = slot_lanes;
     if (threads < kThreads) threads = kThreads;
     if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
     p.threads = threads;
     return p;
+}
+
+DispatchPlan plan_dispatch(const moedisp_shape& s) {
+    return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1);
+}
+
+// Quantising scatter: a lane unit is 16 channels (32 source bytes, 16 code
+// bytes); column ranges are whole waves so that no scale block (<= 64 lanes)
+// straddles two of them.
+DispatchPlan plan_dispatch_quant(const moedisp_shape& s) {
+    return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64);
 }
 
 CombinePlan plan_combine(const moedisp_shape& s) {
@@ -199,7 +213,11 @@ static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_s
     a->k = s->topk;
     a->E = s->num_experts;
     a->row16 = (int)(row_bytes(*s) / 16);
+    a->out16 = a->row16;
     a->scale_words = fp8 ? scales_per_row(*s) : 0;
+    a->q_block_lanes = 0;
+    a->q_scales_per_row = 0;
+    a->recv_qscales = nullptr;
     a->capacity = s->num_tokens * s->topk;
     a->plan = plan_dispatch(*s);
     a->x = (const v4u*)x;
@@ -249,6 +267,82 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
     const hipError_t e = launch_dispatch_notify(a, (hipStream_t)stream);
     if (e != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+}
+
+// Checks of the quantising dispatch calls; fills the launch arguments.
+static int quant_args(const moedisp_shape* s, int32_t quant_block, int32_t scale_fmt, const void* x,
+                      const int32_t* topk_idx, const float* topk_weights, const int32_t* tokens_per_expert,
+                      void* recv_x, void* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                      const int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes,
+                      DispatchArgs* a) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->x_dtype != MOEDISP_BF16) return MOEDISP_ERR_UNSUPPORTED;
+    if (scale_fmt != MOEDISP_SCALE_FP32 && scale_fmt != MOEDISP_SCALE_UE8M0) return MOEDISP_ERR_UNSUPPORTED;
+    if (quant_block < 32 || quant_block > 1024 || (quant_block & (quant_block - 1)) != 0)
+        return MOEDISP_ERR_UNSUPPORTED;
+    if (s->hidden % quant_block != 0) return MOEDISP_ERR_INVALID_ARG;
+    if (!tokens_per_expert || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (!topk_idx || !x || !topk_weights || !recv_x || !recv_scales || !recv_src_idx ||
+                              !recv_weights || !slot_to_row))
+        return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOEDISP_ERR_MISALIGNED;
+    if ((scale_fmt == MOEDISP_SCALE_FP32 && !aligned(recv_scales, 4)) || !aligned(topk_idx, 4) ||
+        !aligned(topk_weights, 4) || !aligned(tokens_per_expert, 4) || !aligned(recv_src_idx, 4) ||
+        !aligned(recv_weights, 4) || !aligned(expert_offsets, 4) || !aligned(slot_to_row, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    const WsPlan w = plan_workspace(*s);
+    a->T = s->num_tokens;
+    a->k = s->topk;
+    a->E = s->num_experts;
+    a->row16 = (int)((size_t)s->hidden * 2 / 16);
+    a->out16 = s->hidden / 16;
+    a->scale_words = 0;
+    a->q_block_lanes = quant_block / 16;
+    a->q_scales_per_row = s->hidden / quant_block;
+    a->capacity = s->num_tokens * s->topk;
+    a->plan = plan_dispatch_quant(*s);
+    a->x = (const v4u*)x;
+    a->x_scales = nullptr;
+    a->topk_idx = topk_idx;
+    a->topk_weights = topk_weights;
+    a->tokens_per_expert = tokens_per_expert;
+    a->recv_x = (v4u*)recv_x;
+    a->recv_scales = nullptr;
+    a->recv_src_idx = recv_src_idx;
+    a->recv_weights = recv_weights;
+    a->expert_offsets = const_cast<int32_t*>(expert_offsets);
+    a->slot_to_row = slot_to_row;
+    a->recv_qscales = recv_scales;
+    a->hdr = (WsHeader*)ws;
+    a->tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    return MOEDISP_OK;
+}
+
+int ep_dispatch_scatter_quant(const moedisp_shape* s, int32_t quant_block, int32_t scale_fmt, const void* x,
+                              const int32_t* topk_idx, const float* topk_weights,
+                              const int32_t* tokens_per_expert, void* recv_x, void* recv_scales,
+                              int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
+                              int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
+    DispatchArgs a;
+    const int st = quant_args(s, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
+                              recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, &a);
+    if (st) return st;
+    return hip_status(launch_dispatch_scatter_quant(a, scale_fmt, (hipStream_t)stream));
+}
+
+int ep_dispatch_quant(const moedisp_shape* s, int32_t quant_block, int32_t scale_fmt, const void* x,
+                      const int32_t* topk_idx, const float* topk_weights, const int32_t* tokens_per_expert,
+                      void* recv_x, void* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                      int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
+    DispatchArgs a;
+    const int st = quant_args(s, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
+                              recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, &a);
+    if (st) return st;
+    // the count kernel's tile plan is the shape's, shared with the copy path
+    if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
+    return hip_status(launch_dispatch_scatter_quant(a, scale_fmt, (hipStream_t)stream));
 }
 
 int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,

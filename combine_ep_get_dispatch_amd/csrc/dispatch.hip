@@ -117,67 +117,67 @@ __global__ __launch_bounds__(kThreads) void moedisp_count(DispatchArgs a) {
     if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
 }
 
-// U: 16-byte units per lane per pass.
-template <int U>
-__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchArgs a) {
-    const DispatchPlan& P = a.plan;
-    extern __shared__ int32_t dyn[];  // routing of the tile up to this workgroup's last slot
-    int32_t* s_ids = dyn;
-    __shared__ int32_t s_pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
-    __shared__ int32_t s_base[kMaxBlockSlots];  // expert_offsets[e]
-    __shared__ int32_t s_len[kMaxBlockSlots];   // tokens_per_expert[e]
-    __shared__ int32_t s_rows[kMaxBlockSlots];
-    __shared__ int32_t s_routed;
-    __shared__ uint32_t s_err;
+// LDS of a scatter workgroup besides the staged routing ids.
+struct ScatterSmem {
+    int32_t pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
+    int32_t base[kMaxBlockSlots];  // expert_offsets[e]
+    int32_t len[kMaxBlockSlots];   // tokens_per_expert[e]
+    int32_t rows[kMaxBlockSlots];  // receive row of each slot of the workgroup, -1 if none
+    int32_t routed;
+    uint32_t err;
+};
 
+// Which tokens and columns a scatter workgroup owns.
+struct ScatterBlock {
+    int blk_t0, blk_nt, blk_slots;
+    int tile, tile_t0, first;  // first: slots of the tile before this workgroup's
+    int split;
+};
+
+__device__ inline ScatterBlock scatter_block(const DispatchArgs& a) {
+    const DispatchPlan& P = a.plan;
+    ScatterBlock b;
+    const int tok = blockIdx.x / P.col_splits;
+    b.split = blockIdx.x - tok * P.col_splits;
+    b.blk_t0 = tok * P.block_tokens;
+    b.blk_nt = max(0, min(P.block_tokens, a.T - b.blk_t0));
+    b.blk_slots = b.blk_nt * a.k;
+    b.tile = b.blk_t0 / P.tile_tokens;  // tile_tokens is a multiple of block_tokens
+    b.tile_t0 = b.tile * P.tile_tokens;
+    b.first = (b.blk_t0 - b.tile_t0) * a.k;
+    return b;
+}
+
+// Receive rows of the workgroup's slots into sm.rows (whole workgroup; has
+// barriers).  Returns this lane's BAD_LAYOUT bits.
+__device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, int32_t* s_ids, ScatterSmem& sm) {
+    const DispatchPlan& P = a.plan;
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
     const int k = a.k;
     const int E = a.E;
-    const int tok = blockIdx.x / P.col_splits;
-    const int split = blockIdx.x - tok * P.col_splits;
-    const int blk_t0 = tok * P.block_tokens;
-    const int blk_nt = max(0, min(P.block_tokens, a.T - blk_t0));
-    const int blk_slots = blk_nt * k;
-    const int tile = blk_t0 / P.tile_tokens;  // tile_tokens is a multiple of block_tokens
-    const int tile_t0 = tile * P.tile_tokens;
-    const int first = (blk_t0 - tile_t0) * k;  // slots of the tile before this workgroup's
-    const int per_split = (a.row16 + P.col_splits - 1) / P.col_splits;
-    const int c0 = split * per_split;
-    const int c1 = min(a.row16, c0 + per_split);
-
-    // first pass of source units: independent of the rows, so issued first
-    v4u pre[U];
-    if (blk_nt > 0) {
-        const v4u* src = a.x + (size_t)blk_t0 * a.row16;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int cc = c0 + tid + u * nth;
-            if (cc < c1) pre[u] = src[cc];
-        }
-    }
-    for (int i = tid; i < first + blk_slots; i += nth) {
-        const int id = a.topk_idx[(size_t)tile_t0 * k + i];
+    for (int i = tid; i < b.first + b.blk_slots; i += nth) {
+        const int id = a.topk_idx[(size_t)b.tile_t0 * k + i];
         s_ids[i] = (id >= 0 && id < E) ? id : -1;
     }
-    for (int q = tid; q < blk_slots; q += nth) s_pre[q] = 0;
+    for (int q = tid; q < b.blk_slots; q += nth) sm.pre[q] = 0;
     if (tid == 0) {
-        s_routed = 0;
-        s_err = 0;
+        sm.routed = 0;
+        sm.err = 0;
     }
     __syncthreads();
 
     // counts of each slot's expert in the earlier tiles: L lanes per slot,
     // 16-byte loads of the expert's contiguous count column
-    if (blk_slots > 0) {
-        const int L = nth / blk_slots;  // >= 1: the plan keeps blk_slots <= threads
-        if (tid < L * blk_slots) {
+    if (b.blk_slots > 0) {
+        const int L = nth / b.blk_slots;  // >= 1: the plan keeps blk_slots <= threads
+        if (tid < L * b.blk_slots) {
             const int q = tid / L;
             const int l = tid - q * L;
-            const int e = s_ids[first + q];
+            const int e = s_ids[b.first + q];
             if (e >= 0) {
                 const int32_t* col = a.tile_counts + (size_t)e * P.tile_stride;  // 16-byte aligned
-                const int n4 = tile >> 2;
+                const int n4 = b.tile >> 2;
                 int32_t sum = 0;
                 for (int c = l; c < n4; c += 4 * L) {
                     int4 v[4];
@@ -188,64 +188,118 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
                     for (int u = 0; u < 4; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
                 }
                 if (l == 0) {
-                    for (int j = n4 * 4; j < tile; ++j) sum += col[j];
-                    s_base[q] = a.expert_offsets[e];
-                    s_len[q] = a.tokens_per_expert[e];
+                    for (int j = n4 * 4; j < b.tile; ++j) sum += col[j];
+                    sm.base[q] = a.expert_offsets[e];
+                    sm.len[q] = a.tokens_per_expert[e];
                 }
-                if (sum) atomicAdd(&s_pre[q], sum);
+                if (sum) atomicAdd(&sm.pre[q], sum);
             }
         }
     }
     __syncthreads();
 
-    // rows of this workgroup's slots
     uint32_t err = 0;
-    for (int q = tid; q < blk_slots; q += nth) {
-        const int s = first + q;
+    for (int q = tid; q < b.blk_slots; q += nth) {
+        const int s = b.first + q;
         const int e = s_ids[s];
         int row = -1;
         if (e >= 0) {
             int before = 0;
             for (int u = 0; u < s; ++u) before += s_ids[u] == e;
-            const long long base = s_base[q];
-            const long long r = base + s_pre[q] + before;
-            if (r < 0 || r < base || r >= base + s_len[q] || r >= a.capacity)
+            const long long base = sm.base[q];
+            const long long r = base + sm.pre[q] + before;
+            if (r < 0 || r < base || r >= base + sm.len[q] || r >= a.capacity)
                 err |= MOEDISP_DEV_BAD_LAYOUT;
             else
                 row = (int)r;
         }
-        s_rows[q] = row;
+        sm.rows[q] = row;
     }
     __syncthreads();
+    return err;
+}
 
-    // handle: slot -> row, row -> source token and weight, fp8 scales
-    if (split == 0) {
-        for (int q = tid; q < blk_slots; q += nth) {
-            const size_t slot = (size_t)blk_t0 * k + q;
-            const int row = s_rows[q];
-            a.slot_to_row[slot] = row;
-            if (row >= 0) {
-                a.recv_src_idx[row] = blk_t0 + q / k;
-                a.recv_weights[row] = a.topk_weights[slot];
-            }
+// Handle of the workgroup's slots: slot -> row, row -> source token and weight.
+__device__ void write_handle(const DispatchArgs& a, const ScatterBlock& b, const ScatterSmem& sm) {
+    for (int q = threadIdx.x; q < b.blk_slots; q += blockDim.x) {
+        const size_t slot = (size_t)b.blk_t0 * a.k + q;
+        const int row = sm.rows[q];
+        a.slot_to_row[slot] = row;
+        if (row >= 0) {
+            a.recv_src_idx[row] = b.blk_t0 + q / a.k;
+            a.recv_weights[row] = a.topk_weights[slot];
         }
-        if (a.scale_words) {
-            const int n = blk_slots * a.scale_words;
+    }
+}
+
+// Workgroup 0: the routed slots must add up to the layout's total.  Whole
+// workgroup (has a barrier); returns this lane's BAD_LAYOUT bit.
+__device__ uint32_t check_total(const DispatchArgs& a, ScatterSmem& sm) {
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    const int n = a.T * a.k;
+    int32_t routed = 0;
+    for (int i0 = tid; i0 < n; i0 += 8 * nth) {
+        int32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nth < n) ? a.topk_idx[i0 + u * nth] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) routed += (v[u] >= 0 && v[u] < a.E);
+    }
+    if (routed) atomicAdd(&sm.routed, routed);
+    __syncthreads();
+    return (tid == 0 && sm.routed != a.expert_offsets[a.E]) ? MOEDISP_DEV_BAD_LAYOUT : 0u;
+}
+
+__device__ inline void publish_err(const DispatchArgs& a, ScatterSmem& sm, uint32_t err) {
+    if (err) atomicOr(&sm.err, err);
+    __syncthreads();
+    if (threadIdx.x == 0 && sm.err) atomicOr(&a.hdr->status, sm.err);
+}
+
+// U: 16-byte units per lane per pass.
+template <int U>
+__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchArgs a) {
+    extern __shared__ int32_t dyn[];  // routing of the tile up to this workgroup's last slot
+    __shared__ ScatterSmem sm;
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    const int k = a.k;
+    const ScatterBlock b = scatter_block(a);
+    const int c0 = b.split * a.plan.split_units;
+    const int c1 = min(a.row16, c0 + a.plan.split_units);
+
+    // first pass of source units: independent of the rows, so issued first
+    v4u pre[U];
+    if (b.blk_nt > 0) {
+        const v4u* src = a.x + (size_t)b.blk_t0 * a.row16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c0 + tid + u * nth;
+            if (cc < c1) pre[u] = src[cc];
+        }
+    }
+    uint32_t err = scatter_rows(a, b, dyn, sm);
+
+    if (b.split == 0) {
+        write_handle(a, b, sm);
+        if (a.scale_words) {  // fp8 input: its scales travel with the row
+            const int n = b.blk_slots * a.scale_words;
             for (int i = tid; i < n; i += nth) {
                 const int q = i / a.scale_words;
                 const int c = i - q * a.scale_words;
-                const int row = s_rows[q];
+                const int row = sm.rows[q];
                 if (row >= 0)
                     a.recv_scales[(size_t)row * a.scale_words + c] =
-                        a.x_scales[(size_t)(blk_t0 + q / k) * a.scale_words + c];
+                        a.x_scales[(size_t)(b.blk_t0 + q / k) * a.scale_words + c];
             }
         }
     }
 
     // row scatter: each 16-byte unit is loaded once and stored k times
-    for (int tt = 0; tt < blk_nt; ++tt) {
-        const v4u* src = a.x + (size_t)(blk_t0 + tt) * a.row16;
-        const int32_t* rows = s_rows + tt * k;
+    for (int tt = 0; tt < b.blk_nt; ++tt) {
+        const v4u* src = a.x + (size_t)(b.blk_t0 + tt) * a.row16;
+        const int32_t* rows = sm.rows + tt * k;
         for (int c = c0 + tid; c < c1; c += U * nth) {
             v4u v[U];
             if (tt == 0 && c == c0 + tid) {
@@ -271,30 +325,156 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
         }
     }
 
-    // workgroup 0: the routed slots must add up to the layout's total
-    if (blockIdx.x == 0) {
-        const int n = a.T * k;
-        int32_t routed = 0;
-        for (int i0 = tid; i0 < n; i0 += 8 * nth) {
-            int32_t v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nth < n) ? a.topk_idx[i0 + u * nth] : -1;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) routed += (v[u] >= 0 && v[u] < E);
-        }
-        if (routed) atomicAdd(&s_routed, routed);
-        __syncthreads();
-        if (tid == 0 && s_routed != a.expert_offsets[E]) err |= MOEDISP_DEV_BAD_LAYOUT;
+    if (blockIdx.x == 0) err |= check_total(a, sm);
+    publish_err(a, sm, err);
+}
+
+// ---------------------------------------------------------------------------
+// Quantise-on-dispatch ("MSCCLPP EP implementation - #852": the PR's commit
+// messages give the low-latency dispatch E4M3 payloads with FP32 scales per
+// block of 32 elements, then UE8M0 scale bytes, and keep tiny nonzero blocks
+// nonzero at UE8M0 code zero; the review file table lists E4M3 quantization
+// helpers for that dispatch).  Each token row is quantised once, in
+// registers, and its codes are stored to all k receive rows:
+//   amax  = largest |x| of the block of B channels;
+//   FP32:  scale = amax / 448 (1 for an all-zero block), element codes are
+//          E4M3(x / scale), the quotient correctly rounded to binary32;
+//   UE8M0: scale = 2^s with s the smallest integer with 448 * 2^s >= amax,
+//          clamped to [-127, 127] (0 for an all-zero block), stored as the
+//          byte s + 127; element codes are E4M3(x * 2^-s);
+// E4M3 is OCP e4m3fn, nearest-even, saturating at +-448 (the gfx950
+// conversion instruction after a clamp to [-448, 448]).
+// Lane layout: each lane owns 16 consecutive channels (two 16-byte bf16
+// loads, one 16-byte store of codes); a block of B channels is B/16
+// consecutive lanes of one wave, reduced with lane shuffles.
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Four E4M3 codes of (v0..v3), lowest byte first.
+__device__ inline uint32_t pack4_e4m3(float v0, float v1, float v2, float v3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    return (uint32_t)w;
+}
+
+__device__ inline float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
+
+// UE8M0 exponent of a block (amax finite, >= 0).
+__device__ inline int ue8m0_exponent(float amax) {
+    if (amax == 0.0f) return 0;
+    int ex;
+    const float m = frexpf(amax, &ex);  // amax = m * 2^ex, m in [0.5, 1)
+    // 448 * 2^(ex-9) = 0.875 * 2^ex covers amax iff m <= 0.875
+    const int s = ex - 9 + (m > 0.875f ? 1 : 0);
+    return min(127, max(-127, s));
+}
+
+// FMT: MOEDISP_SCALE_FP32 or MOEDISP_SCALE_UE8M0.
+template <int FMT>
+__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_quant(DispatchArgs a) {
+    extern __shared__ int32_t dyn[];
+    __shared__ ScatterSmem sm;
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    const int k = a.k;
+    const ScatterBlock b = scatter_block(a);
+    const int units = a.out16;  // 16-channel units of a row
+    const int c0 = b.split * a.plan.split_units;  // a multiple of 64
+    const int c1 = min(units, c0 + a.plan.split_units);
+    const int glanes = a.q_block_lanes;  // lanes per scale block (power of two <= 64)
+
+    // first pass of the first token: issued before the row computation
+    v4u pre0 = {0, 0, 0, 0}, pre1 = {0, 0, 0, 0};
+    if (b.blk_nt > 0 && c0 + tid < c1) {
+        const v4u* src = a.x + (size_t)b.blk_t0 * a.row16 + 2 * (size_t)(c0 + tid);
+        pre0 = src[0];
+        pre1 = src[1];
     }
-    if (err) atomicOr(&s_err, err);
-    __syncthreads();
-    if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
+    uint32_t err = scatter_rows(a, b, dyn, sm);
+    if (b.split == 0) write_handle(a, b, sm);
+
+    for (int tt = 0; tt < b.blk_nt; ++tt) {
+        const v4u* src = a.x + (size_t)(b.blk_t0 + tt) * a.row16;
+        const int32_t* rows = sm.rows + tt * k;
+        // every lane runs the same passes: the block reduction is a wave shuffle
+        for (int c00 = c0; c00 < c1; c00 += nth) {
+            const int c = c00 + tid;
+            const bool on = c < c1;
+            v4u v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
+            if (tt == 0 && c00 == c0) {
+                v0 = pre0;
+                v1 = pre1;
+            } else if (on) {
+                v0 = src[2 * (size_t)c];
+                v1 = src[2 * (size_t)c + 1];
+            }
+            float f[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f[2 * i] = bf16_lo(v0[i]);
+                f[2 * i + 1] = bf16_hi(v0[i]);
+                f[8 + 2 * i] = bf16_lo(v1[i]);
+                f[8 + 2 * i + 1] = bf16_hi(v1[i]);
+            }
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+            for (int m = 1; m < glanes; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+
+            v4u q;
+            float scale = 1.0f;
+            int sx = 0;
+            if (FMT == MOEDISP_SCALE_FP32) {
+                scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    q[i] = pack4_e4m3(clamp448(f[4 * i] / scale), clamp448(f[4 * i + 1] / scale),
+                                      clamp448(f[4 * i + 2] / scale), clamp448(f[4 * i + 3] / scale));
+            } else {
+                sx = ue8m0_exponent(amax);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    q[i] = pack4_e4m3(clamp448(ldexpf(f[4 * i], -sx)), clamp448(ldexpf(f[4 * i + 1], -sx)),
+                                      clamp448(ldexpf(f[4 * i + 2], -sx)), clamp448(ldexpf(f[4 * i + 3], -sx)));
+            }
+            if (!on) continue;
+            const bool lead = (c & (glanes - 1)) == 0;
+            const int blk = c / glanes;
+            for (int j = 0; j < k; ++j) {
+                const int r = rows[j];
+                if (r < 0) continue;
+                __builtin_nontemporal_store(q, a.recv_x + (size_t)r * units + c);
+                if (lead) {
+                    if (FMT == MOEDISP_SCALE_FP32)
+                        reinterpret_cast<float*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] = scale;
+                    else
+                        reinterpret_cast<uint8_t*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] =
+                            (uint8_t)(sx + 127);
+                }
+            }
+        }
+    }
+
+    if (blockIdx.x == 0) err |= check_total(a, sm);
+    publish_err(a, sm, err);
 }
 
 }  // namespace
 
 hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(moedisp_count, dim3(a.plan.tiles), dim3(kThreads), (size_t)a.E * sizeof(int32_t), stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, hipStream_t stream) {
+    const DispatchPlan& p = a.plan;
+    const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
+    const dim3 grid(p.blocks), block(p.threads);
+    if (scale_fmt == MOEDISP_SCALE_UE8M0)
+        hipLaunchKernelGGL((moedisp_scatter_quant<MOEDISP_SCALE_UE8M0>), grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL((moedisp_scatter_quant<MOEDISP_SCALE_FP32>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

@@ -36,14 +36,18 @@ static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 // `tile_stride` >= tiles ints per expert, a multiple of 4).  The scatter kernel
 // runs `blocks` workgroups of `threads` lanes: each computes the rows of and
 // copies `block_tokens` consecutive tokens (inside one tile), restricted to
-// one of `col_splits` equal column ranges of the row, `units_per_lane`
-// 16-byte units per lane and pass.
+// one of `col_splits` column ranges of `split_units` lane units each (the
+// last one may be shorter), `units_per_lane` units per lane and pass.  A lane
+// unit is 16 bytes of the row for the copy and 16 channels for the
+// quantising scatter.  The tile plan depends only on the shape, so the count
+// kernel serves both scatter kernels.
 struct DispatchPlan {
     int tile_tokens;
     int tiles;
     int tile_stride;
     int block_tokens;
     int col_splits;
+    int split_units;
     int blocks;
     int threads;
     int units_per_lane;  // 1, 2 or 4
@@ -70,6 +74,7 @@ struct WsPlan {
 };
 
 DispatchPlan plan_dispatch(const moedisp_shape& s);
+DispatchPlan plan_dispatch_quant(const moedisp_shape& s);
 CombinePlan plan_combine(const moedisp_shape& s);
 WsPlan plan_workspace(const moedisp_shape& s);
 
@@ -96,8 +101,11 @@ struct LayoutArgs {
 
 struct DispatchArgs {
     int T, k, E;
-    int row16;         // 16-byte units per row
-    int scale_words;   // fp32 scales per row (0 without scales)
+    int row16;         // 16-byte units per source row
+    int out16;         // 16-byte units per received row (quantising scatter)
+    int scale_words;   // fp32 scales per row of an fp8 input (0 without scales)
+    int q_block_lanes;     // quantising scatter: lanes (16 channels each) per scale block
+    int q_scales_per_row;  // quantising scatter: scale blocks per row
     int capacity;      // T * k receive rows
     DispatchPlan plan;
     const v4u* x;
@@ -111,6 +119,7 @@ struct DispatchArgs {
     float* recv_weights;
     int32_t* expert_offsets;
     int32_t* slot_to_row;
+    void* recv_qscales;  // quantising scatter: fp32 or UE8M0 bytes [rows][q_scales_per_row]
     WsHeader* hdr;
     int32_t* tile_counts;
 };
@@ -132,6 +141,7 @@ struct CombineArgs {
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream);

@@ -17,13 +17,16 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
-KERNELS = ("moedisp_layout", "moedisp_count", "moedisp_scatter", "moedisp_combine", "moedisp_probe_copy")
+KERNELS = ("moedisp_layout", "moedisp_count", "moedisp_scatter", "moedisp_scatter_quant", "moedisp_combine",
+           "moedisp_probe_copy")
+_NAME = re.compile(r"\b(moedisp_\w+?)(<[^>(]*>)?\(")
 
 
 def source_hash() -> str:
@@ -37,10 +40,22 @@ def source_hash() -> str:
 
 
 def short_name(kernel_name: str) -> str:
-    for k in KERNELS:
-        if k in kernel_name:
-            return k
-    return ""
+    """Kernel instance as `name<template args>` (e.g. moedisp_scatter<1>), or
+    "" for kernels that are not the library's."""
+    m = _NAME.search(kernel_name)
+    if not m or m.group(1) not in KERNELS:
+        return ""
+    return m.group(1) + (m.group(2) or "").replace(" ", "")
+
+
+def base_name(instance: str) -> str:
+    return instance.split("<", 1)[0]
+
+
+def kernel_traffic(measured: dict, kernel: str):
+    """Bytes of the instance of `kernel` with the most counted dispatches."""
+    cands = [(v["dispatches"][0], v) for k, v in measured.get("kernels", {}).items() if base_name(k) == kernel]
+    return max(cands, key=lambda c: c[0])[1] if cands else None
 
 
 def read_counter(run_dir: str, counter: str) -> dict:
@@ -68,11 +83,10 @@ def summarise(fetch_dir: str, write_dir: str, probe_bytes: int, workload: str) -
     f_scale = probe_bytes / f_probe   # bytes per counter unit
     w_scale = probe_bytes / w_probe
     kernels = {}
-    for k in KERNELS:
-        if k in fetch and k in write:
-            kernels[k] = {"fetch_bytes": med(fetch[k]) * f_scale, "write_bytes": med(write[k]) * w_scale,
-                          "fetch_kib_raw": med(fetch[k]), "write_kib_raw": med(write[k]),
-                          "dispatches": [len(fetch[k]), len(write[k])]}
+    for k in sorted(set(fetch) & set(write)):
+        kernels[k] = {"fetch_bytes": med(fetch[k]) * f_scale, "write_bytes": med(write[k]) * w_scale,
+                      "fetch_kib_raw": med(fetch[k]), "write_kib_raw": med(write[k]),
+                      "dispatches": [len(fetch[k]), len(write[k])]}
     return {"source_sha256": source_hash(), "workload": workload, "probe_bytes": probe_bytes,
             "calibration": {"fetch_bytes_per_unit": f_scale, "write_bytes_per_unit": w_scale},
             "kernels": kernels}

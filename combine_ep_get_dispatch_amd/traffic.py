@@ -32,3 +32,17 @@ def algorithmic_bytes(T: int, H: int, E: int, G: int, k: int, R: int, x_elt: int
     notify = T * k * 4 + (E + 1) * 4
     return dict(layout=layout, dispatch=dispatch, notify=notify, combine=combine,
                 dispatch_combine=dispatch + combine, step=layout + dispatch + combine)
+
+
+def algorithmic_bytes_quant(T: int, H: int, E: int, k: int, R: int, block: int, scale_bytes: int) -> dict:
+    """Dispatch with quantisation: bf16 rows read once, E4M3 codes plus one
+    scale per block written per routed copy."""
+    row_out = H + (H // block) * scale_bytes
+    dispatch = (T * H * 2             # x read once
+                + R * row_out         # codes and scales per routed copy
+                + 2 * T * k * 4       # topk_idx, topk_weights
+                + 2 * R * 4           # recv_src_idx, recv_weights
+                + T * k * 4           # slot_to_row
+                + (E + 1) * 4)        # expert_offsets
+    notify = T * k * 4 + (E + 1) * 4
+    return dict(dispatch=dispatch, notify=notify, scatter=dispatch - notify)

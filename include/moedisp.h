@@ -56,6 +56,12 @@ typedef enum {
     MOEDISP_FP32 = 2       /* float32 (combine output only) */
 } moedisp_dtype;
 
+/* Scale formats of quantise-on-dispatch (ep_dispatch_quant). */
+typedef enum {
+    MOEDISP_SCALE_FP32 = 0,  /* one binary32 scale per block */
+    MOEDISP_SCALE_UE8M0 = 1  /* one byte per block: the scale is 2^(byte - 127) */
+} moedisp_scale_fmt;
+
 /* Problem shape.  T tokens of H elements, E experts in G groups (E % G == 0,
  * group of expert e = e / (E/G)), top-k slots per token. */
 typedef struct {
@@ -140,6 +146,44 @@ int ep_dispatch_scatter(const moedisp_shape* shape, const void* x, const float* 
                         const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
                         int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                         int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+
+/* Dispatch with quantisation: as ep_dispatch for a bf16 x, but every
+ * received row holds OCP E4M3 codes of the token's row plus one scale per
+ * block of `quant_block` channels ("MSCCLPP EP implementation - #852": the
+ * PR's commit messages give its low-latency dispatch E4M3 payloads with FP32
+ * scales per block of 32 elements, then UE8M0 scale bytes per block, and keep
+ * tiny nonzero blocks nonzero at UE8M0 code zero; the review file table lists
+ * the E4M3 quantization helpers of that dispatch).  Per block, with amax the
+ * largest |x| of its channels:
+ *   MOEDISP_SCALE_FP32:  scale = amax / 448 (binary32; 1 for an all-zero
+ *                        block); code = E4M3(x / scale), the quotient
+ *                        correctly rounded to binary32;
+ *   MOEDISP_SCALE_UE8M0: scale = 2^s, s the smallest integer with
+ *                        448 * 2^s >= amax, clamped to [-127, 127] (0 for an
+ *                        all-zero block), stored as the byte s + 127;
+ *                        code = E4M3(x * 2^-s);
+ * E4M3(v) is the nearest e4m3fn value, ties to even, saturating at +-448;
+ * signs (of zeros too) are kept.  x must be finite.
+ *   shape          x_dtype MOEDISP_BF16, scale_block 0.
+ *   quant_block    channels per scale: a power of two in [32, 1024] dividing H.
+ *   scale_fmt      MOEDISP_SCALE_FP32 or MOEDISP_SCALE_UE8M0.
+ *   recv_x         uint8 [T*k][H] E4M3 codes (16-byte aligned).
+ *   recv_scales    [T*k][H/quant_block]: float (4-byte aligned) or uint8.
+ * The other arguments, the handle and the status bits are those of
+ * ep_dispatch; the received rows are in the same order.  Unsupported
+ * quant_block or scale_fmt: MOEDISP_ERR_UNSUPPORTED; a block that does not
+ * divide H: MOEDISP_ERR_INVALID_ARG.
+ * ep_dispatch_scatter_quant is its second phase, after ep_dispatch_notify of
+ * the same shape, topk_idx and tokens_per_expert in the same `ws`. */
+int ep_dispatch_quant(const moedisp_shape* shape, int32_t quant_block, int32_t scale_fmt, const void* x,
+                      const int32_t* topk_idx, const float* topk_weights, const int32_t* tokens_per_expert,
+                      void* recv_x, void* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                      int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+int ep_dispatch_scatter_quant(const moedisp_shape* shape, int32_t quant_block, int32_t scale_fmt,
+                              const void* x, const int32_t* topk_idx, const float* topk_weights,
+                              const int32_t* tokens_per_expert, void* recv_x, void* recv_scales,
+                              int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
+                              int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: the reverse of dispatch through its handle.
  *   out[t][h] = sum over j = 0..k-1 in ascending order, skipping masked slots,

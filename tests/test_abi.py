@@ -122,6 +122,32 @@ def test_host_checks_dispatch_phases(lib):
                                    1 << 30, None) == B.ERR_MISALIGNED
 
 
+def quant_rc(lib, s, block=128, fmt=M.SCALE_FP32, x=None, recv_x=None, rs=None, idx=None, ws_bytes=1 << 30):
+    return lib.ep_dispatch_quant(C.byref(s), block, fmt, x or p(), idx or p(), p(), p(), recv_x or p(),
+                                 rs or p(), p(), p(), p(), p(), p(), ws_bytes, None)
+
+
+def test_host_checks_dispatch_quant(lib):
+    s = shape()
+    assert quant_rc(lib, shape(dt=M.FP8_E4M3, sb=128)) == B.ERR_UNSUPPORTED   # input must be bf16
+    assert quant_rc(lib, s, fmt=2) == B.ERR_UNSUPPORTED
+    assert quant_rc(lib, s, block=48) == B.ERR_UNSUPPORTED                    # not a power of two
+    assert quant_rc(lib, s, block=16) == B.ERR_UNSUPPORTED                    # below 32
+    assert quant_rc(lib, s, block=2048) == B.ERR_UNSUPPORTED                  # above 1024
+    assert quant_rc(lib, shape(H=96), block=64) == B.ERR_INVALID_ARG          # block does not divide H
+    assert quant_rc(lib, s, x=p(8)) == B.ERR_MISALIGNED
+    assert quant_rc(lib, s, recv_x=p(8)) == B.ERR_MISALIGNED
+    assert quant_rc(lib, s, rs=p(2)) == B.ERR_MISALIGNED                      # fp32 scales need 4 bytes
+    assert quant_rc(lib, s, ws_bytes=64) == B.ERR_WORKSPACE_TOO_SMALL
+    assert quant_rc(lib, shape(E=255)) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_quant(C.byref(s), 128, M.SCALE_FP32, p(), p(), p(), p(), p(), None, p(), p(), p(), p(),
+                                 p(), 1 << 30, None) == B.ERR_INVALID_ARG     # null scales
+    assert lib.ep_dispatch_scatter_quant(C.byref(s), 128, M.SCALE_FP32, None, p(), p(), p(), p(), p(), p(), p(),
+                                         p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_scatter_quant(C.byref(s), 96, M.SCALE_UE8M0, p(), p(), p(), p(), p(), p(), p(), p(),
+                                         p(), p(), p(), 1 << 30, None) == B.ERR_UNSUPPORTED
+
+
 def test_host_checks_combine(lib):
     assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
     assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED
