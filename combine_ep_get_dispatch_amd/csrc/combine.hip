@@ -14,8 +14,8 @@
 // How.  One workgroup per (token, column range).  The token's k rows and
 // weights are uniform across the workgroup, so they come through scalar loads;
 // the handle is checked there (row inside the receive buffer and, when
-// recv_src_idx is given, naming this token) and bad slots are skipped with
-// BAD_HANDLE raised.  Each lane owns U 16-byte units (8 bf16) of the output
+// recv_src_idx is given, naming this token) and a slot that fails is skipped
+// at accumulation, with BAD_HANDLE raised.  Each lane owns U 16-byte units (8 bf16) of the output
 // row (U = 1 for k = 8: 896 lanes cover a 7168-wide row in one pass): it
 // issues all k*U gathered 16-byte loads before the first FMA, so each lane
 // keeps k*U loads in flight, then accumulates slot by slot in order.
@@ -96,28 +96,60 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
     uint32_t err = 0;
 
     if constexpr (KC > 0) {
+        // Loads carry no per-slot branch, so the compiler issues all k*U of
+        // them back to back: a slot that is masked or fails the handle check
+        // loads an in-bounds fallback row (the token's first good row, else
+        // row 0; capacity >= 1 whenever a kernel runs) and is skipped at the
+        // FMA; idle lanes of the last wave load a clamped column and store
+        // nothing.
         int rows[KC];
+        bool use[KC];
         float wts[KC];
 #pragma unroll
-        for (int j = 0; j < KC; ++j) rows[j] = handle_row(a, t, j, &wts[j], &err);
-        for (int c = c0 + tid; c < c1; c += U * nth) {
+        for (int j = 0; j < KC; ++j) {
+            const int r = a.slot_to_row[(size_t)t * KC + j];
+            if (r < -1 || r >= a.capacity) err |= MOEDISP_DEV_BAD_HANDLE;
+            use[j] = r >= 0 && r < a.capacity;
+            rows[j] = r;
+        }
+        int fallback = 0;
+#pragma unroll
+        for (int j = KC - 1; j >= 0; --j)
+            if (use[j]) fallback = rows[j];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) rows[j] = use[j] ? rows[j] : fallback;
+        // first pass of row loads, issued before the weights are fetched
+        v4u v[KC][U];
+        int c = c0 + tid;
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 +
+                                                     min(c + u * nth, c1 - 1));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < KC; ++j) wts[j] = a.recv_weights[rows[j]];
+        if (a.recv_src_idx) {
+            int src[KC];
+#pragma unroll
+            for (int j = 0; j < KC; ++j) src[j] = a.recv_src_idx[rows[j]];
+#pragma unroll
+            for (int j = 0; j < KC; ++j) {
+                const bool bad = use[j] && src[j] != t;
+                err |= bad ? MOEDISP_DEV_BAD_HANDLE : 0u;
+                use[j] = use[j] && !bad;
+            }
+        }
+        while (c < c1) {
             float acc[U][8];
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-            v4u v[KC][U];
-#pragma unroll
-            for (int j = 0; j < KC; ++j)
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * nth;
-                    if (rows[j] >= 0 && cc < c1)
-                        v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 + cc);
-                }
 #pragma unroll
             for (int j = 0; j < KC; ++j) {
-                if (rows[j] < 0) continue;
+                if (!use[j]) continue;
 #pragma unroll
                 for (int u = 0; u < U; ++u) fma8(acc[u], wts[j], v[j][u]);
             }
@@ -126,6 +158,14 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
                 const int cc = c + u * nth;
                 if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
             }
+            c += U * nth;
+            if (c >= c1) break;
+#pragma unroll
+            for (int j = 0; j < KC; ++j)
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 +
+                                                         min(c + u * nth, c1 - 1));
         }
     } else {
         if (tid == 0)

@@ -122,7 +122,8 @@ struct ScatterSmem {
     int32_t pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
     int32_t base[kMaxBlockSlots];  // expert_offsets[e]
     int32_t len[kMaxBlockSlots];   // tokens_per_expert[e]
-    int32_t rows[kMaxBlockSlots];  // receive row of each slot of the workgroup, -1 if none
+    int32_t rows[kMaxBlockSlots + 8];  // receive row of each slot of the workgroup, -1 if none
+                                       // (8 spare entries: the stores read rows 8 at a time)
     int32_t routed;
     uint32_t err;
 };
@@ -312,14 +313,21 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
                     if (cc < c1) v[u] = src[cc];
                 }
             }
-            for (int j = 0; j < k; ++j) {
-                const int r = rows[j];
-                if (r < 0) continue;
-                v4u* dst = a.recv_x + (size_t)r * a.row16;
+            // destination rows 8 at a time from LDS, then the stores
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                int rr[8];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * nth;
-                    if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
+                for (int q = 0; q < 8; ++q) rr[q] = rows[j0 + q];
+                asm volatile("" ::: "memory");  // all 8 reads before the stores
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (j0 + q >= k || rr[q] < 0) continue;
+                    v4u* dst = a.recv_x + (size_t)rr[q] * a.row16;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int cc = c + u * nth;
+                        if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
+                    }
                 }
             }
         }
@@ -441,16 +449,23 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_quant(Dis
             if (!on) continue;
             const bool lead = (c & (glanes - 1)) == 0;
             const int blk = c / glanes;
-            for (int j = 0; j < k; ++j) {
-                const int r = rows[j];
-                if (r < 0) continue;
-                __builtin_nontemporal_store(q, a.recv_x + (size_t)r * units + c);
-                if (lead) {
-                    if (FMT == MOEDISP_SCALE_FP32)
-                        reinterpret_cast<float*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] = scale;
-                    else
-                        reinterpret_cast<uint8_t*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] =
-                            (uint8_t)(sx + 127);
+            for (int j0 = 0; j0 < k; j0 += 8) {
+                int rr[8];
+#pragma unroll
+                for (int w = 0; w < 8; ++w) rr[w] = rows[j0 + w];
+                asm volatile("" ::: "memory");  // all 8 reads before the stores
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const int r = rr[w];
+                    if (j0 + w >= k || r < 0) continue;
+                    __builtin_nontemporal_store(q, a.recv_x + (size_t)r * units + c);
+                    if (lead) {
+                        if (FMT == MOEDISP_SCALE_FP32)
+                            reinterpret_cast<float*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] = scale;
+                        else
+                            reinterpret_cast<uint8_t*>(a.recv_qscales)[(size_t)r * a.q_scales_per_row + blk] =
+                                (uint8_t)(sx + 127);
+                    }
                 }
             }
         }
