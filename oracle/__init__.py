@@ -79,6 +79,11 @@ class Oracle:
         L.oracle_dispatch_quant.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
                                             P, P, P, P, P, P, P, P, P]
         L.oracle_dispatch_quant.restype = C.c_int
+        L.oracle_dispatch_groups.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
+                                             P, P, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_dispatch_groups.restype = C.c_int
+        L.oracle_combine_groups.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, P, P, P, P]
+        L.oracle_combine_groups.restype = C.c_int
         self.L = L
         self.path = path
 
@@ -194,6 +199,53 @@ class Oracle:
             raise ValueError("oracle_dispatch_quant: bad arguments")
         return dict(recv_x=rq, recv_scales=rs, recv_src_idx=src, recv_weights=rw,
                     expert_offsets=off, slot_to_row=s2r, status=st)
+
+
+    # -- group-deduplicated dispatch --------------------------------------------
+
+    def dispatch_groups(self, x, x_scales, topk_idx, topk_weights, is_token_in_group, E: int, G: int):
+        """Returns a dict: recv_x [T*min(G,k)][...], recv_scales, recv_src_idx,
+        recv_topk_idx [rows][k], recv_topk_weights [rows][k], group_offsets
+        [G+1], token_group_row [T][G], status.  Rows at or past
+        group_offsets[G] stay zero (unused capacity)."""
+        idx = _c(topk_idx, np.int32)
+        T, k = idx.shape
+        x = np.ascontiguousarray(x)
+        row_bytes = int(np.prod(x.shape[1:])) * x.itemsize
+        cap = T * min(G, k)
+        recv_x = np.zeros((cap,) + x.shape[1:], x.dtype)
+        if x_scales is not None:
+            xs = np.ascontiguousarray(x_scales)
+            srb = int(np.prod(xs.shape[1:])) * xs.itemsize
+            recv_scales = np.zeros((cap,) + xs.shape[1:], xs.dtype)
+        else:
+            xs, srb, recv_scales = None, 0, None
+        src = np.full(cap, -1, np.int32)
+        rti = np.full((cap, k), -1, np.int32)
+        rtw = np.zeros((cap, k), np.float32)
+        goff = np.zeros(G + 1, np.int32)
+        tgr = np.zeros((T, G), np.int32)
+        w = _c(topk_weights, np.float32)
+        bm = _c(is_token_in_group, np.uint32)
+        st = self.L.oracle_dispatch_groups(T, k, E, G, row_bytes, srb, _p(x), _p(xs), _p(idx), _p(w), _p(bm),
+                                           _p(recv_x), _p(recv_scales), _p(src), _p(rti), _p(rtw), _p(goff),
+                                           _p(tgr))
+        if st < 0:
+            raise ValueError("oracle_dispatch_groups: bad shape")
+        return dict(recv_x=recv_x, recv_scales=recv_scales, recv_src_idx=src, recv_topk_idx=rti,
+                    recv_topk_weights=rtw, group_offsets=goff, token_group_row=tgr, status=st)
+
+    def combine_groups(self, group_rows_bf16, token_group_row, want_f32=True, want_bf16=True):
+        """group_rows_bf16: uint16 [R_g][H].  Returns (out_f32, out_bf16) [T][H]."""
+        gr = _c(group_rows_bf16, np.uint16)
+        Rg, H = gr.shape
+        tgr = _c(token_group_row, np.int32)
+        T, G = tgr.shape
+        of = np.zeros((T, H), np.float32) if want_f32 else None
+        ob = np.zeros((T, H), np.uint16) if want_bf16 else None
+        if self.L.oracle_combine_groups(T, G, H, Rg, _p(gr), _p(tgr), _p(of), _p(ob)) < 0:
+            raise ValueError("oracle_combine_groups: bad arguments")
+        return of, ob
 
 
 _default = None

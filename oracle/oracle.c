@@ -405,3 +405,97 @@ int oracle_dispatch_quant(int T, int k, int E, int H, int B, int fmt,
     free(sc);
     return st;
 }
+
+/* ------------------------------------------------------------------------ */
+/* group-deduplicated dispatch and its combine                               */
+/*                                                                           */
+/* Same page: in the high-throughput path the layout's token-in-rank flags   */
+/* decide which ranks receive a token, each such rank receives it once, and  */
+/* the receiver's layout holds one row per (token, source rank) pair (the    */
+/* bench commits that change the byte accounting describe that expanded      */
+/* receive layout); the receiver then orders rows by its local experts.      */
+/* Here a rank is a destination group.  Readings:                            */
+/*   - group g's rows are [group_offsets[g], group_offsets[g+1]), one per    */
+/*     token whose bit g is set in is_token_in_group, in token order;        */
+/*   - each row carries the token index and the token's k slots restricted   */
+/*     to the group: the global expert id where the slot's expert lies in    */
+/*     g, else -1, and the slot's weight there, else 0;                      */
+/*   - token_group_row[t][g] is the row of (t, g), -1 if t does not reach g; */
+/*   - the way back: each group row gets the bf16 (nearest-even) rounding of */
+/*     its weighted expert sum (fp32 fused multiply-add, ascending slot),    */
+/*     and out[t] is the bf16 rounding of the fp32 sum of the token's group  */
+/*     rows in ascending g.                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Group-deduplicated dispatch.  is_token_in_group is the layout's bitmap for
+ * the same topk_idx (only bits < G are read).  Outputs have capacity
+ * T*min(G,k) rows; rows at or past group_offsets[G] are left untouched. */
+int oracle_dispatch_groups(int T, int k, int E, int G, int64_t row_bytes, int64_t scale_row_bytes,
+                           const uint8_t* x, const uint8_t* x_scales,
+                           const int32_t* topk_idx, const float* topk_weights,
+                           const uint32_t* is_token_in_group,
+                           uint8_t* recv_x, uint8_t* recv_scales, int32_t* recv_src_idx,
+                           int32_t* recv_topk_idx, float* recv_topk_weights,
+                           int32_t* group_offsets, int32_t* token_group_row)
+{
+    if (bad_shape(T, k, E, G) || row_bytes < 0 || scale_row_bytes < 0) return -1;
+    int experts_per_group = E / G;
+
+    /* rows per group and their exclusive prefix */
+    int64_t run = 0;
+    for (int g = 0; g < G; ++g) {
+        group_offsets[g] = (int32_t)run;
+        for (int t = 0; t < T; ++t) run += (is_token_in_group[t] >> g) & 1u;
+    }
+    group_offsets[G] = (int32_t)run;
+
+    /* group by group, tokens in order */
+    for (int g = 0; g < G; ++g) {
+        int64_t r = group_offsets[g];
+        for (int t = 0; t < T; ++t) {
+            if (!((is_token_in_group[t] >> g) & 1u)) {
+                token_group_row[(int64_t)t * G + g] = -1;
+                continue;
+            }
+            const uint8_t* row = x + (int64_t)t * row_bytes;
+            memcpy(recv_x + r * row_bytes, row, (size_t)row_bytes);
+            if (x_scales && recv_scales && scale_row_bytes > 0)
+                memcpy(recv_scales + r * scale_row_bytes, x_scales + (int64_t)t * scale_row_bytes,
+                       (size_t)scale_row_bytes);
+            recv_src_idx[r] = (int32_t)t;
+            for (int j = 0; j < k; ++j) {
+                int32_t id = topk_idx[(int64_t)t * k + j];
+                int here = routed(id, E) && id / experts_per_group == g;
+                recv_topk_idx[r * k + j] = here ? id : -1;
+                recv_topk_weights[r * k + j] = here ? topk_weights[(int64_t)t * k + j] : 0.0f;
+            }
+            token_group_row[(int64_t)t * G + g] = (int32_t)r;
+            ++r;
+        }
+    }
+    return routing_status(T, k, E, topk_idx);
+}
+
+/* Sum of each token's group rows: out[t] = sum over g ascending with
+ * token_group_row[t][g] >= 0 of group_rows[that row], accumulated in fp32
+ * from 0.0f; out_bf16 is its nearest-even bf16 rounding.  group_rows: bf16
+ * [R_g][H].  Either output may be NULL. */
+int oracle_combine_groups(int T, int G, int H, int64_t Rg, const uint16_t* group_rows,
+                          const int32_t* token_group_row, float* out_f32, uint16_t* out_bf16)
+{
+    if (T < 0 || G < 1 || H < 0 || Rg < 0) return -1;
+    for (int t = 0; t < T; ++t) {
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int g = 0; g < G; ++g) {
+                int32_t r = token_group_row[(int64_t)t * G + g];
+                if (r < 0) continue;
+                if ((int64_t)r >= Rg) return -1;
+                acc = acc + (float)oracle_bf16_to_double(group_rows[(int64_t)r * H + h]);
+            }
+            if (out_f32) out_f32[(int64_t)t * H + h] = acc;
+            if (out_bf16) out_bf16[(int64_t)t * H + h] = oracle_f32_to_bf16(acc);
+        }
+    }
+    return 0;
+}

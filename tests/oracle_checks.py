@@ -516,6 +516,146 @@ def check_quant_all(orc):
     check_dispatch_quant(orc, wl, 32, SCALE_UE8M0)
 
 
+# ---------------------------------------------------------------------------
+# group-deduplicated dispatch and its combine
+# ---------------------------------------------------------------------------
+
+def group_dispatch_reference(idx, bm, E, G):
+    """Second formulation: the (group, token) pairs with their bit set,
+    sorted; and each pair's restricted slots from the expert -> group map."""
+    T, k = idx.shape
+    pairs = sorted((g, t) for t in range(T) for g in range(G) if (int(bm[t]) >> g) & 1)
+    per = E // G
+    rti = np.full((len(pairs), k), -1, np.int64)
+    for r, (g, t) in enumerate(pairs):
+        for j in range(k):
+            e = int(idx[t, j])
+            if 0 <= e < E and e // per == g:
+                rti[r, j] = e
+    return pairs, rti
+
+
+def check_groups_bruteforce(orc, shapes=((2, 1, 2, 2), (3, 1, 4, 2), (2, 2, 4, 2), (2, 2, 4, 4), (1, 3, 6, 3))):
+    for T, k, E, G in shapes:
+        opts = token_options(E, k)
+        H = 4
+        for combo in itertools.product(range(len(opts)), repeat=T):
+            idx = np.array([opts[c] for c in combo], np.int32).reshape(T, k)
+            w = (np.arange(T * k, dtype=np.float32).reshape(T, k) + 1) / 64
+            x = torch_bf16_bits(np.repeat((np.arange(T, dtype=np.float32) + 1)[:, None], H, axis=1))
+            _, tpg, bm, _ = orc.layout(idx, E, G)
+            d = orc.dispatch_groups(x, None, idx, w, bm, E, G)
+            pairs, rti = group_dispatch_reference(idx, bm, E, G)
+            Rg = len(pairs)
+            assert d["group_offsets"][-1] == Rg
+            assert np.array_equal(np.diff(d["group_offsets"]), tpg)
+            assert d["recv_src_idx"][:Rg].tolist() == [t for _, t in pairs]
+            assert np.array_equal(d["recv_topk_idx"][:Rg], rti)
+            srcs = [t for _, t in pairs]
+            exp_w = np.where(rti >= 0, w[srcs], 0.0) if Rg else np.zeros((0, k))
+            assert np.array_equal(d["recv_topk_weights"][:Rg], exp_w)
+            assert np.array_equal(d["recv_x"][:Rg], x[srcs])
+            tgr = np.full((T, G), -1)
+            for r, (g, t) in enumerate(pairs):
+                tgr[t, g] = r
+            assert np.array_equal(d["token_group_row"], tgr)
+
+
+def ht_path(orc, wl):
+    """layout -> group dispatch -> local permutation (dispatch of the group
+    rows) -> stand-in experts -> local reduce (combine of the group rows) ->
+    combine of the groups.  Returns every intermediate."""
+    tpe, tpg, bm, _ = orc.layout(wl.topk_idx, wl.E, wl.G)
+    gd = orc.dispatch_groups(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, bm, wl.E, wl.G)
+    Rg = int(gd["group_offsets"][-1])
+    gs = None if gd["recv_scales"] is None else gd["recv_scales"][:Rg]
+    pm = orc.dispatch(gd["recv_x"][:Rg], gs, gd["recv_topk_idx"][:Rg], gd["recv_topk_weights"][:Rg], wl.E)
+    R = int(pm["expert_offsets"][-1])
+    re = W.row_experts(pm["expert_offsets"])
+    eo = W.expert_outputs(wl, pm["recv_x"][:R], None if pm["recv_scales"] is None else pm["recv_scales"][:R], re)
+    eo_bits = eo.view(torch.int16).numpy().view(np.uint16)
+    _, part = orc.combine(eo_bits, pm["recv_weights"][:R], pm["slot_to_row"], want_f32=False)
+    of, ob = orc.combine_groups(part, gd["token_group_row"])
+    return dict(tpe=tpe, tpg=tpg, bm=bm, gd=gd, Rg=Rg, pm=pm, R=R, eo_bits=eo_bits, part=part, out_f32=of, out_bf16=ob)
+
+
+def check_groups_invariants(orc, wl):
+    h = ht_path(orc, wl)
+    gd, pm, Rg = h["gd"], h["pm"], h["Rg"]
+    off = gd["group_offsets"].astype(np.int64)
+    assert np.array_equal(np.diff(off), h["tpg"]), "group segments are the layout's group counts"
+    src = gd["recv_src_idx"][:Rg]
+    for g in range(wl.G):
+        assert np.all(np.diff(src[off[g]:off[g + 1]]) > 0), "token order inside a group"
+    assert np.array_equal(gd["recv_x"][:Rg], wl.x[src]), "group rows are their token's row"
+    tgr = gd["token_group_row"]
+    assert np.array_equal(np.sort(tgr[tgr >= 0]), np.arange(Rg)), "token_group_row is a bijection onto [0,R_g)"
+    assert np.array_equal(tgr >= 0, ((h["bm"][:, None] >> np.arange(wl.G)) & 1).astype(bool))
+    rti = gd["recv_topk_idx"][:Rg]
+    assert int((rti >= 0).sum()) == wl.num_routed, "every routed slot lands in exactly one group row"
+    # the local permutation of the group rows is the flat dispatch
+    flat = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+    R = h["R"]
+    assert np.array_equal(pm["expert_offsets"], flat["expert_offsets"])
+    assert np.array_equal(pm["recv_x"][:R], flat["recv_x"][:R]), "permuted rows equal the flat dispatch's"
+    assert np.array_equal(src[pm["recv_src_idx"][:R]], flat["recv_src_idx"][:R])
+    assert np.array_equal(pm["recv_weights"][:R].view(np.uint32), flat["recv_weights"][:R].view(np.uint32))
+    per = wl.E // wl.G
+    idx = wl.topk_idx
+    t_of, j_of = np.nonzero(idx >= 0)
+    grow = tgr[t_of, idx[t_of, j_of] // per]
+    assert np.array_equal(pm["slot_to_row"][grow, j_of], flat["slot_to_row"][t_of, j_of])
+    return h
+
+
+def check_groups_combine_exact(orc, T=97, H=32, E=16, G=4, seed=51):
+    """k = 2 with weights 1/2, 1/2 and identity experts: every group partial
+    (x/2 or x) and the sum over groups are exact, so the result is x."""
+    wl = W.make_workload("ht_exact", T, H, E, G, 2, seed=seed, expert_kind="identity")
+    wl.topk_weights = np.full((T, 2), 0.5, np.float32)
+    h = ht_path(orc, wl)
+    assert np.array_equal(h["out_bf16"], wl.x)
+
+
+def check_groups_combine_closed_form(orc, wl, rel_bound):
+    """out = x * sum_j w_j c(e_j) in fp64, within the bound of two bf16
+    roundings (expert output, group partial) plus fp32 sums."""
+    h = ht_path(orc, wl)
+    c = W.expert_factors(wl.expert_kind, wl.E).astype(np.float64)
+    idx = wl.topk_idx
+    w = np.where(idx >= 0, wl.topk_weights.astype(np.float64), 0.0)
+    exact = bf16_to_f64(wl.x) * (w * c[np.maximum(idx, 0)]).sum(axis=1)[:, None]
+    of = h["out_f32"].astype(np.float64)
+    nz = exact != 0
+    rel = np.abs(of[nz] - exact[nz]) / np.abs(exact[nz])
+    assert rel.size == 0 or rel.max() <= rel_bound, f"group combine off by {rel.max():.3e} > {rel_bound:.3e}"
+    assert np.all(of[~nz] == 0.0)
+    assert np.array_equal(h["out_bf16"], torch_bf16_bits(h["out_f32"]))
+
+
+# one rounding of each group partial on top of the flat path's bounds
+GROUP_BOUND = {"identity": 2.0 ** -8 + 2.0 ** -15, "double_odd": 2.0 ** -8 + 2.0 ** -15,
+               "scale_by_id": 2.0 ** -7 + 2.0 ** -15}
+
+
+def group_configs():
+    return [
+        W.make_workload("ht_uniform", 300, 64, 64, 8, 8, seed=52, expert_kind="scale_by_id"),
+        W.make_workload("ht_zipf", 300, 64, 256, 8, 8, seed=53, routing="zipf", mask_frac=0.05,
+                        expert_kind="scale_by_id"),
+        W.make_workload("ht_mixtral", 500, 64, 8, 8, 2, seed=54, expert_kind="double_odd"),
+        W.make_workload("ht_g_lt_k", 200, 64, 16, 2, 6, seed=55, expert_kind="identity"),
+    ]
+
+
+def check_groups_all(orc):
+    check_groups_bruteforce(orc)
+    check_groups_combine_exact(orc)
+    for wl in group_configs():
+        check_groups_invariants(orc, wl)
+        check_groups_combine_closed_form(orc, wl, GROUP_BOUND[wl.expert_kind])
+
+
 ALL_BASIC = [check_bf16_rounding, check_bruteforce, check_combine_exact_dyadic, check_combine_k1_inverse,
              check_worked_example, check_error_status]
 
@@ -538,6 +678,7 @@ def run_all(orc):
     for chk in ALL_BASIC:
         chk(orc)
     check_quant_all(orc)
+    check_groups_all(orc)
     for wl in small_configs():
         check_layout_invariants(orc, wl)
         check_dispatch_invariants(orc, wl)

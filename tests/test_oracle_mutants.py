@@ -88,6 +88,19 @@ MUTANTS = {
     # quantiser: block offset forgotten (every block reads the first)
     "quant_block_offset": ("const uint16_t* xb = x + (int64_t)t * H + (int64_t)b * B;",
                            "const uint16_t* xb = x + (int64_t)t * H;"),
+    # group dispatch: group membership taken from the neighbouring bit
+    "group_bit": ("run += (is_token_in_group[t] >> g) & 1u;", "run += (is_token_in_group[t] >> (g + 1)) & 1u;"),
+    # group dispatch: restricted slots keep every expert
+    "group_no_restrict": ("int here = routed(id, E) && id / experts_per_group == g;", "int here = routed(id, E);"),
+    # group dispatch: weights of other groups' slots kept
+    "group_weights_kept": ("recv_topk_weights[r * k + j] = here ? topk_weights[(int64_t)t * k + j] : 0.0f;",
+                           "recv_topk_weights[r * k + j] = topk_weights[(int64_t)t * k + j];"),
+    # group dispatch: row of (t, g) recorded one too high
+    "group_row_off_by_one": ("token_group_row[(int64_t)t * G + g] = (int32_t)r;",
+                             "token_group_row[(int64_t)t * G + g] = (int32_t)(r + 1);"),
+    # group combine: the last group dropped
+    "group_combine_drop": ("            for (int g = 0; g < G; ++g) {\n                int32_t r = token_group_row",
+                           "            for (int g = 0; g + 1 < G; ++g) {\n                int32_t r = token_group_row"),
     # quantised dispatch: the scales are not moved with the rows
     "quant_scales_dropped": ("st = oracle_dispatch(T, k, E, H, scale_bytes, q, sc, topk_idx",
                              "st = oracle_dispatch(T, k, E, H, scale_bytes, q, NULL, topk_idx"),

@@ -100,3 +100,18 @@ def test_quant_worked_example(orc):
 def test_dispatch_quant_is_quantise_then_dispatch(orc, B, fmt):
     wl = W.make_workload("quant_mid", 300, 256, 64, 8, 6, seed=26, routing="zipf", mask_frac=0.05)
     K.check_dispatch_quant(orc, wl, B, fmt)
+
+
+def test_group_dispatch_bruteforce_every_tiny_routing(orc):
+    K.check_groups_bruteforce(orc)
+
+
+def test_group_combine_exact_with_half_weights(orc):
+    K.check_groups_combine_exact(orc)
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_group_path_invariants_and_closed_form(orc, i):
+    wl = K.group_configs()[i]
+    K.check_groups_invariants(orc, wl)
+    K.check_groups_combine_closed_form(orc, wl, K.GROUP_BOUND[wl.expert_kind])
