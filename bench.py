@@ -189,6 +189,60 @@ def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
     return res
 
 
+def run_gpu_groups(cid, steps, warmup, dev):
+    """Time the group-deduplicated path on config `cid`: layout, group
+    dispatch, local expert permutation, local reduce, group combine."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    from combine_ep_get_dispatch_amd import workloads as W
+    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS, algorithmic_bytes_groups
+
+    wl = W.config(cid)
+    bufs = M.EpBuffers(shape_of(M, W, wl), dev)
+    gb = M.EpGroupBuffers(bufs)
+    x, xs, idx, w = make_inputs(wl, dev)
+    bufs.layout(idx)
+    gb.dispatch_groups(x, xs, idx, w)
+    gb.permute()
+    if bufs.status():
+        raise RuntimeError(f"device status on the group path, config {cid}")
+    R = int(bufs.expert_offsets[-1].item())
+    Rg = int(gb.group_offsets[-1].item())
+    eo = torch.zeros((wl.T * wl.k, wl.H), dtype=torch.bfloat16, device=dev)
+    eo[:R] = bufs.recv_x[:R].view(torch.bfloat16) if wl.x_dtype == W.X_BF16 else 0
+    part = torch.empty((gb.capacity, wl.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = [lambda: bufs.layout(idx, stream), lambda: gb.dispatch_groups(x, xs, idx, w, stream),
+             lambda: gb.permute(stream), lambda: gb.reduce(eo, part, M.BF16, True, stream),
+             lambda: gb.combine_groups(part, out, M.BF16, True, stream)]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        for j, c in enumerate(calls):
+            evs[i][j].record(stream)
+            c()
+        evs[i][-1].record(stream)
+    torch.cuda.synchronize()
+    if bufs.status():
+        raise RuntimeError(f"device status after the group path steps, config {cid}")
+    us = np.array([[e[j].elapsed_time(e[j + 1]) * 1e3 for j in range(len(calls))] for e in evs]).mean(axis=0)
+    x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
+    B = algorithmic_bytes_groups(wl.T, wl.H, wl.E, wl.G, wl.k, R, Rg, x_elt, wl.scale_block)
+    names = ["layout", "dispatch_groups", "permute", "reduce", "combine_groups"]
+    res = dict(workload=wl.name, R=R, R_g=Rg, us={n: float(u) for n, u in zip(names, us)})
+    res["gbps"] = {n: B[n] / (res["us"][n] * 1e-6) / 1e9 for n in names[1:]}
+    res["frac"] = {n: g / HBM_PEAK_GBPS for n, g in res["gbps"].items()}
+    res["dispatch_combine_us"] = float(us[1:].sum())
+    res["tokens_per_s"] = wl.T / (us[1:].sum() * 1e-6)
+    del bufs, gb, x, xs, idx, w, eo, part, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
     """Achievable HBM copy bandwidth (read + write bytes) with the library's
     plain 16-byte copy kernel."""
@@ -258,6 +312,7 @@ def main():
     ap.add_argument("--no-other-workloads", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the quantise-on-dispatch timings")
+    ap.add_argument("--no-groups", action="store_true", help="skip the group-deduplicated path timings")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -294,6 +349,10 @@ def main():
             log(f"[bench] quantised dispatch {tag}")
             quant[tag] = run_gpu_quant(args.config, block, fmt, max(20, args.steps // 4),
                                        max(5, args.warmup // 4), dev)
+    groups = None
+    if not args.no_groups:
+        log("[bench] group-deduplicated path")
+        groups = run_gpu_groups(args.config, max(20, args.steps // 4), max(5, args.warmup // 4), dev)
     probe = None if args.no_probe else probe_copy_gbps(dev)
     if probe:
         log(f"[bench] probe copy {probe:.0f} GB/s")
@@ -351,6 +410,7 @@ def main():
         "probe_copy_gbps": probe,
         "other_workloads": others,
         "quant_dispatch": quant,
+        "group_path": groups,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -42,6 +42,7 @@ DEV_BAD_HANDLE = 8
 
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch",
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
+           "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy")
 
 
@@ -94,6 +95,14 @@ def load(path: str = LIB_PATH):
     L.ep_dispatch_scatter_quant.argtypes = [S, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                             C.c_size_t, P]
     L.ep_dispatch_scatter_quant.restype = C.c_int
+    L.ep_dispatch_groups.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_dispatch_groups.restype = C.c_int
+    L.ep_group_permute.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_group_permute.restype = C.c_int
+    L.ep_group_reduce.argtypes = [S, P, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
+    L.ep_group_reduce.restype = C.c_int
+    L.ep_combine_groups.argtypes = [S, P, P, P, P, C.c_int32, P, C.c_size_t, P]
+    L.ep_combine_groups.restype = C.c_int
     L.ep_combine.argtypes = [S, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
     L.ep_combine.restype = C.c_int
     L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
@@ -177,6 +186,37 @@ def ep_dispatch_scatter_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_w
         C.byref(shape), int(quant_block), int(scale_fmt), _p(x), _p(topk_idx), _p(topk_weights),
         _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
         _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_dispatch_groups(shape, x, x_scales, topk_idx, topk_weights, is_token_in_group, tokens_per_group, recv_x,
+                       recv_scales, recv_src_idx, recv_topk_idx, recv_topk_weights, group_offsets, token_group_row, ws,
+                       stream=None):
+    _check("ep_dispatch_groups", load().ep_dispatch_groups(
+        C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(is_token_in_group),
+        _p(tokens_per_group), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_topk_idx),
+        _p(recv_topk_weights), _p(group_offsets), _p(token_group_row), _p(ws), ws.numel() * ws.element_size(),
+        _s(stream)))
+
+
+def ep_group_permute(shape, group_x, group_scales, recv_topk_idx, recv_topk_weights, tokens_per_expert, recv_x,
+                     recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
+    _check("ep_group_permute", load().ep_group_permute(
+        C.byref(shape), _p(group_x), _p(group_scales), _p(recv_topk_idx), _p(recv_topk_weights),
+        _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
+        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_group_reduce(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, group_offsets, group_out, out_dtype,
+                    ws, stream=None):
+    _check("ep_group_reduce", load().ep_group_reduce(
+        C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(group_offsets),
+        _p(group_out), int(out_dtype), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_combine_groups(shape, group_rows, recv_src_idx, token_group_row, out, out_dtype, ws, stream=None):
+    _check("ep_combine_groups", load().ep_combine_groups(
+        C.byref(shape), _p(group_rows), _p(recv_src_idx), _p(token_group_row), _p(out), int(out_dtype), _p(ws),
+        ws.numel() * ws.element_size(), _s(stream)))
 
 
 def ep_combine(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, out, out_dtype, ws, stream=None):
@@ -266,3 +306,51 @@ class EpBuffers:
 
     def status(self, stream=None) -> int:
         return ep_check_status(self.ws, stream)
+
+
+class EpGroupBuffers:
+    """Device buffers of the group-deduplicated path (plumbing) on top of an
+    EpBuffers of the same shape: group rows at capacity T*min(G,k), their
+    restricted routing, the token -> group-row handle, and the handle of the
+    local expert permutation (whose rows land in the EpBuffers' receive
+    buffers)."""
+
+    def __init__(self, bufs: EpBuffers):
+        s = bufs.shape
+        T, H, G, k = s.num_tokens, s.hidden, s.num_groups, s.topk
+        self.bufs, self.shape, d = bufs, s, bufs.device
+        cap = T * min(G, k)
+        self.capacity = cap
+        elt = 1 if s.x_dtype == FP8_E4M3 else 2
+        self.group_x = torch.empty((cap, H * elt), dtype=torch.uint8, device=d)
+        nsc = H // s.scale_block if s.x_dtype == FP8_E4M3 else 0
+        self.group_scales = torch.empty((cap, nsc), dtype=torch.float32, device=d) if nsc else None
+        self.group_src_idx = torch.empty(cap, dtype=torch.int32, device=d)
+        self.group_topk_idx = torch.empty((cap, k), dtype=torch.int32, device=d)
+        self.group_topk_weights = torch.empty((cap, k), dtype=torch.float32, device=d)
+        self.group_offsets = torch.empty(G + 1, dtype=torch.int32, device=d)
+        self.token_group_row = torch.empty((T, G), dtype=torch.int32, device=d)
+        self.perm_src_idx = torch.empty(T * k, dtype=torch.int32, device=d)
+        self.perm_slot_to_row = torch.empty((cap, k), dtype=torch.int32, device=d)
+
+    def dispatch_groups(self, x, x_scales, topk_idx, topk_weights, stream=None):
+        b = self.bufs
+        ep_dispatch_groups(self.shape, x, x_scales, topk_idx, topk_weights, b.is_token_in_group,
+                           b.tokens_per_group, self.group_x, self.group_scales, self.group_src_idx,
+                           self.group_topk_idx, self.group_topk_weights, self.group_offsets, self.token_group_row,
+                           b.ws, stream)
+
+    def permute(self, stream=None):
+        b = self.bufs
+        ep_group_permute(self.shape, self.group_x, self.group_scales, self.group_topk_idx, self.group_topk_weights,
+                         b.tokens_per_expert, b.recv_x, b.recv_scales, self.perm_src_idx, b.recv_weights,
+                         b.expert_offsets, self.perm_slot_to_row, b.ws, stream)
+
+    def reduce(self, expert_out, group_out, out_dtype=BF16, check_src=True, stream=None):
+        b = self.bufs
+        ep_group_reduce(self.shape, expert_out, self.perm_src_idx if check_src else None, b.recv_weights,
+                        self.perm_slot_to_row, self.group_offsets, group_out, out_dtype, b.ws, stream)
+
+    def combine_groups(self, group_rows, out, out_dtype=BF16, check_src=True, stream=None):
+        ep_combine_groups(self.shape, group_rows, self.group_src_idx if check_src else None, self.token_group_row,
+                          out, out_dtype, self.bufs.ws, stream)

@@ -83,6 +83,25 @@ DispatchPlan plan_dispatch(const moedisp_shape& s) {
     return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1);
 }
 
+// Group-deduplicated dispatch: the scatter over groups (k = E = G slots per
+// token, from the layout's bitmap).
+static moedisp_shape group_shape(const moedisp_shape& s) {
+    moedisp_shape g = s;
+    g.topk = s.num_groups;
+    g.num_experts = s.num_groups;
+    return g;
+}
+
+DispatchPlan plan_dispatch_groups(const moedisp_shape& s) { return plan_dispatch(group_shape(s)); }
+
+// The group rows seen as tokens (T * min(G, k) of them, the capacity of the
+// group dispatch), for the local expert permutation and reduce.
+moedisp_shape group_rows_shape(const moedisp_shape& s) {
+    moedisp_shape g = s;
+    g.num_tokens = s.num_tokens * (s.num_groups < s.topk ? s.num_groups : s.topk);
+    return g;
+}
+
 // Quantising scatter: a lane unit is 16 channels (32 source bytes, 16 code
 // bytes); column ranges are whole waves so that no scale block (<= 64 lanes)
 // straddles two of them.
@@ -113,12 +132,18 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsPlan plan_workspace(const moedisp_shape& s) {
     WsPlan w;
     w.layout_blocks = s.num_tokens > 0 ? ceil_div(s.num_tokens, kLayoutTokensPerBlock) : 1;
-    const DispatchPlan d = plan_dispatch(s);
     w.partial_offset = sizeof(WsHeader);
     const size_t partial_bytes = (size_t)w.layout_blocks * (s.num_experts + s.num_groups) * sizeof(int32_t);
     w.counts_offset = align256(w.partial_offset + partial_bytes);
-    const size_t count_bytes = (size_t)d.tile_stride * s.num_experts * sizeof(int32_t);
-    w.total = align256(w.counts_offset + count_bytes);
+    // per-tile counts of the largest dispatch the shape allows: over tokens,
+    // over groups (group-deduplicated dispatch) or over group rows (their
+    // local expert permutation)
+    const size_t flat = (size_t)plan_dispatch(s).tile_stride * s.num_experts;
+    const size_t groups = (size_t)plan_dispatch_groups(s).tile_stride * s.num_groups;
+    const size_t rows = (size_t)plan_dispatch(group_rows_shape(s)).tile_stride * s.num_experts;
+    size_t count_words = flat > groups ? flat : groups;
+    if (rows > count_words) count_words = rows;
+    w.total = align256(w.counts_offset + count_words * sizeof(int32_t));
     return w;
 }
 
@@ -189,10 +214,13 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
 // Checks shared by the dispatch calls; fills the launch arguments.  Pointers
 // a phase does not use may be passed as NULL-equivalents by the caller of that
 // phase only through the phase-specific wrappers below.
+// `ws_shape` (when not null) is the shape the workspace was sized and laid
+// out for, if it differs from the dispatched one (the group rows).
 static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
                          const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x,
                          float* recv_scales, int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
-                         int32_t* slot_to_row, void* ws, size_t ws_bytes, bool scatter, DispatchArgs* a) {
+                         int32_t* slot_to_row, void* ws, size_t ws_bytes, bool scatter, DispatchArgs* a,
+                         const moedisp_shape* ws_shape = nullptr) {
     int st = check_shape(s);
     if (st) return st;
     const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
@@ -207,8 +235,9 @@ static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_s
         !aligned(tokens_per_expert, 4) || !aligned(recv_src_idx, 4) || !aligned(recv_weights, 4) ||
         !aligned(expert_offsets, 4) || !aligned(slot_to_row, 4))
         return MOEDISP_ERR_MISALIGNED;
-    if ((st = check_ws(s, ws, ws_bytes))) return st;
-    const WsPlan w = plan_workspace(*s);
+    if (!ws_shape) ws_shape = s;
+    if ((st = check_ws(ws_shape, ws, ws_bytes))) return st;
+    const WsPlan w = plan_workspace(*ws_shape);
     a->T = s->num_tokens;
     a->k = s->topk;
     a->E = s->num_experts;
@@ -218,6 +247,11 @@ static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_s
     a->q_block_lanes = 0;
     a->q_scales_per_row = 0;
     a->recv_qscales = nullptr;
+    a->bitmap = nullptr;
+    a->src_k = s->topk;
+    a->experts_per_group = s->num_experts / s->num_groups;
+    a->recv_topk_idx = nullptr;
+    a->recv_topk_weights = nullptr;
     a->capacity = s->num_tokens * s->topk;
     a->plan = plan_dispatch(*s);
     a->x = (const v4u*)x;
@@ -315,6 +349,11 @@ static int quant_args(const moedisp_shape* s, int32_t quant_block, int32_t scale
     a->expert_offsets = const_cast<int32_t*>(expert_offsets);
     a->slot_to_row = slot_to_row;
     a->recv_qscales = recv_scales;
+    a->bitmap = nullptr;
+    a->src_k = s->topk;
+    a->experts_per_group = s->num_experts / s->num_groups;
+    a->recv_topk_idx = nullptr;
+    a->recv_topk_weights = nullptr;
     a->hdr = (WsHeader*)ws;
     a->tile_counts = (int32_t*)((char*)ws + w.counts_offset);
     return MOEDISP_OK;
@@ -370,9 +409,141 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     a.recv_src_idx = recv_src_idx;
     a.recv_weights = recv_weights;
     a.slot_to_row = slot_to_row;
+    a.row_limit = nullptr;
     a.out = out;
     a.hdr = (WsHeader*)ws;
     return hip_status(launch_combine(a, out_dtype == MOEDISP_FP32, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Group-deduplicated (high-throughput) path
+
+int ep_dispatch_groups(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                       const float* topk_weights, const uint32_t* is_token_in_group, const int32_t* tokens_per_group,
+                       void* recv_x, float* recv_scales, int32_t* recv_src_idx, int32_t* recv_topk_idx,
+                       float* recv_topk_weights, int32_t* group_offsets, int32_t* token_group_row, void* ws,
+                       size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
+    if (!tokens_per_group || !group_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !is_token_in_group || !recv_x ||
+                              !recv_src_idx || !recv_topk_idx || !recv_topk_weights || !token_group_row))
+        return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && fp8 && (!x_scales || !recv_scales)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOEDISP_ERR_MISALIGNED;
+    if (!aligned(x_scales, 4) || !aligned(recv_scales, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+        !aligned(is_token_in_group, 4) || !aligned(tokens_per_group, 4) || !aligned(recv_src_idx, 4) ||
+        !aligned(recv_topk_idx, 4) || !aligned(recv_topk_weights, 4) || !aligned(group_offsets, 4) ||
+        !aligned(token_group_row, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    const WsPlan w = plan_workspace(*s);
+    DispatchArgs a;
+    a.T = s->num_tokens;
+    a.k = s->num_groups;
+    a.E = s->num_groups;
+    a.row16 = (int)(row_bytes(*s) / 16);
+    a.out16 = a.row16;
+    a.scale_words = fp8 ? scales_per_row(*s) : 0;
+    a.q_block_lanes = 0;
+    a.q_scales_per_row = 0;
+    a.capacity = group_rows_shape(*s).num_tokens;
+    a.plan = plan_dispatch_groups(*s);
+    a.x = (const v4u*)x;
+    a.x_scales = fp8 ? x_scales : nullptr;
+    a.topk_idx = topk_idx;
+    a.topk_weights = topk_weights;
+    a.tokens_per_expert = tokens_per_group;
+    a.recv_x = (v4u*)recv_x;
+    a.recv_scales = fp8 ? recv_scales : nullptr;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_weights = nullptr;
+    a.expert_offsets = group_offsets;
+    a.slot_to_row = token_group_row;
+    a.recv_qscales = nullptr;
+    a.bitmap = is_token_in_group;
+    a.src_k = s->topk;
+    a.experts_per_group = s->num_experts / s->num_groups;
+    a.recv_topk_idx = recv_topk_idx;
+    a.recv_topk_weights = recv_topk_weights;
+    a.hdr = (WsHeader*)ws;
+    a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
+    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+}
+
+int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* group_scales,
+                     const int32_t* recv_topk_idx, const float* recv_topk_weights, const int32_t* tokens_per_expert,
+                     void* recv_x, float* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                     int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    const moedisp_shape rs = group_rows_shape(*s);
+    DispatchArgs a;
+    // the workspace of the token shape also holds the group rows' tile counts
+    st = dispatch_args(&rs, group_x, group_scales, recv_topk_idx, recv_topk_weights, tokens_per_expert, recv_x,
+                       recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a, s);
+    if (st) return st;
+    a.capacity = s->num_tokens * s->topk;  // the receive buffers hold T*k rows
+    if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
+    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+}
+
+// The combine kernel over `rows` output rows of `k` slots each.
+static int combine_call(const moedisp_shape* s, int rows, int k, int capacity, const void* in,
+                        const int32_t* src_check, const float* weights, const int32_t* slot_to_row,
+                        const int32_t* row_limit, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                        void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (out_dtype != MOEDISP_BF16 && out_dtype != MOEDISP_FP32) return MOEDISP_ERR_UNSUPPORTED;
+    if ((size_t)s->hidden * 2 % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    if (rows > 0 && (!in || !slot_to_row || !out)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(in, 16) || !aligned(out, 16)) return MOEDISP_ERR_MISALIGNED;
+    if (!aligned(src_check, 4) || !aligned(weights, 4) || !aligned(slot_to_row, 4) || !aligned(row_limit, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    if (rows == 0) return MOEDISP_OK;
+    moedisp_shape cs = *s;
+    cs.num_tokens = rows;
+    cs.topk = k;
+    const CombinePlan p = plan_combine(cs);
+    CombineArgs a;
+    a.T = rows;
+    a.k = k;
+    a.row16 = (int)((size_t)s->hidden * 2 / 16);
+    a.capacity = capacity;
+    a.col_splits = p.col_splits;
+    a.threads = p.threads;
+    a.expert_out = (const v4u*)in;
+    a.recv_src_idx = src_check;
+    a.recv_weights = weights;
+    a.slot_to_row = slot_to_row;
+    a.row_limit = row_limit;
+    a.out = out;
+    a.hdr = (WsHeader*)ws;
+    return hip_status(launch_combine(a, out_dtype == MOEDISP_FP32, (hipStream_t)stream));
+}
+
+int ep_group_reduce(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,
+                    const float* recv_weights, const int32_t* slot_to_row, const int32_t* group_offsets,
+                    void* group_out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+    if (!s) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (!recv_weights || !group_offsets)) return MOEDISP_ERR_INVALID_ARG;
+    const int rows = check_shape(s) == MOEDISP_OK ? group_rows_shape(*s).num_tokens : 0;
+    return combine_call(s, rows, s->topk, s->num_tokens * s->topk, expert_out, recv_src_idx, recv_weights,
+                        slot_to_row, group_offsets ? group_offsets + s->num_groups : nullptr, group_out, out_dtype,
+                        ws, ws_bytes, stream);
+}
+
+int ep_combine_groups(const moedisp_shape* s, const void* group_rows, const int32_t* recv_src_idx,
+                      const int32_t* token_group_row, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                      void* stream) {
+    if (!s) return MOEDISP_ERR_INVALID_ARG;
+    const int cap = check_shape(s) == MOEDISP_OK ? group_rows_shape(*s).num_tokens : 0;
+    return combine_call(s, s->num_tokens, s->num_groups, cap, group_rows, recv_src_idx, nullptr, token_group_row,
+                        nullptr, out, out_dtype, ws, ws_bytes, stream);
 }
 
 int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_status) {

@@ -9,13 +9,18 @@
 //     out[t][h] = sum_{j = 0..k-1, slot routed} recv_weights[r] * expert_out[r][h],
 //     r = slot_to_row[t][j],
 // accumulated in fp32 by fused multiply-add in ascending j from 0, then rounded
-// once to bf16 (nearest-even, v_cvt_pk_bf16_f32) or stored as fp32.
+// once to bf16 (nearest-even, v_cvt_pk_bf16_f32) or stored as fp32.  The same
+// kernel serves the group path: the local reduce of each (token, group) row
+// (rows past a device-side row limit are skipped) and the sum of a token's
+// group rows (no weights: a fused multiply-add by 1 is the plain fp32 add).
 //
 // How.  One workgroup per (token, column range).  The token's k rows and
 // weights are uniform across the workgroup, so they come through scalar loads;
 // the handle is checked there (row inside the receive buffer and, when
 // recv_src_idx is given, naming this token) and a slot that fails is skipped
-// at accumulation, with BAD_HANDLE raised.  Each lane owns U 16-byte units (8 bf16) of the output
+// at accumulation, with BAD_HANDLE raised.  The token's routed slots are
+// compacted (slot order kept) and a switch on their count picks an unrolled
+// gather, so no masked slot costs a load.  Each lane owns U 16-byte units (8 bf16) of the output
 // row (U = 1 for k = 8: 896 lanes cover a 7168-wide row in one pass): it
 // issues all k*U gathered 16-byte loads before the first FMA, so each lane
 // keeps k*U loads in flight, then accumulates slot by slot in order.
@@ -74,13 +79,75 @@ __device__ inline int handle_row(const CombineArgs& a, int t, int j, float* w, u
         return -1;
     }
     if (r >= 0) {
-        *w = a.recv_weights[r];
+        *w = a.recv_weights ? a.recv_weights[r] : 1.0f;
         if (a.recv_src_idx && a.recv_src_idx[r] != t) {
             *err |= MOEDISP_DEV_BAD_HANDLE;
             return -1;
         }
     }
     return r;
+}
+
+// Weighted sum over N compacted slots (rows crow[0..N), in slot order) for
+// this lane's columns.  All N*U row loads of a pass are issued back to back
+// (no per-slot branch); the first pass is issued before the weights and the
+// source check are fetched.  A slot whose row fails the source check is
+// skipped at accumulation.
+template <int N, int U, bool kF32>
+__device__ inline void gather_sum(const CombineArgs& a, int t, int c0, int c1, const int* crow, uint32_t* err) {
+    const int tid = threadIdx.x;
+    const int nth = blockDim.x;
+    int c = c0 + tid;
+    v4u v[N > 0 ? N : 1][U];
+#pragma unroll
+    for (int p = 0; p < N; ++p)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[p][u] = __builtin_nontemporal_load(a.expert_out + (size_t)crow[p] * a.row16 + min(c + u * nth, c1 - 1));
+    asm volatile("" ::: "memory");
+    float w[N > 0 ? N : 1];
+    bool ok[N > 0 ? N : 1];
+#pragma unroll
+    for (int p = 0; p < N; ++p) {
+        w[p] = a.recv_weights ? a.recv_weights[crow[p]] : 1.0f;
+        ok[p] = true;
+    }
+    if (a.recv_src_idx) {
+        int src[N > 0 ? N : 1];
+#pragma unroll
+        for (int p = 0; p < N; ++p) src[p] = a.recv_src_idx[crow[p]];
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            ok[p] = src[p] == t;
+            *err |= ok[p] ? 0u : MOEDISP_DEV_BAD_HANDLE;
+        }
+    }
+    while (c < c1) {
+        float acc[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+#pragma unroll
+        for (int p = 0; p < N; ++p) {
+            if (!ok[p]) continue;
+#pragma unroll
+            for (int u = 0; u < U; ++u) fma8(acc[u], w[p], v[p][u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u * nth;
+            if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
+        }
+        c += U * nth;
+        if (c >= c1) break;
+#pragma unroll
+        for (int p = 0; p < N; ++p)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[p][u] = __builtin_nontemporal_load(a.expert_out + (size_t)crow[p] * a.row16 +
+                                                     min(c + u * nth, c1 - 1));
+    }
 }
 
 // KC: compile-time k (0 = runtime k, slots gathered one at a time).
@@ -94,17 +161,13 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
     const int c0 = split * per_split;
     const int c1 = min(a.row16, c0 + per_split);
     uint32_t err = 0;
+    if (a.row_limit && t >= *a.row_limit) return;  // uniform: whole workgroup
 
     if constexpr (KC > 0) {
-        // Loads carry no per-slot branch, so the compiler issues all k*U of
-        // them back to back: a slot that is masked or fails the handle check
-        // loads an in-bounds fallback row (the token's first good row, else
-        // row 0; capacity >= 1 whenever a kernel runs) and is skipped at the
-        // FMA; idle lanes of the last wave load a clamped column and store
-        // nothing.
+        // the token's rows inside the receive buffer, compacted in slot order
+        // (uniform values: scalar registers and selects, no indexing)
         int rows[KC];
         bool use[KC];
-        float wts[KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j) {
             const int r = a.slot_to_row[(size_t)t * KC + j];
@@ -112,60 +175,34 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
             use[j] = r >= 0 && r < a.capacity;
             rows[j] = r;
         }
-        int fallback = 0;
+        int n = 0;
 #pragma unroll
-        for (int j = KC - 1; j >= 0; --j)
-            if (use[j]) fallback = rows[j];
+        for (int j = 0; j < KC; ++j) n += use[j] ? 1 : 0;
+        if (n == KC) {  // every slot routed (the common case): no compaction
+            gather_sum<KC, U, kF32>(a, t, c0, c1, rows, &err);
+        } else {
+        int crow[KC];
 #pragma unroll
-        for (int j = 0; j < KC; ++j) rows[j] = use[j] ? rows[j] : fallback;
-        // first pass of row loads, issued before the weights are fetched
-        v4u v[KC][U];
-        int c = c0 + tid;
+        for (int p = 0; p < KC; ++p) crow[p] = 0;
+        int m = 0;
 #pragma unroll
-        for (int j = 0; j < KC; ++j)
+        for (int j = 0; j < KC; ++j) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 +
-                                                     min(c + u * nth, c1 - 1));
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int j = 0; j < KC; ++j) wts[j] = a.recv_weights[rows[j]];
-        if (a.recv_src_idx) {
-            int src[KC];
-#pragma unroll
-            for (int j = 0; j < KC; ++j) src[j] = a.recv_src_idx[rows[j]];
-#pragma unroll
-            for (int j = 0; j < KC; ++j) {
-                const bool bad = use[j] && src[j] != t;
-                err |= bad ? MOEDISP_DEV_BAD_HANDLE : 0u;
-                use[j] = use[j] && !bad;
-            }
+            for (int p = 0; p <= j; ++p)
+                if (use[j] && m == p) crow[p] = rows[j];
+            m += use[j] ? 1 : 0;
         }
-        while (c < c1) {
-            float acc[U][8];
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-#pragma unroll
-            for (int j = 0; j < KC; ++j) {
-                if (!use[j]) continue;
-#pragma unroll
-                for (int u = 0; u < U; ++u) fma8(acc[u], wts[j], v[j][u]);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int cc = c + u * nth;
-                if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
-            }
-            c += U * nth;
-            if (c >= c1) break;
-#pragma unroll
-            for (int j = 0; j < KC; ++j)
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[j][u] = __builtin_nontemporal_load(a.expert_out + (size_t)rows[j] * a.row16 +
-                                                         min(c + u * nth, c1 - 1));
+        switch (n) {
+            case 0: gather_sum<0, U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 1: gather_sum<(KC >= 1 ? 1 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 2: gather_sum<(KC >= 2 ? 2 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 3: gather_sum<(KC >= 3 ? 3 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 4: gather_sum<(KC >= 4 ? 4 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 5: gather_sum<(KC >= 5 ? 5 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 6: gather_sum<(KC >= 6 ? 6 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            case 7: gather_sum<(KC >= 7 ? 7 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+            default: gather_sum<(KC >= 8 ? 8 : 0), U, kF32>(a, t, c0, c1, crow, &err); break;
+        }
         }
     } else {
         if (tid == 0)

@@ -18,10 +18,11 @@
 //    expert_offsets, the exclusive scan of tokens_per_expert.
 //  - scatter kernel, one workgroup per `block_tokens` tokens (and column
 //    range): for each of its slots with expert e, the row is
-//      expert_offsets[e] + (counts of e in the earlier tiles, summed by
-//      several lanes with 16-byte loads from the L2-resident count table)
-//      + (the number of earlier slots of its own tile with expert e, counted
-//      from an LDS copy of the tile's routing).
+//      expert_offsets[e] + (counts of e in the earlier tiles, from 16-byte
+//      loads of the L2-resident count table)
+//      + (the number of earlier slots of its own tile with expert e, from an
+//      LDS copy of the tile's routing),
+//    both sums split over several lanes per slot.
 //    Every workgroup does this small prefix sum for itself, so no workgroup
 //    ever waits for another: on a multi-XCD part a cross-workgroup wait (a
 //    chained or decoupled look-back) costs a cross-XCD round trip per hop,
@@ -78,6 +79,20 @@ __device__ long long block_exclusive_scan(const int32_t* __restrict__ in, int n,
     return total;
 }
 
+// Expert (or, in group mode, group) of flat slot s = t*k + j, -1 if masked;
+// sets BAD_EXPERT_ID in *err for an id outside {-1} U [0,E).
+__device__ inline int slot_id(const DispatchArgs& a, size_t s, uint32_t* err) {
+    if (a.bitmap) {
+        const size_t t = s / (unsigned)a.k;
+        const int g = (int)(s - t * a.k);
+        return ((a.bitmap[t] >> g) & 1u) ? g : -1;
+    }
+    const int id = a.topk_idx[s];
+    if (id >= 0 && id < a.E) return id;
+    if (id != -1) *err |= MOEDISP_DEV_BAD_EXPERT_ID;
+    return -1;
+}
+
 __global__ __launch_bounds__(kThreads) void moedisp_count(DispatchArgs a) {
     const DispatchPlan& P = a.plan;
     extern __shared__ int32_t dyn[];  // hist[E]
@@ -96,11 +111,8 @@ __global__ __launch_bounds__(kThreads) void moedisp_count(DispatchArgs a) {
     __syncthreads();
     uint32_t err = 0;
     for (int s = tid; s < tile_slots; s += kThreads) {
-        const int id = a.topk_idx[(size_t)tile_t0 * k + s];
-        if (id >= 0 && id < E)
-            atomicAdd(&s_hist[id], 1);
-        else if (id != -1)
-            err |= MOEDISP_DEV_BAD_EXPERT_ID;
+        const int id = slot_id(a, (size_t)tile_t0 * k + s, &err);
+        if (id >= 0) atomicAdd(&s_hist[id], 1);
     }
     __syncthreads();
     for (int e = tid; e < E; e += kThreads) a.tile_counts[(size_t)e * P.tile_stride + tile] = s_hist[e];
@@ -156,11 +168,8 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
     const int k = a.k;
-    const int E = a.E;
-    for (int i = tid; i < b.first + b.blk_slots; i += nth) {
-        const int id = a.topk_idx[(size_t)b.tile_t0 * k + i];
-        s_ids[i] = (id >= 0 && id < E) ? id : -1;
-    }
+    uint32_t ignored = 0;  // bad ids are reported by the count kernel
+    for (int i = tid; i < b.first + b.blk_slots; i += nth) s_ids[i] = slot_id(a, (size_t)b.tile_t0 * k + i, &ignored);
     for (int q = tid; q < b.blk_slots; q += nth) sm.pre[q] = 0;
     if (tid == 0) {
         sm.routed = 0;
@@ -168,8 +177,10 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
     }
     __syncthreads();
 
-    // counts of each slot's expert in the earlier tiles: L lanes per slot,
-    // 16-byte loads of the expert's contiguous count column
+    // slots with the same expert before each of this workgroup's slots: in the
+    // earlier tiles (16-byte loads of the expert's contiguous count column)
+    // and earlier in this tile (the staged routing ids); L lanes per slot
+    // share both scans
     if (b.blk_slots > 0) {
         const int L = nth / b.blk_slots;  // >= 1: the plan keeps blk_slots <= threads
         if (tid < L * b.blk_slots) {
@@ -188,6 +199,8 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
 #pragma unroll
                     for (int u = 0; u < 4; ++u) sum += v[u].x + v[u].y + v[u].z + v[u].w;
                 }
+                const int s = b.first + q;
+                for (int u = l; u < s; u += L) sum += s_ids[u] == e;
                 if (l == 0) {
                     for (int j = n4 * 4; j < b.tile; ++j) sum += col[j];
                     sm.base[q] = a.expert_offsets[e];
@@ -205,10 +218,8 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
         const int e = s_ids[s];
         int row = -1;
         if (e >= 0) {
-            int before = 0;
-            for (int u = 0; u < s; ++u) before += s_ids[u] == e;
             const long long base = sm.base[q];
-            const long long r = base + sm.pre[q] + before;
+            const long long r = base + sm.pre[q];
             if (r < 0 || r < base || r >= base + sm.len[q] || r >= a.capacity)
                 err |= MOEDISP_DEV_BAD_LAYOUT;
             else
@@ -220,7 +231,9 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
     return err;
 }
 
-// Handle of the workgroup's slots: slot -> row, row -> source token and weight.
+// Handle of the workgroup's slots: slot -> row, row -> source token and
+// weight (group mode: row -> source token and the token's slots restricted to
+// the row's group).
 __device__ void write_handle(const DispatchArgs& a, const ScatterBlock& b, const ScatterSmem& sm) {
     for (int q = threadIdx.x; q < b.blk_slots; q += blockDim.x) {
         const size_t slot = (size_t)b.blk_t0 * a.k + q;
@@ -228,7 +241,23 @@ __device__ void write_handle(const DispatchArgs& a, const ScatterBlock& b, const
         a.slot_to_row[slot] = row;
         if (row >= 0) {
             a.recv_src_idx[row] = b.blk_t0 + q / a.k;
-            a.recv_weights[row] = a.topk_weights[slot];
+            if (!a.bitmap) a.recv_weights[row] = a.topk_weights[slot];
+        }
+    }
+    if (a.bitmap) {
+        const int sk = a.src_k;
+        const int n = b.blk_slots * sk;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+            const int q = i / sk;
+            const int j = i - q * sk;
+            const int row = sm.rows[q];
+            if (row < 0) continue;
+            const int g = q % a.k;
+            const size_t src = (size_t)(b.blk_t0 + q / a.k) * sk + j;
+            const int id = a.topk_idx[src];
+            const bool here = id >= 0 && id < a.E * a.experts_per_group && id / a.experts_per_group == g;
+            a.recv_topk_idx[(size_t)row * sk + j] = here ? id : -1;
+            a.recv_topk_weights[(size_t)row * sk + j] = here ? a.topk_weights[src] : 0.0f;
         }
     }
 }
@@ -238,14 +267,19 @@ __device__ void write_handle(const DispatchArgs& a, const ScatterBlock& b, const
 __device__ uint32_t check_total(const DispatchArgs& a, ScatterSmem& sm) {
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
-    const int n = a.T * a.k;
     int32_t routed = 0;
-    for (int i0 = tid; i0 < n; i0 += 8 * nth) {
-        int32_t v[8];
+    if (a.bitmap) {
+        const uint32_t mask = a.k >= 32 ? 0xFFFFFFFFu : ((1u << a.k) - 1u);
+        for (int t = tid; t < a.T; t += nth) routed += __popc(a.bitmap[t] & mask);
+    } else {
+        const int n = a.T * a.k;
+        for (int i0 = tid; i0 < n; i0 += 8 * nth) {
+            int32_t v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nth < n) ? a.topk_idx[i0 + u * nth] : -1;
+            for (int u = 0; u < 8; ++u) v[u] = (i0 + u * nth < n) ? a.topk_idx[i0 + u * nth] : -1;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) routed += (v[u] >= 0 && v[u] < a.E);
+            for (int u = 0; u < 8; ++u) routed += (v[u] >= 0 && v[u] < a.E);
+        }
     }
     if (routed) atomicAdd(&sm.routed, routed);
     __syncthreads();
@@ -294,6 +328,18 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
                     a.recv_scales[(size_t)row * a.scale_words + c] =
                         a.x_scales[(size_t)(b.blk_t0 + q / k) * a.scale_words + c];
             }
+        }
+    }
+
+    // group mode: rows past the last group row are marked unrouted, so that the
+    // whole capacity can be handed to the local expert permutation
+    if (a.bitmap) {
+        const int rg = a.expert_offsets[a.E];  // a bad total is reported by the count kernel
+        if (rg >= 0 && rg <= a.capacity) {
+            const size_t end = (size_t)a.capacity * a.src_k;
+            for (size_t i = (size_t)rg * a.src_k + (size_t)blockIdx.x * nth + tid; i < end;
+                 i += (size_t)gridDim.x * nth)
+                a.recv_topk_idx[i] = -1;
         }
     }
 

@@ -24,10 +24,11 @@ __device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active)
     uint64_t peers = active;
 #pragma unroll
     for (int b = 0; b < 12; ++b) {
-        if (b >= nbits) break;  // nbits is uniform
-        const bool bit = (key >> b) & 1u;
-        const uint64_t ones = __ballot(bit);
-        peers &= bit ? ones : ~ones;
+        if (b < nbits) {  // nbits is uniform
+            const bool bit = (key >> b) & 1u;
+            const uint64_t ones = __ballot(bit);
+            peers &= bit ? ones : ~ones;
+        }
     }
     return peers;
 }
@@ -99,13 +100,14 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
             if (ids[j] >= 0 && ids[j] == ids[jj]) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        if (j >= k) break;  // k is uniform
-        const int id = ids[j];
-        const bool routed = id >= 0;
-        if (routed) gmask |= 1u << group_of((uint32_t)id, a);
-        const uint64_t active = __ballot(routed);
-        const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
-        if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+        if (j < k) {  // k is uniform
+            const int id = ids[j];
+            const bool routed = id >= 0;
+            if (routed) gmask |= 1u << group_of((uint32_t)id, a);
+            const uint64_t active = __ballot(routed);
+            const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
+            if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+        }
     }
     for (int g = 0; g < a.G; ++g) {
         const uint64_t in_g = __ballot((gmask >> g) & 1u);

@@ -75,6 +75,8 @@ struct WsPlan {
 
 DispatchPlan plan_dispatch(const moedisp_shape& s);
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s);
+DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
+moedisp_shape group_rows_shape(const moedisp_shape& s);
 CombinePlan plan_combine(const moedisp_shape& s);
 WsPlan plan_workspace(const moedisp_shape& s);
 
@@ -120,6 +122,15 @@ struct DispatchArgs {
     int32_t* expert_offsets;
     int32_t* slot_to_row;
     void* recv_qscales;  // quantising scatter: fp32 or UE8M0 bytes [rows][q_scales_per_row]
+    // group mode (group-deduplicated dispatch) when bitmap != nullptr: the
+    // "experts" are the G groups, slot g of token t is routed iff bit g of
+    // bitmap[t] is set, k = E = G, and each row also gets the token's src_k
+    // slots restricted to its group (recv_topk_idx / recv_topk_weights)
+    const uint32_t* bitmap;
+    int src_k;
+    int experts_per_group;
+    int32_t* recv_topk_idx;
+    float* recv_topk_weights;
     WsHeader* hdr;
     int32_t* tile_counts;
 };
@@ -132,8 +143,9 @@ struct CombineArgs {
     int threads;
     const v4u* expert_out;
     const int32_t* recv_src_idx;
-    const float* recv_weights;
+    const float* recv_weights;  // nullptr: every weight is 1 (plain sum)
     const int32_t* slot_to_row;
+    const int32_t* row_limit;   // if set, output rows >= *row_limit are skipped (not written)
     void* out;
     WsHeader* hdr;
 };

@@ -46,3 +46,23 @@ def algorithmic_bytes_quant(T: int, H: int, E: int, k: int, R: int, block: int, 
                 + (E + 1) * 4)        # expert_offsets
     notify = T * k * 4 + (E + 1) * 4
     return dict(dispatch=dispatch, notify=notify, scatter=dispatch - notify)
+
+
+def algorithmic_bytes_groups(T: int, H: int, E: int, G: int, k: int, R: int, Rg: int, x_elt: int = 2,
+                             scale_block: int = 0) -> dict:
+    """The group-deduplicated path: group dispatch (one row per (token,
+    group)), local expert permutation, local reduce, group combine."""
+    row = H * x_elt + ((H // scale_block) * 4 if scale_block else 0)
+    out_row = H * 2
+    dispatch_groups = (T * row + Rg * row      # rows read once, one group row per (token, group)
+                       + 2 * T * k * 4 + T * 4  # topk_idx, topk_weights, bitmap
+                       + Rg * 4 + Rg * k * 8    # recv_src_idx, restricted ids and weights
+                       + (G + 1) * 4 + T * G * 4)
+    permute = (Rg * row + R * row             # group rows in, expert rows out
+               + Rg * k * 8                   # restricted ids and weights
+               + 2 * R * 4 + Rg * k * 4       # recv_src_idx, recv_weights, slot_to_row
+               + (E + 1) * 4)
+    reduce = R * out_row + Rg * out_row + Rg * k * 4 + R * 4
+    combine_groups = Rg * out_row + T * out_row + T * G * 4
+    return dict(dispatch_groups=dispatch_groups, permute=permute, reduce=reduce, combine_groups=combine_groups,
+                total=dispatch_groups + permute + reduce + combine_groups)

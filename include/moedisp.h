@@ -185,6 +185,70 @@ int ep_dispatch_scatter_quant(const moedisp_shape* shape, int32_t quant_block, i
                               int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                               int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
 
+/* Group-deduplicated (high-throughput) path.  "MSCCLPP EP implementation -
+ * #852": in the high-throughput path the layout's token-in-rank flags decide
+ * which ranks receive a token, each such rank receives it once (the bench
+ * commits describe the receiver's layout as one row per (token, source rank)
+ * pair), and the receiver orders its rows by local expert.  A rank is a
+ * destination group here; rows of group g are what GPU g would receive.
+ *
+ * ep_dispatch_groups: one row per (token, group it reaches), group by group,
+ * tokens in order.  Row of (t, g):
+ *   group_offsets[g] + #{t' < t : bit g of is_token_in_group[t'] is set}.
+ *   is_token_in_group  uint32 [T] and tokens_per_group int32 [G] from
+ *                      ep_get_dispatch_layout of the same topk_idx (bits >= G
+ *                      are ignored).
+ *   recv_x             [T*min(G,k)][H] capacity (bf16 or fp8 bytes, copied).
+ *   recv_scales        fp32 [T*min(G,k)][H/scale_block] for fp8, NULL for bf16.
+ *   recv_src_idx       int32 [T*min(G,k)]: source token of each row.
+ *   recv_topk_idx      int32 [T*min(G,k)][k]: the token's slot j expert where
+ *                      that expert lies in the row's group, else -1 (global ids).
+ *   recv_topk_weights  fp32 [T*min(G,k)][k]: topk_weights[t][j] where
+ *                      recv_topk_idx >= 0, else 0.
+ *   group_offsets      int32 [G+1]: exclusive prefix of tokens_per_group;
+ *                      [G] = R_g, the number of group rows.
+ *   token_group_row    int32 [T][G]: row of (t, g), -1 if t does not reach g.
+ * Rows at or past R_g get recv_topk_idx = -1 (all k slots) and are otherwise
+ * not written.  Status bits: BAD_LAYOUT.
+ *
+ * ep_group_permute: the local expert permutation of the group rows, i.e.
+ * ep_dispatch applied to the T*min(G,k) group rows as tokens, with
+ * recv_topk_idx / recv_topk_weights as their routing and the layout's
+ * tokens_per_expert (rows past R_g hold recv_topk_idx = -1, as
+ * ep_dispatch_groups leaves them, and route nothing).  Its outputs equal
+ * ep_dispatch's for the original tokens byte for byte (expert_offsets,
+ * recv_x, recv_scales, recv_weights), except that recv_src_idx names the group
+ * row and slot_to_row is [T*min(G,k)][k] over group rows.  recv_x and the
+ * other receive buffers hold T*k rows.
+ *
+ * ep_group_reduce: each group row's weighted sum of its expert outputs, i.e.
+ * ep_combine over the group rows through ep_group_permute's handle; rows at or
+ * past group_offsets[G] (read on the device) are skipped.
+ *   group_out  [T*min(G,k)][H] bf16 or fp32 (out_dtype).
+ *
+ * ep_combine_groups: out[t][h] = sum over g ascending with
+ * token_group_row[t][g] >= 0 of group_rows[that row][h] (bf16), accumulated in
+ * fp32 from 0; bf16 output is that sum rounded once to nearest-even.
+ *   recv_src_idx  ep_dispatch_groups' recv_src_idx (checks the handle) or NULL.
+ * Status bits of the last three: those of ep_dispatch / ep_combine. */
+int ep_dispatch_groups(const moedisp_shape* shape, const void* x, const float* x_scales,
+                       const int32_t* topk_idx, const float* topk_weights,
+                       const uint32_t* is_token_in_group, const int32_t* tokens_per_group, void* recv_x,
+                       float* recv_scales, int32_t* recv_src_idx, int32_t* recv_topk_idx,
+                       float* recv_topk_weights, int32_t* group_offsets, int32_t* token_group_row,
+                       void* ws, size_t ws_bytes, void* stream);
+int ep_group_permute(const moedisp_shape* shape, const void* group_x, const float* group_scales,
+                     const int32_t* recv_topk_idx, const float* recv_topk_weights,
+                     const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
+                     int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets,
+                     int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+int ep_group_reduce(const moedisp_shape* shape, const void* expert_out, const int32_t* recv_src_idx,
+                    const float* recv_weights, const int32_t* slot_to_row, const int32_t* group_offsets,
+                    void* group_out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+int ep_combine_groups(const moedisp_shape* shape, const void* group_rows, const int32_t* recv_src_idx,
+                      const int32_t* token_group_row, void* out, int32_t out_dtype, void* ws,
+                      size_t ws_bytes, void* stream);
+
 /* Combine: the reverse of dispatch through its handle.
  *   out[t][h] = sum over j = 0..k-1 in ascending order, skipping masked slots,
  *               of recv_weights[r] * expert_out[r][h] with r = slot_to_row[t][j],

@@ -148,6 +148,42 @@ def test_host_checks_dispatch_quant(lib):
                                          p(), p(), p(), 1 << 30, None) == B.ERR_UNSUPPORTED
 
 
+def test_host_checks_group_path(lib):
+    s = shape()
+    P = p
+    def groups(x=None, bm=None, tgr=None, goff=None, ws_bytes=1 << 30, sh=s):
+        return lib.ep_dispatch_groups(C.byref(sh), x or P(), None, P(), P(), bm or P(), P(), P(), None, P(), P(),
+                                      P(), goff or P(), tgr or P(), P(), ws_bytes, None)
+    assert groups(x=P(8)) == B.ERR_MISALIGNED
+    assert groups(bm=P(2)) == B.ERR_MISALIGNED
+    assert groups(ws_bytes=64) == B.ERR_WORKSPACE_TOO_SMALL
+    assert groups(sh=shape(E=255)) == B.ERR_INVALID_ARG
+    assert lib.ep_dispatch_groups(C.byref(s), P(), None, P(), P(), None, P(), P(), None, P(), P(), P(), P(), P(),
+                                  P(), 1 << 30, None) == B.ERR_INVALID_ARG          # null bitmap
+    fp8 = shape(dt=M.FP8_E4M3, sb=128)
+    assert groups(sh=fp8) == B.ERR_INVALID_ARG                                      # fp8 without scales
+    assert lib.ep_group_permute(C.byref(s), P(8), None, P(), P(), P(), P(), None, P(), P(), P(), P(), P(),
+                                1 << 30, None) == B.ERR_MISALIGNED
+    assert lib.ep_group_permute(C.byref(s), P(), None, P(), P(), P(), P(), None, P(), P(), P(), P(), P(),
+                                64, None) == B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.ep_group_reduce(C.byref(s), P(), None, P(), P(), P(), P(), M.FP8_E4M3, P(), 1 << 30,
+                               None) == B.ERR_UNSUPPORTED
+    assert lib.ep_group_reduce(C.byref(s), P(), None, None, P(), P(), P(), M.BF16, P(), 1 << 30,
+                               None) == B.ERR_INVALID_ARG                             # null weights
+    assert lib.ep_group_reduce(C.byref(s), P(), None, P(), P(), None, P(), M.BF16, P(), 1 << 30,
+                               None) == B.ERR_INVALID_ARG                             # null offsets
+    assert lib.ep_combine_groups(C.byref(s), P(4), None, P(), P(), M.BF16, P(), 1 << 30, None) == B.ERR_MISALIGNED
+    assert lib.ep_combine_groups(C.byref(s), P(), None, None, P(), M.BF16, P(), 1 << 30, None) == B.ERR_INVALID_ARG
+    assert lib.ep_combine_groups(None, P(), None, P(), P(), M.BF16, P(), 1 << 30, None) == B.ERR_INVALID_ARG
+
+
+def test_workspace_covers_group_rows(lib):
+    # the local permutation runs over T*min(G,k) group rows: the workspace
+    # must hold their per-tile counts too
+    for T, E, G, k in ((4096, 256, 8, 8), (100000, 64, 32, 8), (20000, 8, 8, 2)):
+        assert M.ep_workspace_bytes(shape(T=T, E=E, G=G, k=k)) >= 256 + 64 * 4 * E
+
+
 def test_host_checks_combine(lib):
     assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
     assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED

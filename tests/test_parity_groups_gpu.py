@@ -1,0 +1,136 @@
+"""GPU parity of the group-deduplicated (high-throughput) path against the
+CPU oracle (needs an MI355X): ep_dispatch_groups, ep_group_permute,
+ep_group_reduce and ep_combine_groups.
+
+Bit-exact: group offsets, the token -> group-row handle, group rows and
+scales, source tokens, restricted routing (ids and weight bits), the rows
+past the last group row marked unrouted, and everything the local expert
+permutation writes (its rows, offsets, weights and handle).  The local reduce
+and the group combine are held to the combine bar (max relative error 1e-3
+in fp32, at most one bf16 ulp); each runs on the oracle's own inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_get_dispatch_amd as M
+from combine_ep_get_dispatch_amd import workloads as W
+import gpu_harness as GH
+import oracle_checks as K
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    M.load()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def eq(g, o, what):
+    g = np.ascontiguousarray(g)
+    o = np.ascontiguousarray(o)
+    if g.dtype == np.float32:
+        g, o = g.view(np.uint32), o.view(np.uint32)
+    if not np.array_equal(g, o):
+        bad = np.argwhere(g != o) if g.shape == o.shape else None
+        raise AssertionError(f"{what} differs (shape {g.shape} vs {o.shape}), first at {None if bad is None else bad[:4]}")
+
+
+def run_groups(orc, wl, dev, sample_tokens=0, seed=0):
+    _say(f"[groups] {wl.name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k} {wl.x_dtype}")
+    h = K.ht_path(orc, wl)
+    gd, pm, Rg, R = h["gd"], h["pm"], h["Rg"], h["R"]
+    bufs = M.EpBuffers(GH.shape_of(wl), dev)
+    gb = M.EpGroupBuffers(bufs)
+    inp = GH.GpuInputs(wl, dev)
+    # stale values in the padding rows must not survive the call
+    gb.group_topk_idx.fill_(3)
+    bufs.layout(inp.topk_idx)
+    gb.dispatch_groups(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    st = bufs.status()
+    assert st == gd["status"], f"device status {st} != oracle {gd['status']}"
+    eq(gb.group_offsets.cpu().numpy(), gd["group_offsets"], "group_offsets")
+    eq(gb.token_group_row.cpu().numpy(), gd["token_group_row"], "token_group_row")
+    eq(gb.group_src_idx[:Rg].cpu().numpy(), gd["recv_src_idx"][:Rg], "group recv_src_idx")
+    eq(gb.group_topk_idx[:Rg].cpu().numpy(), gd["recv_topk_idx"][:Rg], "group recv_topk_idx")
+    eq(gb.group_topk_weights[:Rg].cpu().numpy(), gd["recv_topk_weights"][:Rg], "group recv_topk_weights")
+    assert np.all(gb.group_topk_idx[Rg:].cpu().numpy() == -1), "rows past R_g must be unrouted"
+    orx = np.ascontiguousarray(gd["recv_x"][:Rg]).view(np.uint8).reshape(Rg, wl.row_bytes)
+    eq(gb.group_x[:Rg].cpu().numpy(), orx, "group rows")
+    if gb.group_scales is not None:
+        eq(gb.group_scales[:Rg].cpu().numpy(), gd["recv_scales"][:Rg], "group scales")
+
+    gb.permute()
+    st = bufs.status()
+    assert st == 0, f"permute status {st}"
+    eq(bufs.expert_offsets.cpu().numpy(), pm["expert_offsets"], "permute expert_offsets")
+    prx = np.ascontiguousarray(pm["recv_x"][:R]).view(np.uint8).reshape(R, wl.row_bytes)
+    eq(bufs.recv_x[:R].cpu().numpy(), prx, "permuted rows")
+    eq(gb.perm_src_idx[:R].cpu().numpy(), pm["recv_src_idx"][:R], "permute recv_src_idx (group rows)")
+    eq(bufs.recv_weights[:R].cpu().numpy(), pm["recv_weights"][:R], "permute recv_weights")
+    eq(gb.perm_slot_to_row[:Rg].cpu().numpy(), pm["slot_to_row"], "permute slot_to_row")
+    assert np.all(gb.perm_slot_to_row[Rg:].cpu().numpy() == -1)
+    if bufs.recv_scales is not None:
+        eq(bufs.recv_scales[:R].cpu().numpy(), pm["recv_scales"][:R], "permuted scales")
+
+    # local reduce on the oracle's expert outputs
+    eo = GH.upload_expert_out(h["eo_bits"], wl.T * wl.k, wl.H, dev)
+    cap = gb.capacity
+    red32 = torch.empty((max(cap, 1), wl.H), dtype=torch.float32, device=dev)
+    red16 = torch.empty((max(cap, 1), wl.H), dtype=torch.bfloat16, device=dev)
+    gb.reduce(eo, red32, M.FP32)
+    gb.reduce(eo, red16, M.BF16)
+    assert bufs.status() == 0
+    o32, o16 = orc.combine(h["eo_bits"], pm["recv_weights"][:R], pm["slot_to_row"])
+    GH.assert_combine_close(red32[:Rg].cpu().numpy(), red16[:Rg].view(torch.int16).cpu().numpy().view(np.uint16),
+                            o32, o16)
+    # group combine on the oracle's group partials
+    grows = GH.upload_expert_out(h["part"], max(cap, 1), wl.H, dev)
+    of = torch.empty((max(wl.T, 1), wl.H), dtype=torch.float32, device=dev)
+    ob = torch.empty((max(wl.T, 1), wl.H), dtype=torch.bfloat16, device=dev)
+    gb.combine_groups(grows, of, M.FP32)
+    gb.combine_groups(grows, ob, M.BF16)
+    assert bufs.status() == 0
+    g32 = of[:wl.T].cpu().numpy()
+    g16 = ob[:wl.T].view(torch.int16).cpu().numpy().view(np.uint16)
+    if sample_tokens and wl.T > sample_tokens:
+        toks = np.sort(np.random.default_rng(seed).choice(wl.T, size=sample_tokens, replace=False))
+        toks[-1] = wl.T - 1
+        res = GH.assert_combine_close(g32[toks], g16[toks], h["out_f32"][toks], h["out_bf16"][toks])
+    else:
+        res = GH.assert_combine_close(g32, g16, h["out_f32"], h["out_bf16"])
+    _say(f"[groups] {wl.name} ok R_g={Rg} R={R} max_ulp={res['max_ulp']} exact_f32={res['exact_f32']:.4f}")
+
+
+CASES = {
+    "tiny": lambda: W.config(1),
+    "decode_fp8": lambda: W.config(4),
+    "dsv3_ragged": lambda: W.make_workload("dsv3_ragged", 601, 7168, 256, 8, 8, seed=31, expert_kind="scale_by_id"),
+    "zipf_ragged": lambda: W.make_workload("zipf_ragged", 777, 7168, 256, 8, 8, seed=32, routing="zipf",
+                                           mask_frac=0.05, expert_kind="scale_by_id"),
+    "mixtral_ragged": lambda: W.make_workload("mixtral_ragged", 3001, 4096, 8, 8, 2, seed=33,
+                                              expert_kind="double_odd"),
+    "groups_lt_k": lambda: W.make_workload("g_lt_k", 450, 512, 16, 2, 6, seed=70, mask_frac=0.2),
+    "one_group": lambda: W.make_workload("g1", 333, 256, 16, 1, 4, seed=71),
+    "groups_of_3": lambda: W.make_workload("g3", 300, 256, 24, 8, 4, seed=72, routing="zipf"),
+    "g32_k8": lambda: W.make_workload("g32", 129, 256, 64, 32, 8, seed=73),
+    "empty": lambda: W.make_workload("empty", 0, 256, 8, 2, 2, seed=74),
+    "all_masked": lambda: W.make_workload("all_masked", 40, 256, 8, 2, 2, seed=75, mask_frac=1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_group_path_parity(orc, dev, name):
+    run_groups(orc, CASES[name](), dev)
+
+
+def test_group_path_parity_full_size(orc, dev):
+    """DeepSeek-V3 prefill shape: every group row, permuted row and partial,
+    combine on 384 sampled tokens (the last always included)."""
+    run_groups(orc, W.config(2), dev, sample_tokens=384, seed=2)
