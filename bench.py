@@ -243,6 +243,87 @@ def run_gpu_groups(cid, steps, warmup, dev):
     return res
 
 
+def run_gpu_decode(cid, steps, warmup, dev):
+    """Decode-step latency on config `cid` (T=128): the four calls (layout,
+    notify, scatter, combine), the small-batch path (layout + dispatch in one
+    launch, then combine), and that path replayed from a captured HIP graph
+    of 10 steps.  Each figure is the mean GPU time per step over back-to-back
+    steps between two events."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    from combine_ep_get_dispatch_amd import workloads as W
+    from combine_ep_get_dispatch_amd.traffic import algorithmic_bytes
+
+    wl = W.config(cid)
+    bufs = M.EpBuffers(shape_of(M, W, wl), dev)
+    x, xs, idx, w = make_inputs(wl, dev)
+    eo = torch.zeros((wl.T * wl.k, wl.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    bufs.layout_dispatch_small(x, xs, idx, w)
+    R = int(bufs.expert_offsets[-1].item())
+    if bufs.status():
+        raise RuntimeError(f"device status on the decode path, config {cid}")
+
+    def four(stream):
+        bufs.layout(idx, stream)
+        bufs.dispatch_notify(idx, stream)
+        bufs.dispatch_scatter(x, xs, idx, w, stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+
+    def small(stream):
+        bufs.layout_dispatch_small(x, xs, idx, w, stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+
+    def per_step(fn):
+        stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            fn(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    res = dict(workload=wl.name, T=wl.T, R=R)
+    res["four_calls_us"] = per_step(four)
+    res["small_us"] = per_step(small)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        small(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    # a decode graph holds many steps; capture 10 so that the host's replay
+    # call is not what is timed
+    graph = torch.cuda.CUDAGraph()
+    per_graph = 10
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            small(torch.cuda.current_stream())
+    res["small_graph_us"] = per_step(lambda stream: graph.replay()) / per_graph
+    # the small-batch dispatch alone, events around each call
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        bufs.layout_dispatch_small(x, xs, idx, w, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    res["small_dispatch_us"] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    if bufs.status():
+        raise RuntimeError(f"device status after the decode steps, config {cid}")
+    x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
+    B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
+    res["step_bytes"] = B["step"]
+    res["tokens_per_s_graph"] = wl.T / (res["small_graph_us"] * 1e-6)
+    del graph, bufs, x, xs, idx, w, eo, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
     """Achievable HBM copy bandwidth (read + write bytes) with the library's
     plain 16-byte copy kernel."""
@@ -313,6 +394,7 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-quant", action="store_true", help="skip the quantise-on-dispatch timings")
     ap.add_argument("--no-groups", action="store_true", help="skip the group-deduplicated path timings")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-latency timings")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -353,6 +435,10 @@ def main():
     if not args.no_groups:
         log("[bench] group-deduplicated path")
         groups = run_gpu_groups(args.config, max(20, args.steps // 4), max(5, args.warmup // 4), dev)
+    decode = None
+    if not args.no_decode:
+        log("[bench] decode latency (config 4)")
+        decode = run_gpu_decode(4, max(50, args.steps), max(10, args.warmup), dev)
     probe = None if args.no_probe else probe_copy_gbps(dev)
     if probe:
         log(f"[bench] probe copy {probe:.0f} GB/s")
@@ -411,6 +497,7 @@ def main():
         "other_workloads": others,
         "quant_dispatch": quant,
         "group_path": groups,
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -43,6 +43,7 @@ DEV_BAD_HANDLE = 8
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch",
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
+           "ep_layout_dispatch_small",
            "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy")
 
 
@@ -95,6 +96,8 @@ def load(path: str = LIB_PATH):
     L.ep_dispatch_scatter_quant.argtypes = [S, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P, P,
                                             C.c_size_t, P]
     L.ep_dispatch_scatter_quant.restype = C.c_int
+    L.ep_layout_dispatch_small.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_layout_dispatch_small.restype = C.c_int
     L.ep_dispatch_groups.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch_groups.restype = C.c_int
     L.ep_group_permute.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
@@ -188,6 +191,15 @@ def ep_dispatch_scatter_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_w
         _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
+def ep_layout_dispatch_small(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, tokens_per_group,
+                             is_token_in_group, recv_x, recv_scales, recv_src_idx, recv_weights, expert_offsets,
+                             slot_to_row, ws, stream=None):
+    _check("ep_layout_dispatch_small", load().ep_layout_dispatch_small(
+        C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert),
+        _p(tokens_per_group), _p(is_token_in_group), _p(recv_x), _p(recv_scales), _p(recv_src_idx),
+        _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
 def ep_dispatch_groups(shape, x, x_scales, topk_idx, topk_weights, is_token_in_group, tokens_per_group, recv_x,
                        recv_scales, recv_src_idx, recv_topk_idx, recv_topk_weights, group_offsets, token_group_row, ws,
                        stream=None):
@@ -278,6 +290,12 @@ class EpBuffers:
         ep_dispatch_scatter(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,
                             self.recv_scales, self.recv_src_idx, self.recv_weights, self.expert_offsets,
                             self.slot_to_row, self.ws, stream)
+
+    def layout_dispatch_small(self, x, x_scales, topk_idx, topk_weights, stream=None):
+        ep_layout_dispatch_small(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert,
+                                 self.tokens_per_group, self.is_token_in_group, self.recv_x, self.recv_scales,
+                                 self.recv_src_idx, self.recv_weights, self.expert_offsets, self.slot_to_row, self.ws,
+                                 stream)
 
     def enable_quant(self, quant_block: int, scale_fmt: int):
         """Receive buffers of quantise-on-dispatch: E4M3 codes [T*k][H] and one

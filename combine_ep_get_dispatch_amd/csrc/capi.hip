@@ -38,6 +38,22 @@ static int check_shape(const moedisp_shape* s) {
 
 static int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Expert -> group index e / per_group on the device: a shift when per_group is
+// a power of two, else a multiply-high by floor(2^32 / per_group) + 1, which
+// is exact for e, per_group <= 4096 (the error term e * (per_group - 2^32 mod
+// per_group) / (per_group * 2^32) stays below 1 / per_group).
+static void group_index_constants(int per_group, int* shift, uint32_t* magic) {
+    const uint32_t pg = (uint32_t)per_group;
+    *shift = -1;
+    *magic = 0;
+    if ((pg & (pg - 1)) == 0) {
+        *shift = 0;
+        while ((1u << *shift) < pg) ++*shift;
+    } else {
+        *magic = (uint32_t)((1ull << 32) / pg + 1);
+    }
+}
+
 // Scatter plan for rows of `units` lane units whose k copies write
 // `write_per_token` bytes; column ranges are whole multiples of `align` units.
 static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_token, int units, int align) {
@@ -192,15 +208,7 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
     a.G = s->num_groups;
     a.id_bits = 0;
     while ((1 << a.id_bits) < a.E) ++a.id_bits;
-    const uint32_t per_group = (uint32_t)(a.E / a.G);
-    a.pg_shift = -1;
-    a.pg_magic = 0;
-    if ((per_group & (per_group - 1)) == 0) {
-        a.pg_shift = 0;
-        while ((1u << a.pg_shift) < per_group) ++a.pg_shift;
-    } else {
-        a.pg_magic = (uint32_t)((1ull << 32) / per_group + 1);
-    }
+    group_index_constants(a.E / a.G, &a.pg_shift, &a.pg_magic);
     a.topk_idx = topk_idx;
     a.tokens_per_expert = tokens_per_expert;
     a.tokens_per_group = tokens_per_group;
@@ -413,6 +421,71 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     a.out = out;
     a.hdr = (WsHeader*)ws;
     return hip_status(launch_combine(a, out_dtype == MOEDISP_FP32, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+// Small-batch path: layout + dispatch in one launch
+
+int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                             const float* topk_weights, int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                             uint32_t* is_token_in_group, void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                             float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row, void* ws,
+                             size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
+    const long long n = (long long)s->num_tokens * s->topk;
+    // the routing table, two per-expert arrays and the token masks live in
+    // LDS (<= 60 KiB)
+    if (n > kFusedMaxSlots || (n + 2LL * s->num_experts + s->num_tokens) * 4 > 60 * 1024)
+        return MOEDISP_ERR_UNSUPPORTED;
+    if (!tokens_per_expert || !tokens_per_group || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !is_token_in_group || !recv_x || !recv_src_idx ||
+                              !recv_weights || !slot_to_row))
+        return MOEDISP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && fp8 && (!x_scales || !recv_scales)) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(recv_x, 16)) return MOEDISP_ERR_MISALIGNED;
+    if (!aligned(x_scales, 4) || !aligned(recv_scales, 4) || !aligned(topk_idx, 4) || !aligned(topk_weights, 4) ||
+        !aligned(tokens_per_expert, 4) || !aligned(tokens_per_group, 4) || !aligned(is_token_in_group, 4) ||
+        !aligned(recv_src_idx, 4) || !aligned(recv_weights, 4) || !aligned(expert_offsets, 4) ||
+        !aligned(slot_to_row, 4))
+        return MOEDISP_ERR_MISALIGNED;
+    if ((st = check_ws(s, ws, ws_bytes))) return st;
+    FusedArgs a;
+    a.T = s->num_tokens;
+    a.k = s->topk;
+    a.E = s->num_experts;
+    a.G = s->num_groups;
+    a.experts_per_group = s->num_experts / s->num_groups;
+    group_index_constants(a.experts_per_group, &a.pg_shift, &a.pg_magic);
+    a.row16 = (int)(row_bytes(*s) / 16);
+    a.scale_words = fp8 ? scales_per_row(*s) : 0;
+    a.capacity = s->num_tokens * s->topk;
+    // column ranges: split rows while the grid is small, as for the scatter
+    int splits = 1;
+    while ((long long)s->num_tokens * splits < 1024 && a.row16 / (splits * 2) >= kThreads / 2) splits *= 2;
+    const int per = ceil_div(a.row16, splits);
+    a.split_units = per;
+    a.col_splits = ceil_div(a.row16, per);
+    int threads = (per + 63) / 64 * 64;
+    if (threads < kThreads) threads = kThreads;
+    if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
+    a.threads = threads;
+    a.x = (const v4u*)x;
+    a.x_scales = fp8 ? x_scales : nullptr;
+    a.topk_idx = topk_idx;
+    a.topk_weights = topk_weights;
+    a.tokens_per_expert = tokens_per_expert;
+    a.tokens_per_group = tokens_per_group;
+    a.is_token_in_group = is_token_in_group;
+    a.recv_x = (v4u*)recv_x;
+    a.recv_scales = fp8 ? recv_scales : nullptr;
+    a.recv_src_idx = recv_src_idx;
+    a.recv_weights = recv_weights;
+    a.expert_offsets = expert_offsets;
+    a.slot_to_row = slot_to_row;
+    a.hdr = (WsHeader*)ws;
+    return hip_status(launch_dispatch_fused(a, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------------------------

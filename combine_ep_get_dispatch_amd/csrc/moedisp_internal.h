@@ -150,7 +150,37 @@ struct CombineArgs {
     WsHeader* hdr;
 };
 
+// Small-batch path: layout and dispatch in one launch (every workgroup
+// stages the whole routing table, so T*k is bounded).
+constexpr int kFusedMaxSlots = 8192;
+
+struct FusedArgs {
+    int T, k, E, G;
+    int experts_per_group;
+    int pg_shift;       // log2(E/G) if E/G is a power of two, else -1
+    uint32_t pg_magic;  // floor(2^32 / (E/G)) + 1 otherwise (exact for ids < 4096)
+    int row16;
+    int scale_words;
+    int capacity;
+    int col_splits, split_units, threads;
+    const v4u* x;
+    const float* x_scales;
+    const int32_t* topk_idx;
+    const float* topk_weights;
+    int32_t* tokens_per_expert;
+    int32_t* tokens_per_group;
+    uint32_t* is_token_in_group;
+    v4u* recv_x;
+    float* recv_scales;
+    int32_t* recv_src_idx;
+    float* recv_weights;
+    int32_t* expert_offsets;
+    int32_t* slot_to_row;
+    WsHeader* hdr;
+};
+
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+hipError_t launch_dispatch_fused(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, hipStream_t stream);

@@ -147,6 +147,24 @@ int ep_dispatch_scatter(const moedisp_shape* shape, const void* x, const float* 
                         int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                         int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
 
+/* Small-batch (decode) path: ep_get_dispatch_layout and ep_dispatch in one
+ * kernel launch, with exactly their outputs (all of them, bit for bit).  The
+ * page's low-latency path is likewise a single kernel tuned for small
+ * batches.  Every workgroup recomputes the routing layout from the whole
+ * topk_idx in LDS, so no workgroup waits for another; this bounds the size:
+ * T*k <= 8192 and (T*k + 2*E + T) * 4 bytes <= 60 KiB, else
+ * MOEDISP_ERR_UNSUPPORTED (use the two calls).  Arguments as for the two calls;
+ * tokens_per_expert, tokens_per_group and is_token_in_group are outputs here.
+ * Status bits: BAD_EXPERT_ID, DUPLICATE_EXPERT.  With no host synchronisation
+ * and no allocation, the call (and ep_combine after it) can be captured in a
+ * HIP graph. */
+int ep_layout_dispatch_small(const moedisp_shape* shape, const void* x, const float* x_scales,
+                             const int32_t* topk_idx, const float* topk_weights, int32_t* tokens_per_expert,
+                             int32_t* tokens_per_group, uint32_t* is_token_in_group, void* recv_x,
+                             float* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                             int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes,
+                             void* stream);
+
 /* Dispatch with quantisation: as ep_dispatch for a bf16 x, but every
  * received row holds OCP E4M3 codes of the token's row plus one scale per
  * block of `quant_block` channels ("MSCCLPP EP implementation - #852": the

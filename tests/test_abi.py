@@ -184,6 +184,21 @@ def test_workspace_covers_group_rows(lib):
         assert M.ep_workspace_bytes(shape(T=T, E=E, G=G, k=k)) >= 256 + 64 * 4 * E
 
 
+def test_host_checks_layout_dispatch_small(lib):
+    def rc(sh, x=None, idx=None, tpe=None, ws_bytes=1 << 30):
+        return lib.ep_layout_dispatch_small(C.byref(sh), x or p(), None, idx or p(), p(), tpe or p(), p(), p(), p(),
+                                            None, p(), p(), p(), p(), p(), ws_bytes, None)
+    assert rc(shape(T=4096)) == B.ERR_UNSUPPORTED                  # 32768 slots: use the two calls
+    assert rc(shape(T=1025, k=8)) == B.ERR_UNSUPPORTED             # 8200 slots
+    assert rc(shape(T=1000, E=4096, G=8)) == B.ERR_UNSUPPORTED     # LDS: (8000 + 8192 + 1000) * 4 > 60 KiB
+    assert rc(shape(T=128), x=p(8)) == B.ERR_MISALIGNED
+    assert rc(shape(T=128), tpe=p(2)) == B.ERR_MISALIGNED
+    assert rc(shape(T=128), ws_bytes=64) == B.ERR_WORKSPACE_TOO_SMALL
+    assert rc(shape(T=128, dt=M.FP8_E4M3, sb=128)) == B.ERR_INVALID_ARG   # fp8 without scales
+    assert lib.ep_layout_dispatch_small(C.byref(shape(T=128)), p(), None, None, p(), p(), p(), p(), p(), None, p(),
+                                        p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+
+
 def test_host_checks_combine(lib):
     assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
     assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED

@@ -1,0 +1,145 @@
+"""GPU parity of the small-batch path ep_layout_dispatch_small (layout and
+dispatch in one launch) against the CPU oracle, and of the decode step
+(small-batch dispatch + combine) captured in a HIP graph (needs an MI355X).
+
+Bit-exact: every layout and dispatch output.  Combine: the usual bar.  The
+graph test replays a captured decode step several times, with eager work and
+new routing and activations copied into the captured inputs between
+replays, and checks every replay against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_get_dispatch_amd as M
+from combine_ep_get_dispatch_amd import workloads as W
+import gpu_harness as GH
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    M.load()
+    return torch.device("cuda:0")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_small(orc, wl, dev, bufs=None, inputs=None):
+    o = GH.oracle_run(orc, wl)
+    bufs = bufs or M.EpBuffers(GH.shape_of(wl), dev)
+    inputs = inputs or GH.GpuInputs(wl, dev)
+    bufs.layout_dispatch_small(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+    st = bufs.status()
+    assert st == (o["status"] | o["layout_status"]), f"device status {st} != oracle {o['status']}"
+    g, R = GH.fetch_dispatch(bufs, wl)
+    GH.assert_dispatch_equal(g, o, wl)
+    return o, bufs, inputs
+
+
+CASES = {
+    "decode_fp8": lambda: W.config(4),
+    "tiny": lambda: W.config(1),
+    "one_token": lambda: W.make_workload("t1", 1, 7168, 256, 8, 8, seed=80),
+    "ragged_zipf": lambda: W.make_workload("zipf77", 77, 7168, 256, 8, 8, seed=81, routing="zipf", mask_frac=0.1),
+    "k1": lambda: W.make_workload("k1", 200, 2048, 64, 8, 1, seed=82),
+    "e1024": lambda: W.make_workload("e1024", 128, 1024, 1024, 32, 8, seed=83),
+    "mixtral": lambda: W.make_workload("mixtral", 512, 4096, 8, 8, 2, seed=84),
+    "max_slots": lambda: W.make_workload("max_slots", 1024, 512, 256, 8, 8, seed=85),
+    "all_masked": lambda: W.make_workload("all_masked", 33, 256, 16, 4, 4, seed=86, mask_frac=1.0),
+    "empty": lambda: W.make_workload("empty", 0, 256, 16, 4, 4, seed=87),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layout_dispatch_small_parity(orc, dev, name):
+    wl = CASES[name]()
+    _say(f"[small] {name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k} {wl.x_dtype}")
+    o, bufs, _ = run_small(orc, wl, dev)
+    if wl.T:
+        eo_bits = GH.oracle_expert_out(wl, o)
+        eo = GH.upload_expert_out(eo_bits, wl.T * wl.k, wl.H, dev)
+        g32, g16, st = GH.gpu_combine(bufs, eo, wl, dev)
+        assert st == 0
+        o32, o16 = orc.combine(eo_bits, o["recv_weights"][:int(o["expert_offsets"][-1])], o["slot_to_row"])
+        GH.assert_combine_close(g32, g16, o32, o16)
+    _say(f"[small] {name} ok")
+
+
+def test_layout_dispatch_small_bad_and_repeated_ids(orc, dev):
+    wl = W.make_workload("bad_ids", 64, 256, 32, 4, 4, seed=88)
+    wl.topk_idx[3, 1] = 40          # out of range
+    wl.topk_idx[5, 2] = -3          # negative, not -1
+    wl.topk_idx[7, 3] = wl.topk_idx[7, 0]   # repeated expert
+    o, bufs, _ = run_small(orc, wl, dev)
+    assert o["status"] & 1 and o["layout_status"] & 2
+
+
+def test_small_matches_two_call_path(orc, dev):
+    """Same outputs as ep_get_dispatch_layout + ep_dispatch on the same buffers."""
+    wl = W.config(4)
+    inp = GH.GpuInputs(wl, dev)
+    a = M.EpBuffers(GH.shape_of(wl), dev)
+    b = M.EpBuffers(GH.shape_of(wl), dev)
+    a.layout(inp.topk_idx)
+    a.dispatch(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    b.layout_dispatch_small(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    assert a.status() == 0 and b.status() == 0
+    R = int(a.expert_offsets[-1].item())
+    for name in ("tokens_per_expert", "tokens_per_group", "is_token_in_group", "expert_offsets", "slot_to_row"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    for name in ("recv_x", "recv_scales", "recv_src_idx", "recv_weights"):
+        assert torch.equal(getattr(a, name)[:R], getattr(b, name)[:R]), name
+
+
+def test_decode_step_in_hip_graph(orc, dev):
+    """Capture small-batch dispatch + combine; replay with new inputs."""
+    base = W.config(4)
+    bufs = M.EpBuffers(GH.shape_of(base), dev)
+    inp = GH.GpuInputs(base, dev)
+    eo = torch.zeros((base.T * base.k, base.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((base.T, base.H), dtype=torch.bfloat16, device=dev)
+    # warm up on a side stream, then capture
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        bufs.layout_dispatch_small(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+        bufs.combine(eo, out, M.BF16, True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        bufs.layout_dispatch_small(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+        bufs.combine(eo, out, M.BF16, True)
+    for rep, seed in enumerate((90, 91, 92)):
+        wl = W.make_workload(f"graph{rep}", base.T, base.H, base.E, base.G, base.k, seed=seed, x_dtype=W.X_FP8,
+                             scale_block=128, routing="zipf" if rep == 1 else "uniform",
+                             mask_frac=0.05 if rep == 2 else 0.0, expert_kind="dequant_identity")
+        o = GH.oracle_run(orc, wl)
+        eo_bits = GH.oracle_expert_out(wl, o)
+        # new inputs into the captured tensors; eager work between replays
+        new = GH.GpuInputs(wl, dev)
+        inp.x.copy_(new.x)
+        inp.x_scales.copy_(new.x_scales)
+        inp.topk_idx.copy_(new.topk_idx)
+        inp.topk_weights.copy_(new.topk_weights)
+        eo.zero_()
+        R = eo_bits.shape[0]
+        # expert outputs are placed at the oracle's rows, which the graph's
+        # dispatch must reproduce for the combine to match
+        eo[:R] = GH.bits16_to_bf16_tensor(eo_bits).to(dev)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bufs.status() == 0
+        g, _ = GH.fetch_dispatch(bufs, wl)
+        GH.assert_dispatch_equal(g, o, wl)
+        o32, o16 = orc.combine(eo_bits, o["recv_weights"][:R], o["slot_to_row"])
+        g16 = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        d = GH.bf16_ulp_distance(g16, o16)
+        assert d.size == 0 or d.max() <= GH.COMBINE_ULP_TOL, f"replay {rep}: combine off by {int(d.max())} ulp"
+        _say(f"[graph] replay {rep} ok R={R}")
