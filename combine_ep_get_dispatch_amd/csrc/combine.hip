@@ -21,9 +21,9 @@
 // at accumulation, with BAD_HANDLE raised.  The token's routed slots are
 // compacted (slot order kept) and a switch on their count picks an unrolled
 // gather, so no masked slot costs a load.  Each lane owns U 16-byte units (8 bf16) of the output
-// row (U = 1 for k = 8: 896 lanes cover a 7168-wide row in one pass): it
-// issues all k*U gathered 16-byte loads before the first FMA, so each lane
-// keeps k*U loads in flight, then accumulates slot by slot in order.
+// row (U = 2: 448 lanes cover a 7168-wide row in one pass): it issues all
+// k*U gathered 16-byte loads before the first FMA, so each lane keeps k*U
+// loads in flight, then accumulates slot by slot in order.
 // With k known at compile time (1, 2, 4, 8) the slot loop is unrolled; other
 // k take the generic loop.
 #include "moedisp_internal.h"
@@ -90,8 +90,8 @@ __device__ inline int handle_row(const CombineArgs& a, int t, int j, float* w, u
 
 // Weighted sum over N compacted slots (rows crow[0..N), in slot order) for
 // this lane's columns.  All N*U row loads of a pass are issued back to back
-// (no per-slot branch); the first pass is issued before the weights and the
-// source check are fetched.  A slot whose row fails the source check is
+// (no per-slot branch), then the weights and source tokens as scalar loads
+// that are in flight with them.  A slot whose row fails the source check is
 // skipped at accumulation.
 template <int N, int U, bool kF32>
 __device__ inline void gather_sum(const CombineArgs& a, int t, int c0, int c1, const int* crow, uint32_t* err) {
@@ -104,23 +104,30 @@ __device__ inline void gather_sum(const CombineArgs& a, int t, int c0, int c1, c
 #pragma unroll
         for (int u = 0; u < U; ++u)
             v[p][u] = __builtin_nontemporal_load(a.expert_out + (size_t)crow[p] * a.row16 + min(c + u * nth, c1 - 1));
-    asm volatile("" ::: "memory");
+    // weights and source tokens: uniform scalar loads issued after the row
+    // loads (a scheduling barrier keeps that order), in flight with them
+    __builtin_amdgcn_sched_barrier(0);
     float w[N > 0 ? N : 1];
+    int src[N > 0 ? N : 1];
+    if (a.recv_weights) {
+#pragma unroll
+        for (int p = 0; p < N; ++p) w[p] = a.recv_weights[crow[p]];
+    } else {
+#pragma unroll
+        for (int p = 0; p < N; ++p) w[p] = 1.0f;
+    }
+    if (a.recv_src_idx) {
+#pragma unroll
+        for (int p = 0; p < N; ++p) src[p] = a.recv_src_idx[crow[p]];
+    } else {
+#pragma unroll
+        for (int p = 0; p < N; ++p) src[p] = t;
+    }
     bool ok[N > 0 ? N : 1];
 #pragma unroll
     for (int p = 0; p < N; ++p) {
-        w[p] = a.recv_weights ? a.recv_weights[crow[p]] : 1.0f;
-        ok[p] = true;
-    }
-    if (a.recv_src_idx) {
-        int src[N > 0 ? N : 1];
-#pragma unroll
-        for (int p = 0; p < N; ++p) src[p] = a.recv_src_idx[crow[p]];
-#pragma unroll
-        for (int p = 0; p < N; ++p) {
-            ok[p] = src[p] == t;
-            *err |= ok[p] ? 0u : MOEDISP_DEV_BAD_HANDLE;
-        }
+        ok[p] = src[p] == t;
+        *err |= ok[p] ? 0u : MOEDISP_DEV_BAD_HANDLE;
     }
     while (c < c1) {
         float acc[U][8];
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
-    constexpr int U = (KC == 1 || KC == 2 || KC == 4) ? 2 : 1;  // = combine_units_per_lane(k)
+    constexpr int U = 2;  // = combine_units_per_lane(k)
     hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(a.threads), 0, stream, a);
     return hipGetLastError();
 }

@@ -62,9 +62,8 @@ struct CombinePlan {
 };
 
 constexpr int kMaxCombineThreads = 1024;
-// 16-byte units each combine lane owns per pass (k loads in flight per unit);
-// k = 1, 2, 4 have unrolled kernels with 2 units, every other k uses 1
-inline int combine_units_per_lane(int k) { return (k == 1 || k == 2 || k == 4) ? 2 : 1; }
+// 16-byte units each combine lane owns per pass (k loads in flight per unit)
+inline int combine_units_per_lane(int) { return 2; }
 
 struct WsPlan {
     int layout_blocks;
