@@ -147,7 +147,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsPlan plan_workspace(const moedisp_shape& s) {
     WsPlan w;
-    w.layout_blocks = s.num_tokens > 0 ? ceil_div(s.num_tokens, kLayoutTokensPerBlock) : 1;
+    w.layout_blocks = s.num_tokens > 0 ? ceil_div(s.num_tokens, layout_tokens_per_block(s)) : 1;
     w.partial_offset = sizeof(WsHeader);
     const size_t partial_bytes = (size_t)w.layout_blocks * (s.num_experts + s.num_groups) * sizeof(int32_t);
     w.counts_offset = align256(w.partial_offset + partial_bytes);
@@ -209,6 +209,8 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
     a.id_bits = 0;
     while ((1 << a.id_bits) < a.E) ++a.id_bits;
     group_index_constants(a.E / a.G, &a.pg_shift, &a.pg_magic);
+    group_index_constants(a.k, &a.k_shift, &a.k_magic);
+    a.tokens_per_block = layout_tokens_per_block(*s);
     a.topk_idx = topk_idx;
     a.tokens_per_expert = tokens_per_expert;
     a.tokens_per_group = tokens_per_group;

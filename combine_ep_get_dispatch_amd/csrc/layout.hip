@@ -2,16 +2,24 @@
 // bitmap ("counts + token-in-rank" of the high-throughput layout kernel on the
 // "MSCCLPP EP implementation - #852" page, review file table).
 //
-// One thread per token, 256 tokens per workgroup.  The workgroup's routing
-// rows are staged in LDS (padded to an odd stride so a wave reading one slot
-// of 64 tokens hits distinct banks).  Expert counts go to an LDS-private
-// histogram: for each slot, the lanes of a wave that carry the same expert
-// find each other with one ballot per bit of the expert id, and only the
-// lowest such lane adds the popcount of its peer mask - one LDS atomic per
-// distinct expert per wave instead of one per lane, which matters under skewed
-// routing.  Group counts are popcounts of one ballot per group.  Each
-// workgroup writes its partial counts to the workspace; the last workgroup to
-// finish sums them in workgroup order and resets the finish counter.
+// One lane per routing slot: a workgroup of kLayoutThreads lanes covers
+// kLayoutThreads / k whole tokens, so at T = 4096, k = 8 the grid has 32
+// workgroups of 16 waves and every wave handles the 64 slots of 8 tokens at
+// once.  Each lane loads its slot's expert id (coalesced) and:
+//   - expert counts: the lanes of a wave with the same expert find each other
+//     with one ballot per bit of the expert id, and only the lowest such lane
+//     adds the popcount of its peer mask to an LDS-private histogram - one LDS
+//     atomic per distinct expert per wave;
+//   - token masks: an LDS atomicOr of the slot's group bit into its token's
+//     word; repeated experts: a comparison with the token's earlier slots
+//     (LDS copy of the ids, 8 reads in flight);
+// then each token's mask is the bitmap word and group counts are popcounts of
+// one ballot per group.  Each workgroup writes its partial counts to the
+// workspace, and a second, one-workgroup kernel sums them in workgroup order:
+// the kernel boundary is the only synchronisation.  (A last-workgroup finish
+// inside one kernel needs a device-scope fence and a same-address atomic per
+// workgroup; measured on this part, those serialise across the XCDs and cost
+// more than the second launch.)
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -33,106 +41,89 @@ __device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active)
     return peers;
 }
 
-// Group of expert id: id / (E/G) by a shift (power-of-two group sizes) or by
-// a multiply-high with a host-computed reciprocal (exact for id, E <= 4096).
-__device__ inline uint32_t group_of(uint32_t id, const LayoutArgs& a) {
-    return a.pg_shift >= 0 ? id >> a.pg_shift : __umulhi(id, a.pg_magic);
+// x / d for a host-computed (shift, magic) pair: a shift when d is a power of
+// two, else a multiply-high (exact for the ranges the host checks).
+__device__ inline uint32_t div_const(uint32_t x, int shift, uint32_t magic) {
+    return shift >= 0 ? x >> shift : __umulhi(x, magic);
 }
 
-// KMAX: compile-time bound on k; a token's routing row lives in registers.
-template <int KMAX>
-__global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
-    extern __shared__ int32_t dyn[];  // [E + G] counts, then the staged routing rows
+__global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
+    extern __shared__ int32_t dyn[];  // counts [E + G], ids [tokens * k], token masks [tokens]
     const int EG = a.E + a.G;
+    const int k = a.k;
+    const int tpb = a.tokens_per_block;
     int32_t* s_cnt = dyn;
     int32_t* s_ids = dyn + EG;
+    uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_ids + tpb * k);
     __shared__ uint32_t s_err;
-    __shared__ uint32_t s_last;
 
     const int tid = threadIdx.x;
+    const int nth = blockDim.x;
     const int lane = tid & 63;
-    const int k = a.k;
-    const int kp = k | 1;  // odd LDS stride
-    const int t0 = blockIdx.x * kLayoutTokensPerBlock;
-    const int nt = max(0, min(kLayoutTokensPerBlock, a.T - t0));
+    const int t0 = blockIdx.x * tpb;
+    const int nt = max(0, min(tpb, a.T - t0));
+    const int ns = nt * k;
 
-    for (int i = tid; i < EG; i += kThreads) s_cnt[i] = 0;
-    if (tid == 0) s_err = 0;
-    // stage the routing rows: 8 independent coalesced loads in flight per lane
-    constexpr int kStage = 8;
-    const int n = nt * k;
-    for (int i0 = 0; i0 < n; i0 += kStage * kThreads) {
-        int32_t v[kStage];
-#pragma unroll
-        for (int q = 0; q < kStage; ++q) {
-            const int i = i0 + q * kThreads + tid;
-            v[q] = i < n ? a.topk_idx[(size_t)t0 * k + i] : 0;
-        }
-#pragma unroll
-        for (int q = 0; q < kStage; ++q) {
-            const int i = i0 + q * kThreads + tid;
-            if (i < n) {
-                const int tt = i / k;
-                s_ids[tt * kp + (i - tt * k)] = v[q];
-            }
-        }
-    }
-    __syncthreads();
-
-    const bool have = tid < nt;
-    const uint64_t below = (1ull << lane) - 1ull;
-    uint32_t gmask = 0;
+    // this lane's slot (coalesced), validated
     uint32_t err = 0;
-    int ids[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        int id = (have && j < k) ? s_ids[tid * kp + j] : -1;
+    int id = -1;
+    if (tid < ns) {
+        id = a.topk_idx[(size_t)t0 * k + tid];
         if (id < -1 || id >= a.E) {
             err |= MOEDISP_DEV_BAD_EXPERT_ID;
             id = -1;
         }
-        ids[j] = id;
     }
+    for (int i = tid; i < EG; i += nth) s_cnt[i] = 0;
+    for (int i = tid; i < nt; i += nth) s_mask[i] = 0;
+    if (tid < ns) s_ids[tid] = id;
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+
+    // expert counts: one ballot-match round per wave
+    const bool routed = id >= 0;
+    const uint64_t below = (1ull << lane) - 1ull;
+    const uint64_t active = __ballot(routed);
+    const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
+    if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+    // token masks and repeated experts
+    if (routed) {
+        const int tl = (int)div_const((uint32_t)tid, a.k_shift, a.k_magic);
+        const int base = tl * k;
+        atomicOr(&s_mask[tl], 1u << div_const((uint32_t)id, a.pg_shift, a.pg_magic));
+        for (int u0 = base; u0 < tid; u0 += 8) {  // 8 clamped reads per step, no branch
+            int v[8];
 #pragma unroll
-    for (int j = 1; j < KMAX; ++j)
+            for (int m = 0; m < 8; ++m) v[m] = s_ids[min(u0 + m, tid - 1)];
 #pragma unroll
-        for (int jj = 0; jj < j; ++jj)
-            if (ids[j] >= 0 && ids[j] == ids[jj]) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {  // k is uniform
-            const int id = ids[j];
-            const bool routed = id >= 0;
-            if (routed) gmask |= 1u << group_of((uint32_t)id, a);
-            const uint64_t active = __ballot(routed);
-            const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
-            if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+            for (int m = 0; m < 8; ++m)
+                if (u0 + m < tid && v[m] == id) err |= MOEDISP_DEV_DUPLICATE_EXPERT;
         }
     }
+    __syncthreads();
+
+    // bitmap and group counts (one ballot per group and wave)
+    const uint32_t mask = tid < nt ? s_mask[tid] : 0u;  // nt <= tpb <= threads
+    if (tid < nt) a.is_token_in_group[t0 + tid] = mask;
     for (int g = 0; g < a.G; ++g) {
-        const uint64_t in_g = __ballot((gmask >> g) & 1u);
+        const uint64_t in_g = __ballot((mask >> g) & 1u);
         if (lane == 0 && in_g) atomicAdd(&s_cnt[a.E + g], (int32_t)__popcll(in_g));
     }
-    if (have) a.is_token_in_group[t0 + tid] = gmask;
     if (err) atomicOr(&s_err, err);
     __syncthreads();
 
     int32_t* mine = a.partials + (size_t)blockIdx.x * EG;
-    for (int i = tid; i < EG; i += kThreads) mine[i] = s_cnt[i];
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        if (s_err) atomicOr(&a.hdr->status, s_err);
-        const uint32_t prev = atomicAdd(&a.hdr->layout_done, 1u);
-        s_last = prev == (uint32_t)(a.blocks - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
+    for (int i = tid; i < EG; i += nth) mine[i] = s_cnt[i];
+    if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
+}
 
-    __threadfence();
-    // sum the partials in workgroup order, 16 independent loads in flight
-    constexpr int kBatch = 16;
-    for (int i = tid; i < EG; i += kThreads) {
+// Sum of the partial counts in workgroup order (one workgroup; the kernel
+// boundary orders it after every partial), 32 independent loads in flight:
+// one round trip for up to 32 partial rows.
+__global__ __launch_bounds__(kThreads) void moedisp_layout_reduce(LayoutArgs a) {
+    const int EG = a.E + a.G;
+    constexpr int kBatch = 32;
+    for (int i = threadIdx.x; i < EG; i += kThreads) {
         int32_t sum = 0;
         for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
             int32_t v[kBatch];
@@ -147,19 +138,16 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout(LayoutArgs a) {
         else
             a.tokens_per_group[i - a.E] = sum;
     }
-    if (tid == 0) __hip_atomic_store(&a.hdr->layout_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const size_t lds = (size_t)(a.E + a.G + kLayoutTokensPerBlock * (a.k | 1)) * sizeof(int32_t);
-    if (a.k <= 8)
-        hipLaunchKernelGGL((moedisp_layout<8>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
-    else if (a.k <= 16)
-        hipLaunchKernelGGL((moedisp_layout<16>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL((moedisp_layout<kMaxTopk>), dim3(a.blocks), dim3(kThreads), lds, stream, a);
+    const size_t lds = ((size_t)a.E + a.G + (size_t)a.tokens_per_block * (a.k + 1)) * sizeof(int32_t);
+    hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kLayoutThreads), lds, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

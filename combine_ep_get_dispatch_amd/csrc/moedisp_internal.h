@@ -14,7 +14,7 @@ namespace moedisp {
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;              // threads per workgroup (4 wave64s)
-constexpr int kLayoutTokensPerBlock = 256; // layout: one token per thread
+constexpr int kLayoutThreads = 1024;       // layout: one lane per slot, kLayoutThreads / k tokens per workgroup
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGroups = 32;
@@ -26,7 +26,7 @@ constexpr int kMaxBlockSlots = 512;        // >= kMaxBlockTokens * kMaxTopk
 // First 256 bytes of the workspace.
 struct WsHeader {
     uint32_t status;           // MOEDISP_DEV_* bits, or-ed by kernels
-    uint32_t layout_done;      // layout workgroups finished (the last one reduces)
+    uint32_t reserved0;        // unused (kept zero)
     uint32_t reserved[62];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
@@ -78,6 +78,7 @@ DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
 moedisp_shape group_rows_shape(const moedisp_shape& s);
 CombinePlan plan_combine(const moedisp_shape& s);
 WsPlan plan_workspace(const moedisp_shape& s);
+inline int layout_tokens_per_block(const moedisp_shape& s) { return kLayoutThreads / s.topk; }
 
 inline size_t row_bytes(const moedisp_shape& s) {
     return (size_t)s.hidden * (s.x_dtype == MOEDISP_FP8_E4M3 ? 1 : 2);
@@ -91,6 +92,9 @@ struct LayoutArgs {
     int id_bits;        // bits of an expert id (ceil(log2 E))
     int pg_shift;       // log2(E/G) if E/G is a power of two, else -1
     uint32_t pg_magic;  // floor(2^32 / (E/G)) + 1 otherwise
+    int k_shift;        // lane / k the same way
+    uint32_t k_magic;
+    int tokens_per_block;  // kLayoutThreads / k
     const int32_t* topk_idx;
     int32_t* tokens_per_expert;
     int32_t* tokens_per_group;

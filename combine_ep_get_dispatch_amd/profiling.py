@@ -24,7 +24,7 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
-KERNELS = ("moedisp_layout", "moedisp_count", "moedisp_scatter", "moedisp_scatter_quant", "moedisp_combine",
+KERNELS = ("moedisp_layout", "moedisp_layout_reduce", "moedisp_count", "moedisp_scatter", "moedisp_scatter_quant", "moedisp_combine",
            "moedisp_probe_copy")
 _NAME = re.compile(r"\b(moedisp_\w+?)(<[^>(]*>)?\(")
 
