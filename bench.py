@@ -7,14 +7,21 @@ batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168 bf16,
 E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
 stand-in expert outputs are resident in HBM before the timed region; the
 timed region is exactly K steps between two device synchronisations.  HIP
-events on the launch stream between the calls time each kernel (every call
-is one kernel) inside that region; the dominant kernel's algorithmic bytes
-over its mean duration give the roofline entry, with the HBM bytes measured
-by rocprofv3 counters (profiles/hbm_traffic.json) when they were taken on the
-current kernel sources.  The CPU oracle, timed on a bounded sample of the
-same workload on the host, is the reported baseline.
+events on the launch stream between the calls time each call inside that
+region (the layout is two kernels, every other call one); the dominant
+kernel's algorithmic bytes over its mean duration give the roofline entry,
+with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
+when they were taken on the current kernel sources.  The CPU oracle, timed on
+a bounded sample of the same workload on the host, is the reported baseline.
 
-Prints one JSON line.  `--gpus` above 1 is refused: this build runs one GPU.
+Further legs, reported beside the headline (each can be skipped): the other
+workloads (skewed routing, fp8 decode, Mixtral shape), quantise-on-dispatch
+(FP32 and UE8M0 block scales), the group-deduplicated path, decode-step
+latency (four calls, the small-batch path, and that path from a HIP graph),
+and a plain-copy bandwidth probe.
+
+Prints one JSON line.  `--gpus` above 1 is refused: the library runs one
+GPU's share of the path on one GPU.
 """
 from __future__ import annotations
 
@@ -399,7 +406,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share of the path on one GPU; --gpus {args.gpus} is not supported "
-              "(there is no multi-GPU path in this build).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch
