@@ -110,6 +110,15 @@ static moedisp_shape group_shape(const moedisp_shape& s) {
 
 DispatchPlan plan_dispatch_groups(const moedisp_shape& s) { return plan_dispatch(group_shape(s)); }
 
+// The local permutation of group rows: a group row routes about k / (groups
+// per token) of its k slots, at least k / min(G, k); size workgroups by that.
+static DispatchPlan plan_group_permute(const moedisp_shape& s) {
+    const moedisp_shape rs = group_rows_shape(s);
+    const int per_row = (s.topk + (s.num_groups < s.topk ? s.num_groups : s.topk) - 1) /
+                        (s.num_groups < s.topk ? s.num_groups : s.topk);
+    return plan_scatter(rs, (long long)per_row * (long long)row_bytes(rs), (int)(row_bytes(rs) / 16), 1);
+}
+
 // The group rows seen as tokens (T * min(G, k) of them, the capacity of the
 // group dispatch), for the local expert permutation and reduce.
 moedisp_shape group_rows_shape(const moedisp_shape& s) {
@@ -561,6 +570,7 @@ int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* g
                        recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a, s);
     if (st) return st;
     a.capacity = s->num_tokens * s->topk;  // the receive buffers hold T*k rows
+    a.plan = plan_group_permute(*s);       // same tiles as plan_dispatch(rs), more rows per workgroup
     if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
 }

@@ -292,6 +292,28 @@ __device__ inline void publish_err(const DispatchArgs& a, ScatterSmem& sm, uint3
     if (threadIdx.x == 0 && sm.err) atomicOr(&a.hdr->status, sm.err);
 }
 
+// Stores this lane's U units (columns c, c + nth, ...) to every routed row of
+// one token; the destination rows are read from LDS 8 at a time.
+template <int U>
+__device__ inline void store_units(const DispatchArgs& a, const int32_t* rows, const v4u* v, int c, int c1, int nth) {
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+        int rr[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rr[q] = rows[j0 + q];
+        asm volatile("" ::: "memory");  // all 8 reads before the stores
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (j0 + q >= a.k || rr[q] < 0) continue;
+            v4u* dst = a.recv_x + (size_t)rr[q] * a.row16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int cc = c + u * nth;
+                if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
+            }
+        }
+    }
+}
+
 // U: 16-byte units per lane per pass.
 template <int U>
 __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchArgs a) {
@@ -344,37 +366,41 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
     }
 
     // row scatter: each 16-byte unit is loaded once and stored k times
-    for (int tt = 0; tt < b.blk_nt; ++tt) {
-        const v4u* src = a.x + (size_t)(b.blk_t0 + tt) * a.row16;
-        const int32_t* rows = sm.rows + tt * k;
-        for (int c = c0 + tid; c < c1; c += U * nth) {
-            v4u v[U];
-            if (tt == 0 && c == c0 + tid) {
+    if (c1 - c0 <= U * nth) {
+        // the column range is one pass: the next token's units are loaded
+        // while this token's are stored
+        const int c = c0 + tid;
+        v4u cur[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = pre[u];
-            } else {
+        for (int u = 0; u < U; ++u) cur[u] = pre[u];
+        for (int tt = 0; tt < b.blk_nt; ++tt) {
+            v4u nxt[U];
+            if (tt + 1 < b.blk_nt) {
+                const v4u* src = a.x + (size_t)(b.blk_t0 + tt + 1) * a.row16;
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int cc = c + u * nth;
-                    if (cc < c1) v[u] = src[cc];
-                }
+                for (int u = 0; u < U; ++u)
+                    if (c + u * nth < c1) nxt[u] = src[c + u * nth];
             }
-            // destination rows 8 at a time from LDS, then the stores
-            for (int j0 = 0; j0 < k; j0 += 8) {
-                int rr[8];
+            store_units<U>(a, sm.rows + tt * k, cur, c, c1, nth);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) rr[q] = rows[j0 + q];
-                asm volatile("" ::: "memory");  // all 8 reads before the stores
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+    } else {
+        for (int tt = 0; tt < b.blk_nt; ++tt) {
+            const v4u* src = a.x + (size_t)(b.blk_t0 + tt) * a.row16;
+            for (int c = c0 + tid; c < c1; c += U * nth) {
+                v4u v[U];
+                if (tt == 0 && c == c0 + tid) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (j0 + q >= k || rr[q] < 0) continue;
-                    v4u* dst = a.recv_x + (size_t)rr[q] * a.row16;
+                    for (int u = 0; u < U; ++u) v[u] = pre[u];
+                } else {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int cc = c + u * nth;
-                        if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
+                        if (cc < c1) v[u] = src[cc];
                     }
                 }
+                store_units<U>(a, sm.rows + tt * k, v, c, c1, nth);
             }
         }
     }
