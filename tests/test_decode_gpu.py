@@ -143,3 +143,54 @@ def test_decode_step_in_hip_graph(orc, dev):
         d = GH.bf16_ulp_distance(g16, o16)
         assert d.size == 0 or d.max() <= GH.COMBINE_ULP_TOL, f"replay {rep}: combine off by {int(d.max())} ulp"
         _say(f"[graph] replay {rep} ok R={R}")
+
+
+def test_prefill_step_in_hip_graph(orc, dev):
+    """Capture layout + dispatch (two phases) + combine at a ragged mid size;
+    replay with new routing and activations, every replay against the oracle."""
+    base = W.make_workload("graph_prefill", 601, 2048, 64, 8, 8, seed=95)
+    bufs = M.EpBuffers(GH.shape_of(base), dev)
+    inp = GH.GpuInputs(base, dev)
+    eo = torch.zeros((base.T * base.k, base.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((base.T, base.H), dtype=torch.float32, device=dev)
+
+    def step():
+        bufs.layout(inp.topk_idx)
+        bufs.dispatch_notify(inp.topk_idx)
+        bufs.dispatch_scatter(inp.x, None, inp.topk_idx, inp.topk_weights)
+        bufs.combine(eo, out, M.FP32, True)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep, seed in enumerate((96, 97)):
+        wl = W.make_workload(f"graph_prefill{rep}", base.T, base.H, base.E, base.G, base.k, seed=seed,
+                             routing="zipf" if rep else "uniform", mask_frac=0.05 * rep, expert_kind="scale_by_id")
+        o = GH.oracle_run(orc, wl)
+        eo_bits = GH.oracle_expert_out(wl, o)
+        new = GH.GpuInputs(wl, dev)
+        inp.x.copy_(new.x)
+        inp.topk_idx.copy_(new.topk_idx)
+        inp.topk_weights.copy_(new.topk_weights)
+        eo.zero_()
+        R = eo_bits.shape[0]
+        eo[:R] = GH.bits16_to_bf16_tensor(eo_bits).to(dev)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bufs.status() == 0
+        g, _ = GH.fetch_dispatch(bufs, wl)
+        GH.assert_dispatch_equal(g, o, wl)
+        o32, _ = orc.combine(eo_bits, o["recv_weights"][:R], o["slot_to_row"], want_bf16=False)
+        g32 = out.cpu().numpy()
+        nz = o32 != 0
+        rel = np.abs(g32[nz].astype(np.float64) - o32[nz]) / np.abs(o32[nz])
+        assert rel.size == 0 or rel.max() <= GH.COMBINE_REL_TOL
+        assert np.all(g32[~nz] == 0.0)
+        _say(f"[graph-prefill] replay {rep} ok R={R}")
