@@ -89,8 +89,9 @@ typedef struct {
 #define MOEDISP_DEV_BAD_HANDLE 8u        /* combine handle inconsistent; those slots skipped */
 
 /* Bytes of workspace the calls need for `shape`; 0 if the shape is invalid.
- * One workspace serves layout, dispatch and combine of that shape (or of any
- * shape with no more tokens and experts). */
+ * One workspace serves every call of that shape, and of any other shape whose
+ * ep_workspace_bytes is not larger (calls check this and return
+ * MOEDISP_ERR_WORKSPACE_TOO_SMALL otherwise). */
 size_t ep_workspace_bytes(const moedisp_shape* shape);
 
 /* Zero a workspace before its first use.  The calls keep its counters
