@@ -31,7 +31,9 @@
 // The scatter then streams: each lane loads U 16-byte units of the source row
 // (U = 1 by default, up to 1024 lanes per workgroup) once - the first pass is
 // issued before the row computation - and stores them,
-// non-temporally, to each of the token's k destination rows.  Workgroups of
+// non-temporally, to each of the token's k destination rows (a token with no
+// receive row, such as a padding group row, is neither loaded past the first
+// pass nor stored).  Workgroups of
 // column range 0 write the handle (slot_to_row, recv_src_idx, recv_weights)
 // and fp8 scales.  Rows outside their expert's segment (or the buffer) are not
 // written and raise BAD_LAYOUT; workgroup 0 also checks that the routed slots
@@ -136,6 +138,7 @@ struct ScatterSmem {
     int32_t len[kMaxBlockSlots];   // tokens_per_expert[e]
     int32_t rows[kMaxBlockSlots + 8];  // receive row of each slot of the workgroup, -1 if none
                                        // (8 spare entries: the stores read rows 8 at a time)
+    int32_t routed_tok[kMaxBlockTokens];  // nonzero if the token has a receive row
     int32_t routed;
     uint32_t err;
 };
@@ -171,6 +174,7 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
     uint32_t ignored = 0;  // bad ids are reported by the count kernel
     for (int i = tid; i < b.first + b.blk_slots; i += nth) s_ids[i] = slot_id(a, (size_t)b.tile_t0 * k + i, &ignored);
     for (int q = tid; q < b.blk_slots; q += nth) sm.pre[q] = 0;
+    if (tid < kMaxBlockTokens) sm.routed_tok[tid] = 0;
     if (tid == 0) {
         sm.routed = 0;
         sm.err = 0;
@@ -226,6 +230,7 @@ __device__ uint32_t scatter_rows(const DispatchArgs& a, const ScatterBlock& b, i
                 row = (int)r;
         }
         sm.rows[q] = row;
+        if (row >= 0) sm.routed_tok[q / k] = 1;
     }
     __syncthreads();
     return err;
@@ -375,18 +380,19 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
         for (int u = 0; u < U; ++u) cur[u] = pre[u];
         for (int tt = 0; tt < b.blk_nt; ++tt) {
             v4u nxt[U];
-            if (tt + 1 < b.blk_nt) {
+            if (tt + 1 < b.blk_nt && sm.routed_tok[tt + 1]) {
                 const v4u* src = a.x + (size_t)(b.blk_t0 + tt + 1) * a.row16;
 #pragma unroll
                 for (int u = 0; u < U; ++u)
                     if (c + u * nth < c1) nxt[u] = src[c + u * nth];
             }
-            store_units<U>(a, sm.rows + tt * k, cur, c, c1, nth);
+            if (sm.routed_tok[tt]) store_units<U>(a, sm.rows + tt * k, cur, c, c1, nth);
 #pragma unroll
             for (int u = 0; u < U; ++u) cur[u] = nxt[u];
         }
     } else {
         for (int tt = 0; tt < b.blk_nt; ++tt) {
+            if (!sm.routed_tok[tt]) continue;
             const v4u* src = a.x + (size_t)(b.blk_t0 + tt) * a.row16;
             for (int c = c0 + tid; c < c1; c += U * nth) {
                 v4u v[U];
