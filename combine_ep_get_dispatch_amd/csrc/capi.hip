@@ -134,17 +134,26 @@ DispatchPlan plan_dispatch_quant(const moedisp_shape& s) {
     return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64);
 }
 
-CombinePlan plan_combine(const moedisp_shape& s) {
+CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {
     CombinePlan p;
     const int row16 = (int)((size_t)s.hidden * 2 / 16);
-    int splits = 1;
-    while ((long long)s.num_tokens * splits < 1024 && row16 / (splits * 2) >= kThreads) splits *= 2;
+    // Each (row, column range) is a workgroup.  Where a row gathers 8 or more
+    // rows, one unit per lane (that many loads in flight per lane) and about
+    // 64 lanes; where it gathers 2 to 7, one unit and 128 lanes.  Many short
+    // workgroups keep loads of other rows issuing while some sum and store;
+    // at H = 7168 and k = 8 a row is 14 ranges of 64 units.  Where a row
+    // gathers about one (a group row of the local reduce), 2 units per lane
+    // over the whole row, so that each lane still has several loads in
+    // flight and the workgroup's fixed cost (handle loads, launch) is paid
+    // once per row.
+    const int per_lane = loads_per_row >= 2 ? 1 : 2;
+    const int target = loads_per_row >= 8 ? 64 : loads_per_row >= 2 ? 128 : kMaxCombineThreads * per_lane;
+    int splits = (row16 + target - 1) / target;
+    if (splits < 1) splits = 1;
     p.col_splits = splits;
     p.blocks = s.num_tokens * splits;
-    // lanes per workgroup: whole waves, enough for one pass of `units_per_lane`
-    // 16-byte units per lane over the workgroup's column range
     const int units = (row16 + splits - 1) / splits;
-    const int per_lane = combine_units_per_lane(s.topk);
+    p.units_per_lane = per_lane;
     int threads = ((units + per_lane - 1) / per_lane + 63) / 64 * 64;
     if (threads > kMaxCombineThreads) threads = kMaxCombineThreads;
     if (threads < 64) threads = 64;
@@ -416,7 +425,7 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
         return MOEDISP_ERR_MISALIGNED;
     if ((st = check_ws(s, ws, ws_bytes))) return st;
     if (s->num_tokens == 0) return MOEDISP_OK;
-    const CombinePlan p = plan_combine(*s);
+    const CombinePlan p = plan_combine(*s, s->topk);
     CombineArgs a;
     a.T = s->num_tokens;
     a.k = s->topk;
@@ -424,6 +433,7 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     a.capacity = s->num_tokens * s->topk;
     a.col_splits = p.col_splits;
     a.threads = p.threads;
+    a.units_per_lane = p.units_per_lane;
     a.expert_out = (const v4u*)expert_out;
     a.recv_src_idx = recv_src_idx;
     a.recv_weights = recv_weights;
@@ -576,7 +586,7 @@ int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* g
 }
 
 // The combine kernel over `rows` output rows of `k` slots each.
-static int combine_call(const moedisp_shape* s, int rows, int k, int capacity, const void* in,
+static int combine_call(const moedisp_shape* s, int rows, int k, int loads_per_row, int capacity, const void* in,
                         const int32_t* src_check, const float* weights, const int32_t* slot_to_row,
                         const int32_t* row_limit, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
                         void* stream) {
@@ -593,7 +603,7 @@ static int combine_call(const moedisp_shape* s, int rows, int k, int capacity, c
     moedisp_shape cs = *s;
     cs.num_tokens = rows;
     cs.topk = k;
-    const CombinePlan p = plan_combine(cs);
+    const CombinePlan p = plan_combine(cs, loads_per_row);
     CombineArgs a;
     a.T = rows;
     a.k = k;
@@ -601,6 +611,7 @@ static int combine_call(const moedisp_shape* s, int rows, int k, int capacity, c
     a.capacity = capacity;
     a.col_splits = p.col_splits;
     a.threads = p.threads;
+    a.units_per_lane = p.units_per_lane;
     a.expert_out = (const v4u*)in;
     a.recv_src_idx = src_check;
     a.recv_weights = weights;
@@ -617,7 +628,11 @@ int ep_group_reduce(const moedisp_shape* s, const void* expert_out, const int32_
     if (!s) return MOEDISP_ERR_INVALID_ARG;
     if (s->num_tokens > 0 && (!recv_weights || !group_offsets)) return MOEDISP_ERR_INVALID_ARG;
     const int rows = check_shape(s) == MOEDISP_OK ? group_rows_shape(*s).num_tokens : 0;
-    return combine_call(s, rows, s->topk, s->num_tokens * s->topk, expert_out, recv_src_idx, recv_weights,
+    // a group row routes about k / min(G, k) of its k slots (the shape is
+    // checked by combine_call)
+    const int m = s->num_groups < s->topk ? s->num_groups : s->topk;
+    const int per_row = m > 0 ? (s->topk + m - 1) / m : 1;
+    return combine_call(s, rows, s->topk, per_row, s->num_tokens * s->topk, expert_out, recv_src_idx, recv_weights,
                         slot_to_row, group_offsets ? group_offsets + s->num_groups : nullptr, group_out, out_dtype,
                         ws, ws_bytes, stream);
 }
@@ -627,8 +642,8 @@ int ep_combine_groups(const moedisp_shape* s, const void* group_rows, const int3
                       void* stream) {
     if (!s) return MOEDISP_ERR_INVALID_ARG;
     const int cap = check_shape(s) == MOEDISP_OK ? group_rows_shape(*s).num_tokens : 0;
-    return combine_call(s, s->num_tokens, s->num_groups, cap, group_rows, recv_src_idx, nullptr, token_group_row,
-                        nullptr, out, out_dtype, ws, ws_bytes, stream);
+    return combine_call(s, s->num_tokens, s->num_groups, s->num_groups, cap, group_rows, recv_src_idx, nullptr,
+                        token_group_row, nullptr, out, out_dtype, ws, ws_bytes, stream);
 }
 
 int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_status) {

@@ -20,10 +20,12 @@
 // recv_src_idx is given, naming this token) and a slot that fails is skipped
 // at accumulation, with BAD_HANDLE raised.  The token's routed slots are
 // compacted (slot order kept) and a switch on their count picks an unrolled
-// gather, so no masked slot costs a load.  Each lane owns U 16-byte units (8 bf16) of the output
-// row (U = 2: 448 lanes cover a 7168-wide row in one pass): it issues all
-// k*U gathered 16-byte loads before the first FMA, so each lane keeps k*U
-// loads in flight, then accumulates slot by slot in order.
+// gather, so no masked slot costs a load.  Each lane owns U 16-byte units (8
+// bf16) of the output row (U = 1 with workgroups of 64 lanes for k >= 8 or
+// 128 lanes otherwise, so a 7168-wide row at k = 8 is 14 workgroups; U = 2
+// over the whole row where a row gathers about one slot): it issues all k*U
+// gathered 16-byte loads before the first FMA, so each lane keeps k*U loads
+// in flight, then accumulates slot by slot in order.
 // With k known at compile time (1, 2, 4, 8) the slot loop is unrolled; other
 // k take the generic loop.
 #include "moedisp_internal.h"
@@ -249,8 +251,12 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
-    constexpr int U = 2;  // = combine_units_per_lane(k)
-    hipLaunchKernelGGL((moedisp_combine<KC, U, kF32>), dim3(a.T * a.col_splits), dim3(a.threads), 0, stream, a);
+    const dim3 grid(a.T * a.col_splits), block(a.threads);
+    switch (a.units_per_lane) {
+        case 1: hipLaunchKernelGGL((moedisp_combine<KC, 1, kF32>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((moedisp_combine<KC, 2, kF32>), grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL((moedisp_combine<KC, 4, kF32>), grid, block, 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 

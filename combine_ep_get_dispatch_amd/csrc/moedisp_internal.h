@@ -59,11 +59,10 @@ struct CombinePlan {
     int col_splits;
     int blocks;
     int threads;
+    int units_per_lane;  // 1, 2 or 4 (16-byte units per lane, one pass)
 };
 
 constexpr int kMaxCombineThreads = 1024;
-// 16-byte units each combine lane owns per pass (k loads in flight per unit)
-inline int combine_units_per_lane(int) { return 2; }
 
 struct WsPlan {
     int layout_blocks;
@@ -76,7 +75,7 @@ DispatchPlan plan_dispatch(const moedisp_shape& s);
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s);
 DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
 moedisp_shape group_rows_shape(const moedisp_shape& s);
-CombinePlan plan_combine(const moedisp_shape& s);
+CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row);
 WsPlan plan_workspace(const moedisp_shape& s);
 inline int layout_tokens_per_block(const moedisp_shape& s) { return kLayoutThreads / s.topk; }
 
@@ -144,6 +143,7 @@ struct CombineArgs {
     int capacity;
     int col_splits;
     int threads;
+    int units_per_lane;
     const v4u* expert_out;
     const int32_t* recv_src_idx;
     const float* recv_weights;  // nullptr: every weight is 1 (plain sum)
