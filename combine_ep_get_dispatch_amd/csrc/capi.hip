@@ -143,11 +143,9 @@ CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {
     // workgroups keep loads of other rows issuing while some sum and store;
     // at H = 7168 and k = 8 a row is 14 ranges of 64 units.  Where a row
     // gathers about one (a group row of the local reduce), 2 units per lane
-    // over the whole row, so that each lane still has several loads in
-    // flight and the workgroup's fixed cost (handle loads, launch) is paid
-    // once per row.
+    // and about 256 lanes, so that each lane still has a few loads in flight.
     const int per_lane = loads_per_row >= 2 ? 1 : 2;
-    const int target = loads_per_row >= 8 ? 64 : loads_per_row >= 2 ? 128 : kMaxCombineThreads * per_lane;
+    const int target = loads_per_row >= 8 ? 64 : loads_per_row >= 2 ? 128 : 512;
     int splits = (row16 + target - 1) / target;
     if (splits < 1) splits = 1;
     p.col_splits = splits;

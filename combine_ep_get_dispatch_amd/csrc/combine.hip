@@ -23,7 +23,7 @@
 // gather, so no masked slot costs a load.  Each lane owns U 16-byte units (8
 // bf16) of the output row (U = 1 with workgroups of 64 lanes for k >= 8 or
 // 128 lanes otherwise, so a 7168-wide row at k = 8 is 14 workgroups; U = 2
-// over the whole row where a row gathers about one slot): it issues all k*U
+// and about 256 lanes where a row gathers about one slot): it issues all k*U
 // gathered 16-byte loads before the first FMA, so each lane keeps k*U loads
 // in flight, then accumulates slot by slot in order.
 // With k known at compile time (1, 2, 4, 8) the slot loop is unrolled; other
