@@ -81,6 +81,11 @@ EDGE = {
     "groups_of_6_zipf": lambda: W.make_workload("groups_of_6", 513, 64, 12, 2, 3, seed=56, routing="zipf",
                                                 mask_frac=0.2),
     "groups_of_96": lambda: W.make_workload("groups_of_96", 200, 64, 3072, 32, 8, seed=57, routing="zipf"),
+    # 875 units per row: column ranges of 63 (k = 8), 125 (k = 4) units, and
+    # the generic-k gather (k = 5), each with a shorter last range
+    "ragged_columns_k8": lambda: W.make_workload("ragged_cols_k8", 300, 7000, 64, 8, 8, seed=58),
+    "ragged_columns_k4": lambda: W.make_workload("ragged_cols_k4", 200, 7000, 32, 4, 4, seed=59, mask_frac=0.2),
+    "ragged_columns_k5": lambda: W.make_workload("ragged_cols_k5", 150, 7000, 40, 5, 5, seed=60, routing="zipf"),
 }
 
 

@@ -122,6 +122,8 @@ CASES = {
     "g32_k8": lambda: W.make_workload("g32", 129, 256, 64, 32, 8, seed=73),
     "empty": lambda: W.make_workload("empty", 0, 256, 8, 2, 2, seed=74),
     "all_masked": lambda: W.make_workload("all_masked", 40, 256, 8, 2, 2, seed=75, mask_frac=1.0),
+    # 875 units per row: the reduce's two column ranges are 438 and 437 units
+    "ragged_columns": lambda: W.make_workload("ragged_cols", 300, 7000, 64, 8, 8, seed=76, mask_frac=0.1),
 }
 
 
