@@ -55,8 +55,10 @@ static void group_index_constants(int per_group, int* shift, uint32_t* magic) {
 }
 
 // Scatter plan for rows of `units` lane units whose k copies write
-// `write_per_token` bytes; column ranges are whole multiples of `align` units.
-static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_token, int units, int align) {
+// `write_per_token` bytes; column ranges are whole multiples of `align` units;
+// a lane takes up to `max_per_lane` units per pass.
+static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_token, int units, int align,
+                                 int max_per_lane) {
     DispatchPlan p;
     const int T = s.num_tokens, k = s.topk;
     // copy: >= 64 KiB of row stores per workgroup
@@ -82,11 +84,14 @@ static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_tok
     p.block_tokens = bt;
     // at least one workgroup, so that workgroup 0 runs the total check
     p.blocks = token_blocks > 0 ? (int)(token_blocks * p.col_splits) : 1;
-    // lanes: whole waves covering one pass of the column range (one unit per
-    // lane and pass, up to 1024 lanes; wider rows loop), and at least one
-    // lane per slot of the workgroup
-    p.units_per_lane = 1;
-    int threads = (per + 63) / 64 * 64;
+    // lanes: whole waves covering one pass of the column range (up to 1024
+    // lanes; wider rows loop), and at least one lane per slot of the
+    // workgroup.  A wide range (>= 512 units) takes 2 units per lane where
+    // allowed: a 7168-wide bf16 row is then 448 lanes, and smaller workgroups
+    // pack the compute units more fully than 896-lane ones.
+    const int u = (max_per_lane >= 2 && per >= 2 * kThreads) ? 2 : 1;
+    p.units_per_lane = u;
+    int threads = ((per + u - 1) / u + 63) / 64 * 64;
     const int slot_lanes = (bt * k + 63) / 64 * 64;
     if (threads < slot_lanes) threads = slot_lanes;
     if (threads < kThreads) threads = kThreads;
@@ -96,7 +101,7 @@ static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_tok
 }
 
 DispatchPlan plan_dispatch(const moedisp_shape& s) {
-    return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1);
+    return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1, 2);
 }
 
 // Group-deduplicated dispatch: the scatter over groups (k = E = G slots per
@@ -116,7 +121,7 @@ static DispatchPlan plan_group_permute(const moedisp_shape& s) {
     const moedisp_shape rs = group_rows_shape(s);
     const int per_row = (s.topk + (s.num_groups < s.topk ? s.num_groups : s.topk) - 1) /
                         (s.num_groups < s.topk ? s.num_groups : s.topk);
-    return plan_scatter(rs, (long long)per_row * (long long)row_bytes(rs), (int)(row_bytes(rs) / 16), 1);
+    return plan_scatter(rs, (long long)per_row * (long long)row_bytes(rs), (int)(row_bytes(rs) / 16), 1, 2);
 }
 
 // The group rows seen as tokens (T * min(G, k) of them, the capacity of the
@@ -131,7 +136,7 @@ moedisp_shape group_rows_shape(const moedisp_shape& s) {
 // bytes); column ranges are whole waves so that no scale block (<= 64 lanes)
 // straddles two of them.
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s) {
-    return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64);
+    return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64, 1);
 }
 
 CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {

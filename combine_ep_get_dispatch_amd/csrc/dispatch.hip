@@ -29,7 +29,8 @@
 //    and while the copy saturates HBM those polls queue behind the stores.
 //    No atomics decide any order, so the result is deterministic.
 // The scatter then streams: each lane loads U 16-byte units of the source row
-// (U = 1 by default, up to 1024 lanes per workgroup) once - the first pass is
+// (U = 2 for column ranges of 512 units or more, such as the 448 lanes of a
+// 7168-wide bf16 row, else 1; up to 1024 lanes per workgroup) once - the first pass is
 // issued before the row computation - and stores them,
 // non-temporally, to each of the token's k destination rows (a token with no
 // receive row, such as a padding group row, is neither loaded past the first
