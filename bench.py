@@ -7,11 +7,14 @@ batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168 bf16,
 E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
 stand-in expert outputs are resident in HBM before the timed region; the
 timed region is exactly K steps between two device synchronisations.  HIP
-events on the launch stream between the calls time each call inside that
-region (the layout is two kernels, every other call one); the dominant
+events on the launch stream bracket the scatter and the combine kernels of
+every timed step (timing-only events without the system-scope cache fence,
+which a default event adds between the kernels it separates); the dominant
 kernel's algorithmic bytes over its mean duration give the roofline entry,
 with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
-when they were taken on the current kernel sources.  The CPU oracle, timed on
+when they were taken on the current kernel sources.  A second, untimed pass
+of K steps with events between every call gives the layout and notify
+phases.  The CPU oracle, timed on
 a bounded sample of the same workload on the host, is the reported baseline.
 
 Further legs, reported beside the headline (each can be skipped): the other
@@ -54,6 +57,49 @@ def make_inputs(wl, dev):
     return x, xs, idx, w
 
 
+class TimingEvent:
+    """A HIP event for timing only, recorded on a given stream: created with
+    hipEventDisableSystemFence, so recording it neither writes back nor
+    invalidates the caches (a default event does both, which costs a few
+    microseconds between the kernels it separates and slows the next one).
+    Same runtime as torch's (the library loaded under the same soname)."""
+
+    _hip = None
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes as C
+        if TimingEvent._hip is None:
+            hip = C.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+            hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+            hip.hipEventDestroy.argtypes = [C.c_void_p]
+            TimingEvent._hip = hip
+        self._C = C
+        self.e = C.c_void_p()
+        rc = TimingEvent._hip.hipEventCreateWithFlags(C.byref(self.e), TimingEvent.FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = TimingEvent._hip.hipEventRecord(self.e, self._C.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end` (both recorded and complete)."""
+        ms = self._C.c_float()
+        rc = TimingEvent._hip.hipEventElapsedTime(self._C.byref(ms), self.e, end.e)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self.e:
+            TimingEvent._hip.hipEventDestroy(self.e)
+
+
 def shape_of(M, W, wl):
     dt = M.FP8_E4M3 if wl.x_dtype == W.X_FP8 else M.BF16
     return M.moedisp_shape.make(wl.T, wl.H, wl.E, wl.G, wl.k, dt, wl.scale_block)
@@ -89,43 +135,53 @@ def run_gpu(cid, steps, warmup, dev):
     stream = torch.cuda.current_stream()
 
     # one step = layout, dispatch (its two phases: notify = count kernel,
-    # scatter = scatter kernel), combine; events between the calls time each
-    # kernel on the launch stream
-    def step(ev=None):
-        if ev is not None:
+    # scatter = scatter kernel), combine.  `ev` holds events recorded at the
+    # positions named in `at` (0 before the layout, 1 before notify, 2 before
+    # the scatter, 3 before the combine, 4 after it).
+    def step(ev=None, at=()):
+        if 0 in at:
             ev[0].record(stream)
         bufs.layout(idx, stream)
-        if ev is not None:
+        if 1 in at:
             ev[1].record(stream)
         bufs.dispatch_notify(idx, stream)
-        if ev is not None:
+        if 2 in at:
             ev[2].record(stream)
         bufs.dispatch_scatter(x, xs, idx, w, stream)
-        if ev is not None:
+        if 3 in at:
             ev[3].record(stream)
         bufs.combine(eo, out, M.BF16, True, stream)
-        if ev is not None:
+        if 4 in at:
             ev[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    # timed region: events bracket the scatter and the combine of every step
+    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i])
+        step(evs[i], (2, 3, 4))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = bufs.status()
     if st:
         raise RuntimeError(f"device status {st} after timed steps on config {cid}")
-
     elapsed = t1 - t0
-    lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
-    ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    sct = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    sct = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3  # us
     com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
+    # untimed pass: events between every call, for the layout and notify phases
+    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i], (0, 1, 2, 3, 4))
+    torch.cuda.synchronize()
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} after the phase pass on config {cid}")
+    lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
     dis = ntf + sct
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
@@ -170,7 +226,7 @@ def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
     for _ in range(warmup):
         bufs.dispatch_notify(idx, stream)
         bufs.dispatch_scatter_quant(x, idx, w, stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         evs[i][0].record(stream)
@@ -226,7 +282,7 @@ def run_gpu_groups(cid, steps, warmup, dev):
     for _ in range(warmup):
         for c in calls:
             c()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    evs = [[TimingEvent() for _ in range(len(calls) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
         for j, c in enumerate(calls):
@@ -285,7 +341,7 @@ def run_gpu_decode(cid, steps, warmup, dev):
         stream = torch.cuda.current_stream()
         for _ in range(warmup):
             fn(stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         torch.cuda.synchronize()
         e0.record(stream)
         for _ in range(steps):
@@ -313,7 +369,7 @@ def run_gpu_decode(cid, steps, warmup, dev):
     res["small_graph_us"] = per_step(lambda stream: graph.replay()) / per_graph
     # the small-batch dispatch alone, events around each call
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     for a, b in ev:
         a.record(stream)
         bufs.layout_dispatch_small(x, xs, idx, w, stream)
@@ -340,12 +396,13 @@ def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
     dst = torch.empty_like(src)
     for _ in range(3):
         M.ep_probe_copy(dst, src, nbytes)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s, e = TimingEvent(), TimingEvent()
+    stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
-    s.record()
+    s.record(stream)
     for _ in range(reps):
         M.ep_probe_copy(dst, src, nbytes)
-    e.record()
+    e.record(stream)
     torch.cuda.synchronize()
     us = s.elapsed_time(e) * 1e3 / reps
     del src, dst
