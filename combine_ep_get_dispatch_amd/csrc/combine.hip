@@ -252,11 +252,10 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
     const dim3 grid(a.T * a.col_splits), block(a.threads);
-    switch (a.units_per_lane) {
-        case 1: hipLaunchKernelGGL((moedisp_combine<KC, 1, kF32>), grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((moedisp_combine<KC, 2, kF32>), grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL((moedisp_combine<KC, 4, kF32>), grid, block, 0, stream, a); break;
-    }
+    if (a.units_per_lane == 1)
+        hipLaunchKernelGGL((moedisp_combine<KC, 1, kF32>), grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL((moedisp_combine<KC, 2, kF32>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

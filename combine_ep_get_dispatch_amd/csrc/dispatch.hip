@@ -576,11 +576,10 @@ hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream) {
     const DispatchPlan& p = a.plan;
     const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
     const dim3 grid(p.blocks), block(p.threads);
-    switch (p.units_per_lane) {
-        case 1: hipLaunchKernelGGL((moedisp_scatter<1>), grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL((moedisp_scatter<2>), grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL((moedisp_scatter<4>), grid, block, lds, stream, a); break;
-    }
+    if (p.units_per_lane == 1)
+        hipLaunchKernelGGL((moedisp_scatter<1>), grid, block, lds, stream, a);
+    else
+        hipLaunchKernelGGL((moedisp_scatter<2>), grid, block, lds, stream, a);
     return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ struct DispatchPlan {
     int split_units;
     int blocks;
     int threads;
-    int units_per_lane;  // 1, 2 or 4
+    int units_per_lane;  // 1 or 2
 };
 
 constexpr int kMaxDispatchThreads = 1024;
@@ -59,7 +59,7 @@ struct CombinePlan {
     int col_splits;
     int blocks;
     int threads;
-    int units_per_lane;  // 1, 2 or 4 (16-byte units per lane, one pass)
+    int units_per_lane;  // 1 or 2 (16-byte units per lane, one pass)
 };
 
 constexpr int kMaxCombineThreads = 1024;
