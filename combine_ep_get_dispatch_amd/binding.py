@@ -40,7 +40,8 @@ DEV_DUPLICATE_EXPERT = 2
 DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
 
-EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_dispatch",
+EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_get_dispatch_layout_notify",
+           "ep_dispatch",
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_layout_dispatch_small",
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH):
     L.ep_workspace_init.restype = C.c_int
     L.ep_get_dispatch_layout.argtypes = [S, P, P, P, P, P, C.c_size_t, P]
     L.ep_get_dispatch_layout.restype = C.c_int
+    L.ep_get_dispatch_layout_notify.argtypes = [S, P, P, P, P, P, P, C.c_size_t, P]
+    L.ep_get_dispatch_layout_notify.restype = C.c_int
     L.ep_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch.restype = C.c_int
     L.ep_dispatch_notify.argtypes = [S, P, P, P, P, C.c_size_t, P]
@@ -150,6 +153,13 @@ def ep_get_dispatch_layout(shape, topk_idx, tokens_per_expert, tokens_per_group,
     _check("ep_get_dispatch_layout", load().ep_get_dispatch_layout(
         C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group),
         _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+def ep_get_dispatch_layout_notify(shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group,
+                                  expert_offsets, ws, stream=None):
+    _check("ep_get_dispatch_layout_notify", load().ep_get_dispatch_layout_notify(
+        C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group),
+        _p(expert_offsets), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
 def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales, recv_src_idx,
@@ -277,6 +287,12 @@ class EpBuffers:
     def layout(self, topk_idx, stream=None):
         ep_get_dispatch_layout(self.shape, topk_idx, self.tokens_per_expert, self.tokens_per_group,
                                self.is_token_in_group, self.ws, stream)
+
+    def layout_notify(self, topk_idx, stream=None):
+        """Layout and the dispatch's notify phase in one call; dispatch_scatter
+        follows."""
+        ep_get_dispatch_layout_notify(self.shape, topk_idx, self.tokens_per_expert, self.tokens_per_group,
+                                      self.is_token_in_group, self.expert_offsets, self.ws, stream)
 
     def dispatch(self, x, x_scales, topk_idx, topk_weights, stream=None):
         ep_dispatch(self.shape, x, x_scales, topk_idx, topk_weights, self.tokens_per_expert, self.recv_x,

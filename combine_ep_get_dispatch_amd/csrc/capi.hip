@@ -28,11 +28,9 @@ static int check_shape(const moedisp_shape* s) {
         return MOEDISP_ERR_UNSUPPORTED;
     }
     if (row_bytes(*s) % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
-    // receive rows and look-back values must fit 30 bits; bf16 rows of the
-    // combine must fit the same index space
+    // receive row indices (T*k of them) are int32 with headroom
     const long long cap = (long long)s->num_tokens * s->topk;
     if (cap >= (1ll << 30)) return MOEDISP_ERR_UNSUPPORTED;
-    if ((long long)s->hidden * 2 / 16 >= (1ll << 30)) return MOEDISP_ERR_UNSUPPORTED;
     return MOEDISP_OK;
 }
 
@@ -191,7 +189,12 @@ static int check_ws(const moedisp_shape* s, void* ws, size_t ws_bytes) {
     return MOEDISP_OK;
 }
 
-static int hip_status(hipError_t e) { return e == hipSuccess ? MOEDISP_OK : MOEDISP_ERR_HIP; }
+// hipErrorInvalidConfiguration comes from a launcher's grid-size check (a
+// shape whose grid exceeds 2^32 work-items); any other failure is a HIP error.
+static int hip_status(hipError_t e) {
+    if (e == hipSuccess) return MOEDISP_OK;
+    return e == hipErrorInvalidConfiguration ? MOEDISP_ERR_UNSUPPORTED : MOEDISP_ERR_HIP;
+}
 
 }  // namespace moedisp
 
@@ -210,9 +213,10 @@ int ep_workspace_init(void* ws, size_t ws_bytes, void* stream) {
     return hip_status(launch_fill_zero(ws, ws_bytes & ~(size_t)3, (hipStream_t)stream));
 }
 
-int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
-                           int32_t* tokens_per_group, uint32_t* is_token_in_group, void* ws, size_t ws_bytes,
-                           void* stream) {
+// Checks of the layout call; fills the launch arguments (notify phase off).
+static int layout_args(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
+                       int32_t* tokens_per_group, uint32_t* is_token_in_group, void* ws, size_t ws_bytes,
+                       LayoutArgs* a) {
     int st = check_shape(s);
     if (st) return st;
     if ((s->num_tokens > 0 && (!topk_idx || !is_token_in_group)) || !tokens_per_expert || !tokens_per_group)
@@ -222,23 +226,37 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
         return MOEDISP_ERR_MISALIGNED;
     if ((st = check_ws(s, ws, ws_bytes))) return st;
     const WsPlan w = plan_workspace(*s);
+    a->T = s->num_tokens;
+    a->k = s->topk;
+    a->E = s->num_experts;
+    a->G = s->num_groups;
+    a->id_bits = 0;
+    while ((1 << a->id_bits) < a->E) ++a->id_bits;
+    group_index_constants(a->E / a->G, &a->pg_shift, &a->pg_magic);
+    group_index_constants(a->k, &a->k_shift, &a->k_magic);
+    a->tokens_per_block = layout_tokens_per_block(*s);
+    a->topk_idx = topk_idx;
+    a->tokens_per_expert = tokens_per_expert;
+    a->tokens_per_group = tokens_per_group;
+    a->is_token_in_group = is_token_in_group;
+    a->hdr = (WsHeader*)ws;
+    a->partials = (int32_t*)((char*)ws + w.partial_offset);
+    a->blocks = w.layout_blocks;
+    a->tile_counts = nullptr;
+    a->tile_shift = 0;
+    a->tiles = 0;
+    a->tile_stride = 0;
+    a->expert_offsets = nullptr;
+    a->capacity = s->num_tokens * s->topk;
+    return MOEDISP_OK;
+}
+
+int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
+                           int32_t* tokens_per_group, uint32_t* is_token_in_group, void* ws, size_t ws_bytes,
+                           void* stream) {
     LayoutArgs a;
-    a.T = s->num_tokens;
-    a.k = s->topk;
-    a.E = s->num_experts;
-    a.G = s->num_groups;
-    a.id_bits = 0;
-    while ((1 << a.id_bits) < a.E) ++a.id_bits;
-    group_index_constants(a.E / a.G, &a.pg_shift, &a.pg_magic);
-    group_index_constants(a.k, &a.k_shift, &a.k_magic);
-    a.tokens_per_block = layout_tokens_per_block(*s);
-    a.topk_idx = topk_idx;
-    a.tokens_per_expert = tokens_per_expert;
-    a.tokens_per_group = tokens_per_group;
-    a.is_token_in_group = is_token_in_group;
-    a.hdr = (WsHeader*)ws;
-    a.partials = (int32_t*)((char*)ws + w.partial_offset);
-    a.blocks = w.layout_blocks;
+    const int st = layout_args(s, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws, ws_bytes, &a);
+    if (st) return st;
     return hip_status(launch_layout(a, (hipStream_t)stream));
 }
 
@@ -310,6 +328,38 @@ int ep_dispatch_notify(const moedisp_shape* s, const int32_t* topk_idx, const in
     return hip_status(launch_dispatch_notify(a, (hipStream_t)stream));
 }
 
+// LDS a layout workgroup may use with the notify phase folded in.
+constexpr size_t kLayoutNotifyLds = 64 * 1024;
+
+int ep_get_dispatch_layout_notify(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
+                                  int32_t* tokens_per_group, uint32_t* is_token_in_group, int32_t* expert_offsets,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    LayoutArgs a;
+    int st = layout_args(s, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws, ws_bytes, &a);
+    if (st) return st;
+    if (!expert_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(expert_offsets, 4)) return MOEDISP_ERR_MISALIGNED;
+    // the dispatch's tiles must lie inside the layout workgroups, and their
+    // counts fit in LDS; otherwise the two calls, in order
+    const DispatchPlan P = plan_dispatch(*s);
+    int shift = 0;
+    while ((1 << shift) < P.tile_tokens) ++shift;
+    const int tpb = a.tokens_per_block;
+    const bool fused = s->num_tokens > 0 && (1 << shift) == P.tile_tokens && tpb % P.tile_tokens == 0 &&
+                       layout_lds_bytes(a.E, a.G, a.k, tpb, tpb / P.tile_tokens) <= kLayoutNotifyLds;
+    if (!fused) {
+        if ((st = hip_status(launch_layout(a, (hipStream_t)stream)))) return st;
+        return ep_dispatch_notify(s, topk_idx, tokens_per_expert, expert_offsets, ws, ws_bytes, stream);
+    }
+    const WsPlan w = plan_workspace(*s);
+    a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    a.tile_shift = shift;
+    a.tiles = P.tiles;
+    a.tile_stride = P.tile_stride;
+    a.expert_offsets = expert_offsets;
+    return hip_status(launch_layout(a, (hipStream_t)stream));
+}
+
 int ep_dispatch_scatter(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
                         const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
                         int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
@@ -329,6 +379,7 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
     const int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
                                  recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a);
     if (st) return st;
+    if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     const hipError_t e = launch_dispatch_notify(a, (hipStream_t)stream);
     if (e != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
@@ -411,6 +462,7 @@ int ep_dispatch_quant(const moedisp_shape* s, int32_t quant_block, int32_t scale
                               recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, &a);
     if (st) return st;
     // the count kernel's tile plan is the shape's, shared with the copy path
+    if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter_quant(a, scale_fmt, (hipStream_t)stream));
 }
@@ -566,6 +618,7 @@ int ep_dispatch_groups(const moedisp_shape* s, const void* x, const float* x_sca
     a.recv_topk_weights = recv_topk_weights;
     a.hdr = (WsHeader*)ws;
     a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
 }
@@ -584,6 +637,7 @@ int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* g
     if (st) return st;
     a.capacity = s->num_tokens * s->topk;  // the receive buffers hold T*k rows
     a.plan = plan_group_permute(*s);       // same tiles as plan_dispatch(rs), more rows per workgroup
+    if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
 }

@@ -251,7 +251,9 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 
 template <int KC, bool kF32>
 hipError_t launch_k(const CombineArgs& a, hipStream_t stream) {
-    const dim3 grid(a.T * a.col_splits), block(a.threads);
+    const long long blocks = (long long)a.T * a.col_splits;
+    if (!grid_fits(blocks, a.threads)) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks), block(a.threads);
     if (a.units_per_lane == 1)
         hipLaunchKernelGGL((moedisp_combine<KC, 1, kF32>), grid, block, 0, stream, a);
     else

@@ -557,6 +557,7 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_quant(Dis
 }  // namespace
 
 hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream) {
+    if (!grid_fits(a.plan.tiles, kThreads)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(moedisp_count, dim3(a.plan.tiles), dim3(kThreads), (size_t)a.E * sizeof(int32_t), stream, a);
     return hipGetLastError();
 }
@@ -564,6 +565,7 @@ hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream) {
 hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, hipStream_t stream) {
     const DispatchPlan& p = a.plan;
     const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
+    if (!grid_fits(p.blocks, p.threads)) return hipErrorInvalidConfiguration;
     const dim3 grid(p.blocks), block(p.threads);
     if (scale_fmt == MOEDISP_SCALE_UE8M0)
         hipLaunchKernelGGL((moedisp_scatter_quant<MOEDISP_SCALE_UE8M0>), grid, block, lds, stream, a);
@@ -575,6 +577,7 @@ hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, h
 hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream) {
     const DispatchPlan& p = a.plan;
     const size_t lds = (size_t)p.tile_tokens * a.k * sizeof(int32_t);
+    if (!grid_fits(p.blocks, p.threads)) return hipErrorInvalidConfiguration;
     const dim3 grid(p.blocks), block(p.threads);
     if (p.units_per_lane == 1)
         hipLaunchKernelGGL((moedisp_scatter<1>), grid, block, lds, stream, a);

@@ -20,6 +20,13 @@
 // inside one kernel needs a device-scope fence and a same-address atomic per
 // workgroup; measured on this part, those serialise across the XCDs and cost
 // more than the second launch.)
+//
+// With the dispatch's notify phase folded in (ep_get_dispatch_layout_notify),
+// each workgroup also counts its slots per (dispatch tile, expert): the lanes
+// of one tile are a contiguous range of the wave, so the expert peer mask
+// restricted to that range gives the tile count with no further ballots; the
+// counts are stored expert-major as the count kernel would, and the reduce
+// kernel also writes expert_offsets, the exclusive scan of the totals.
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -48,13 +55,17 @@ __device__ inline uint32_t div_const(uint32_t x, int shift, uint32_t magic) {
 }
 
 __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
-    extern __shared__ int32_t dyn[];  // counts [E + G], ids [tokens * k], token masks [tokens]
+    // LDS: counts [E + G], ids [tokens * k], token masks [tokens], and with
+    // the notify phase tile counts [tiles per workgroup][E]
+    extern __shared__ int32_t dyn[];
     const int EG = a.E + a.G;
     const int k = a.k;
     const int tpb = a.tokens_per_block;
     int32_t* s_cnt = dyn;
     int32_t* s_ids = dyn + EG;
     uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_ids + tpb * k);
+    int32_t* s_tile = reinterpret_cast<int32_t*>(s_mask + tpb);
+    const int tpw = a.tile_counts ? (tpb >> a.tile_shift) : 0;  // tiles per workgroup
     __shared__ uint32_t s_err;
 
     const int tid = threadIdx.x;
@@ -76,6 +87,7 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
     }
     for (int i = tid; i < EG; i += nth) s_cnt[i] = 0;
     for (int i = tid; i < nt; i += nth) s_mask[i] = 0;
+    for (int i = tid; i < tpw * a.E; i += nth) s_tile[i] = 0;
     if (tid < ns) s_ids[tid] = id;
     if (tid == 0) s_err = 0;
     __syncthreads();
@@ -86,6 +98,19 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
     const uint64_t active = __ballot(routed);
     const uint64_t peers = match_peers(routed ? (uint32_t)id : 0u, a.id_bits, active);
     if (routed && (peers & below) == 0) atomicAdd(&s_cnt[id], (int32_t)__popcll(peers));
+    // tile counts: the peers whose slots lie in this lane's tile (slots
+    // [tile * 2^tile_shift * k, (tile + 1) * 2^tile_shift * k) of the
+    // workgroup, a contiguous lane range of the wave)
+    if (tpw > 0 && routed) {
+        const int tile = (int)div_const((uint32_t)tid, a.k_shift, a.k_magic) >> a.tile_shift;
+        const int span = (k << a.tile_shift);
+        const int w0 = tid - lane;
+        const int lo = max(tile * span - w0, 0);
+        const int hi = min((tile + 1) * span - w0, 64);
+        const uint64_t range = (hi >= 64 ? ~0ull : ((1ull << hi) - 1ull)) & ~((1ull << lo) - 1ull);
+        const uint64_t tp = peers & range;
+        if ((tp & below) == 0) atomicAdd(&s_tile[tile * a.E + id], (int32_t)__popcll(tp));
+    }
     // token masks and repeated experts
     if (routed) {
         const int tl = (int)div_const((uint32_t)tid, a.k_shift, a.k_magic);
@@ -114,6 +139,15 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
 
     int32_t* mine = a.partials + (size_t)blockIdx.x * EG;
     for (int i = tid; i < EG; i += nth) mine[i] = s_cnt[i];
+    if (tpw > 0) {  // expert-major, this workgroup's tiles contiguous per expert
+        const int tile0 = blockIdx.x * tpw;
+        const int ntl = min(tpw, a.tiles - tile0);
+        for (int i = tid; i < a.E * ntl; i += nth) {
+            const int e = i / ntl;
+            const int q = i - e * ntl;
+            a.tile_counts[(size_t)e * a.tile_stride + tile0 + q] = s_tile[q * a.E + e];
+        }
+    }
     if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
 }
 
@@ -121,6 +155,8 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
 // boundary orders it after every partial), 32 independent loads in flight:
 // one round trip for up to 32 partial rows.
 __global__ __launch_bounds__(kThreads) void moedisp_layout_reduce(LayoutArgs a) {
+    __shared__ int32_t s_tot[kMaxExperts];  // expert totals, for expert_offsets
+    __shared__ int32_t s_wave[kThreads / 64];
     const int EG = a.E + a.G;
     constexpr int kBatch = 32;
     for (int i = threadIdx.x; i < EG; i += kThreads) {
@@ -133,17 +169,49 @@ __global__ __launch_bounds__(kThreads) void moedisp_layout_reduce(LayoutArgs a) 
 #pragma unroll
             for (int q = 0; q < kBatch; ++q) sum += v[q];
         }
-        if (i < a.E)
+        if (i < a.E) {
             a.tokens_per_expert[i] = sum;
-        else
+            s_tot[i] = sum;
+        } else {
             a.tokens_per_group[i - a.E] = sum;
+        }
+    }
+    if (!a.expert_offsets) return;  // uniform
+    // expert_offsets: exclusive scan of the totals, a contiguous run per lane
+    __syncthreads();
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (a.E + kThreads - 1) / kThreads;
+    const int lo = min(a.E, tid * per), hi = min(a.E, lo + per);
+    int32_t run = 0;
+    for (int i = lo; i < hi; ++i) run += s_tot[i];
+    int32_t incl = run;
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int32_t off = incl - run, total = 0;
+    for (int w = 0; w < kThreads / 64; ++w) {
+        if (w < wave) off += s_wave[w];
+        total += s_wave[w];
+    }
+    for (int i = lo; i < hi; ++i) {
+        a.expert_offsets[i] = off;
+        off += s_tot[i];
+    }
+    if (tid == 0) {
+        a.expert_offsets[a.E] = total;
+        if (total > a.capacity) atomicOr(&a.hdr->status, (uint32_t)MOEDISP_DEV_BAD_LAYOUT);
     }
 }
 
 }  // namespace
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-    const size_t lds = ((size_t)a.E + a.G + (size_t)a.tokens_per_block * (a.k + 1)) * sizeof(int32_t);
+    const size_t lds = layout_lds_bytes(a.E, a.G, a.k, a.tokens_per_block,
+                                        a.tile_counts ? (a.tokens_per_block >> a.tile_shift) : 0);
+    if (!grid_fits(a.blocks, kLayoutThreads)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kLayoutThreads), lds, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

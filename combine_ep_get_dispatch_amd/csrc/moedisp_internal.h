@@ -78,6 +78,10 @@ moedisp_shape group_rows_shape(const moedisp_shape& s);
 CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row);
 WsPlan plan_workspace(const moedisp_shape& s);
 inline int layout_tokens_per_block(const moedisp_shape& s) { return kLayoutThreads / s.topk; }
+// LDS of a layout workgroup (tiles_per_block > 0 with the notify phase folded in)
+inline size_t layout_lds_bytes(int E, int G, int k, int tokens_per_block, int tiles_per_block) {
+    return ((size_t)E + G + (size_t)tokens_per_block * (k + 1) + (size_t)tiles_per_block * E) * sizeof(int32_t);
+}
 
 inline size_t row_bytes(const moedisp_shape& s) {
     return (size_t)s.hidden * (s.x_dtype == MOEDISP_FP8_E4M3 ? 1 : 2);
@@ -101,6 +105,16 @@ struct LayoutArgs {
     WsHeader* hdr;
     int32_t* partials;
     int blocks;
+    // the dispatch's notify phase in the same launches (ep_get_dispatch_layout_notify)
+    // when tile_counts != nullptr: per-tile expert counts in the dispatch's tile
+    // geometry (2^tile_shift tokens per tile, dividing tokens_per_block; tiles
+    // tiles; tile_stride ints per expert) and expert_offsets [E+1]
+    int32_t* tile_counts;
+    int tile_shift;
+    int tiles;
+    int tile_stride;
+    int32_t* expert_offsets;
+    int capacity;
 };
 
 struct DispatchArgs {
@@ -181,6 +195,14 @@ struct FusedArgs {
     int32_t* slot_to_row;
     WsHeader* hdr;
 };
+
+// A dispatch packet holds the grid size in work-items as 32 bits: a launch of
+// `blocks` workgroups of `threads` lanes must stay below 2^32 work-items.
+// Launchers return hipErrorInvalidConfiguration otherwise (the C ABI reports
+// MOEDISP_ERR_UNSUPPORTED).
+inline bool grid_fits(long long blocks, long long threads) {
+    return blocks >= 1 && blocks <= 0x7FFFFFFFll && blocks * threads <= 0xFFFFFFFFll;
+}
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_fused(const FusedArgs& a, hipStream_t stream);

@@ -77,7 +77,9 @@ typedef struct {
 /* Host-side return codes. */
 #define MOEDISP_OK 0
 #define MOEDISP_ERR_INVALID_ARG (-1)          /* null pointer, negative size, E % G != 0, ... */
-#define MOEDISP_ERR_UNSUPPORTED (-2)          /* a limit above exceeded, row not whole 16-B units */
+#define MOEDISP_ERR_UNSUPPORTED (-2)          /* a limit above exceeded, row not whole 16-B units,
+                                                T*k >= 2^30, or a launch grid of 2^32 work-items or
+                                                more (T*H beyond about 2^35); nothing is launched */
 #define MOEDISP_ERR_MISALIGNED (-3)           /* pointer alignment rule broken */
 #define MOEDISP_ERR_WORKSPACE_TOO_SMALL (-4)  /* ws_bytes < ep_workspace_bytes(shape) */
 #define MOEDISP_ERR_HIP (-5)                  /* a HIP runtime call or launch failed */
@@ -147,6 +149,22 @@ int ep_dispatch_scatter(const moedisp_shape* shape, const void* x, const float* 
                         const int32_t* tokens_per_expert, void* recv_x, float* recv_scales,
                         int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                         int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
+
+/* ep_get_dispatch_layout followed by ep_dispatch_notify of the same topk_idx,
+ * with exactly their outputs (tokens_per_expert, tokens_per_group,
+ * is_token_in_group, expert_offsets, and the per-tile counts that
+ * ep_dispatch_scatter reads from `ws`), in the layout's two launches instead
+ * of three: the layout workgroups also count their slots per dispatch tile,
+ * and the layout's reduce also scans the totals.  Where the dispatch's tiles
+ * do not lie inside the layout's workgroups (k that does not divide 1024,
+ * very large T) or their counts do not fit in 64 KiB of LDS with the
+ * layout's own (large E), it makes the two calls in order.  Arguments and
+ * layouts as for the two calls; expert_offsets int32 [E+1].  Status bits:
+ * BAD_EXPERT_ID, DUPLICATE_EXPERT, BAD_LAYOUT. */
+int ep_get_dispatch_layout_notify(const moedisp_shape* shape, const int32_t* topk_idx,
+                                  int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                                  uint32_t* is_token_in_group, int32_t* expert_offsets, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* Small-batch (decode) path: ep_get_dispatch_layout and ep_dispatch in one
  * kernel launch, with exactly their outputs (all of them, bit for bit).  The

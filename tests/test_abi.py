@@ -91,6 +91,19 @@ def test_host_checks_layout(lib):
     assert lib.ep_get_dispatch_layout(None, p(), p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
 
 
+def test_host_checks_layout_notify(lib):
+    """The fused layout + notify call: the layout's checks, plus expert_offsets."""
+    def rc(s, offs=None, tpe=None, ws_bytes=1 << 30):
+        return lib.ep_get_dispatch_layout_notify(C.byref(s), p(), tpe or p(), p(), p(), offs, p(), ws_bytes, None)
+    assert rc(shape(), offs=None) == B.ERR_INVALID_ARG
+    assert rc(shape(), offs=p(2)) == B.ERR_MISALIGNED
+    assert rc(shape(), offs=p(), tpe=p(1)) == B.ERR_MISALIGNED
+    assert rc(shape(E=255), offs=p()) == B.ERR_INVALID_ARG
+    assert rc(shape(k=33, E=64), offs=p()) == B.ERR_UNSUPPORTED
+    assert rc(shape(), offs=p(), ws_bytes=100) == B.ERR_WORKSPACE_TOO_SMALL
+    assert lib.ep_get_dispatch_layout_notify(None, p(), p(), p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
+
+
 def test_host_checks_dispatch(lib):
     assert dispatch_rc(lib, shape(), x=p(8)) == B.ERR_MISALIGNED           # rows need 16-byte alignment
     assert dispatch_rc(lib, shape(), recv_x=p(4)) == B.ERR_MISALIGNED
