@@ -21,7 +21,8 @@ Further legs, reported beside the headline (each can be skipped): the other
 workloads (skewed routing, fp8 decode, Mixtral shape), quantise-on-dispatch
 (FP32 and UE8M0 block scales), the group-deduplicated path, decode-step
 latency (four calls, the small-batch path, and that path from a HIP graph),
-and a plain-copy bandwidth probe.
+a plain-copy bandwidth probe, and a write probe (4 KiB chunks in address
+order and permuted) that brackets the scatter's achievable write rate.
 
 Prints one JSON line.  `--gpus` above 1 is refused: the library runs one
 GPU's share of the path on one GPU.
@@ -387,6 +388,33 @@ def run_gpu_decode(cid, steps, warmup, dev):
     return res
 
 
+def probe_fill_gbps(dev, nbytes=32768 * 14336, reps=20):
+    """HBM write bandwidth of 4 KiB chunks written in address order and in a
+    permuted order (ep_probe_fill), over a buffer the size of the
+    T=4096 H=7168 k=8 receive rows: the two ends between which the scatter's
+    row writes (one moving write front per expert segment) fall."""
+    import torch
+    import combine_ep_get_dispatch_amd as M
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    res = {"bytes": nbytes}
+    for shuffled, tag in ((False, "sequential_4k"), (True, "shuffled_4k")):
+        for _ in range(3):
+            M.ep_probe_fill(dst, nbytes, shuffled)
+        s, e = TimingEvent(), TimingEvent()
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            M.ep_probe_fill(dst, nbytes, shuffled)
+        e.record(stream)
+        torch.cuda.synchronize()
+        us = s.elapsed_time(e) * 1e3 / reps
+        res[tag] = nbytes / (us * 1e-6) / 1e9
+    del dst
+    torch.cuda.empty_cache()
+    return res
+
+
 def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
     """Achievable HBM copy bandwidth (read + write bytes) with the library's
     plain 16-byte copy kernel."""
@@ -506,6 +534,10 @@ def main():
     probe = None if args.no_probe else probe_copy_gbps(dev)
     if probe:
         log(f"[bench] probe copy {probe:.0f} GB/s")
+    probe_w = None if args.no_probe else probe_fill_gbps(dev)
+    if probe_w:
+        log(f"[bench] probe write {probe_w['sequential_4k']:.0f} GB/s in address order, "
+            f"{probe_w['shuffled_4k']:.0f} GB/s permuted")
 
     # dominant kernel: the longer of the scatter kernel (which moves all of the
     # dispatch's row bytes) and the combine kernel
@@ -558,6 +590,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": dom_us},
         "probe_copy_gbps": probe,
+        "probe_write_gbps": probe_w,
         "other_workloads": others,
         "quant_dispatch": quant,
         "group_path": groups,

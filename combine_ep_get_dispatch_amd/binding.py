@@ -45,7 +45,7 @@ EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", 
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_layout_dispatch_small",
-           "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy")
+           "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy", "ep_probe_fill")
 
 
 class MoeDispError(RuntimeError):
@@ -117,6 +117,8 @@ def load(path: str = LIB_PATH):
     L.ep_status_string.restype = C.c_char_p
     L.ep_probe_copy.argtypes = [P, P, C.c_size_t, P]
     L.ep_probe_copy.restype = C.c_int
+    L.ep_probe_fill.argtypes = [P, C.c_size_t, C.c_int32, P]
+    L.ep_probe_fill.restype = C.c_int
     _lib = L
     return L
 
@@ -256,6 +258,10 @@ def ep_check_status(ws, stream=None) -> int:
 
 def ep_probe_copy(dst, src, nbytes: int, stream=None):
     _check("ep_probe_copy", load().ep_probe_copy(_p(dst), _p(src), int(nbytes), _s(stream)))
+
+
+def ep_probe_fill(dst, nbytes: int, shuffled: bool = False, stream=None):
+    _check("ep_probe_fill", load().ep_probe_fill(_p(dst), int(nbytes), 1 if shuffled else 0, _s(stream)))
 
 
 class EpBuffers:

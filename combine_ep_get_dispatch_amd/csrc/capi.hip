@@ -735,4 +735,23 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     return hip_status(launch_copy((v4u*)dst, (const v4u*)src, bytes / 16, (hipStream_t)stream));
 }
 
+int ep_probe_fill(void* dst, size_t bytes, int32_t shuffled, void* stream) {
+    if (!dst && bytes) return MOEDISP_ERR_INVALID_ARG;
+    if (bytes % 4096 != 0 || (shuffled != 0 && shuffled != 1)) return MOEDISP_ERR_UNSUPPORTED;
+    if (!aligned(dst, 16)) return MOEDISP_ERR_MISALIGNED;
+    const size_t chunks = bytes / 4096;
+    size_t mult = 1;
+    if (shuffled && chunks > 1) {
+        // a prime near chunks * golden ratio that does not divide chunks:
+        // consecutive workgroups land far apart, and the map is a bijection
+        static const size_t primes[] = {1000003, 999983, 999979, 1299709, 15485863, 32452843};
+        for (size_t p : primes)
+            if (chunks % p != 0) {
+                mult = p;
+                break;
+            }
+    }
+    return hip_status(launch_probe_fill((v4u*)dst, chunks, mult, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -309,12 +309,14 @@ __device__ inline void store_units(const DispatchArgs& a, const int32_t* rows, c
         asm volatile("" ::: "memory");  // all 8 reads before the stores
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            if (j0 + q >= a.k || rr[q] < 0) continue;
-            v4u* dst = a.recv_x + (size_t)rr[q] * a.row16;
+            // the row is the same for the whole workgroup (one LDS word)
+            const int r = __builtin_amdgcn_readfirstlane(rr[q]);
+            if (j0 + q >= a.k || r < 0) continue;
+            v4u* dst = a.recv_x + (size_t)r * a.row16;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int cc = c + u * nth;
-                if (cc < c1) __builtin_nontemporal_store(v[u], dst + cc);
+                if (cc < c1) stream_store(v[u], dst, (uint32_t)a.row16 * 16u, cc);
             }
         }
     }

@@ -13,6 +13,19 @@ namespace moedisp {
 // 16-byte unit of a row (one global_load/store_dwordx4 per lane).
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// Streaming store of one 16-byte unit into a row that is written once and
+// not read again by this kernel: buffer_store_dwordx4 with the non-temporal
+// and both system-coherence bits (sc0 sc1 nt).  For the row copy of the
+// scatter (k full-row writes per loaded row) this measured slightly faster
+// on gfx950 than the plain non-temporal global store.  `row` (the row's base
+// address) must be the same in every lane of the wave: it becomes the buffer
+// descriptor (scalar registers).
+constexpr int kStreamStorePolicy = 1 | 2 | 16;  // sc0 | nt | sc1
+__device__ inline void stream_store(v4u v, v4u* row, uint32_t row_bytes, int unit) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)row_bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, unit * 16, 0, kStreamStorePolicy);
+}
+
 constexpr int kThreads = 256;              // threads per workgroup (4 wave64s)
 constexpr int kLayoutThreads = 1024;       // layout: one lane per slot, kLayoutThreads / k tokens per workgroup
 constexpr int kMaxExperts = 4096;
@@ -213,5 +226,6 @@ hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream);
 hipError_t launch_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream);
+hipError_t launch_probe_fill(v4u* dst, size_t chunks, size_t mult, hipStream_t stream);
 
 }  // namespace moedisp

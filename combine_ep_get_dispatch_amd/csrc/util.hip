@@ -1,5 +1,6 @@
-// Small helper kernels: workspace fill, single-word store, and the plain
-// 16-byte copy used to calibrate achievable HBM bandwidth.
+// Small helper kernels: workspace fill, single-word store, and the
+// calibration probes of achievable HBM bandwidth: a plain 16-byte copy and a
+// 4 KiB-chunk write in address or permuted order.
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -29,7 +30,29 @@ __global__ __launch_bounds__(kThreads) void moedisp_probe_copy(v4u* __restrict__
     for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Write-order probe: workgroup b writes chunk (b * mult) mod nchunks of
+// kFillChunk16 16-byte units, one store per lane (mult = 1: address order;
+// mult coprime with nchunks: a permutation of the chunks).  Unit i of the
+// buffer gets {i, i >> 32, ~i, 0x5EED}, so the result does not depend on the
+// order.
+constexpr int kFillChunk16 = 256;  // 4 KiB chunks of 256 lanes
+__global__ __launch_bounds__(kFillChunk16) void moedisp_probe_fill(v4u* __restrict__ dst, uint64_t nchunks,
+                                                                   uint64_t mult) {
+    const uint64_t chunk = ((uint64_t)blockIdx.x * mult) % nchunks;
+    const uint64_t i = chunk * kFillChunk16 + threadIdx.x;
+    const v4u v = {(uint32_t)i, (uint32_t)(i >> 32), ~(uint32_t)i, 0x5EEDu};
+    dst[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_probe_fill(v4u* dst, size_t chunks, size_t mult, hipStream_t stream) {
+    if (chunks == 0) return hipSuccess;
+    if (!grid_fits((long long)chunks, kFillChunk16)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(moedisp_probe_fill, dim3((unsigned)chunks), dim3(kFillChunk16), 0, stream, dst,
+                       (uint64_t)chunks, (uint64_t)mult);
+    return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
     const size_t n = bytes / 4;

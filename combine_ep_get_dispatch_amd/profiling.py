@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
 KERNELS = ("moedisp_layout", "moedisp_layout_reduce", "moedisp_count", "moedisp_scatter", "moedisp_scatter_quant", "moedisp_combine",
-           "moedisp_probe_copy")
+           "moedisp_probe_copy", "moedisp_probe_fill")
 _NAME = re.compile(r"\b(moedisp_\w+?)(<[^>(]*>)?\(")
 
 

@@ -229,6 +229,10 @@ def test_host_checks_misc(lib):
     assert lib.ep_workspace_init(p(4), 1 << 20, None) == B.ERR_MISALIGNED
     assert lib.ep_probe_copy(p(), p(), 15, None) == B.ERR_UNSUPPORTED
     assert lib.ep_probe_copy(p(4), p(), 16, None) == B.ERR_MISALIGNED
+    assert lib.ep_probe_fill(None, 4096, 0, None) == B.ERR_INVALID_ARG
+    assert lib.ep_probe_fill(p(), 4095, 0, None) == B.ERR_UNSUPPORTED
+    assert lib.ep_probe_fill(p(), 4096, 2, None) == B.ERR_UNSUPPORTED
+    assert lib.ep_probe_fill(p(8), 4096, 1, None) == B.ERR_MISALIGNED
     for code in (0, -1, -2, -3, -4, -5):
         assert M.ep_status_string(code) != "unknown status"
     assert M.ep_status_string(-99) == "unknown status"

@@ -205,6 +205,21 @@ def test_bad_handle_is_reported_and_skipped(dev):
     assert bufs.status() & M.binding.DEV_BAD_HANDLE
 
 
+@pytest.mark.parametrize("shuffled", [False, True])
+def test_probe_fill(dev, shuffled):
+    """Every 16-byte unit i is written exactly with {i, i >> 32, ~i, 0x5EED},
+    in either chunk order (a chunk the permutation missed would stay zero)."""
+    n = 2 * 32768 * 14336  # 917504 KiB: 229376 chunks of 4 KiB
+    dst = torch.zeros(n // 4, dtype=torch.int32, device=dev)
+    M.ep_probe_fill(dst, n, shuffled)
+    torch.cuda.synchronize()
+    i = torch.arange(n // 16, dtype=torch.int64, device=dev)
+    lo = (i & 0xFFFFFFFF).to(torch.int64)
+    want = torch.stack([lo, i >> 32, lo ^ 0xFFFFFFFF, torch.full_like(i, 0x5EED)], dim=1)
+    want = torch.where(want >= 2**31, want - 2**32, want).to(torch.int32)
+    assert torch.equal(dst.view(-1, 4), want)
+
+
 def test_probe_copy(dev):
     n = 64 << 20
     src = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
