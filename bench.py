@@ -1,21 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of one GPU's share of MoE EP layout -> dispatch -> combine.
 
-One step = ep_get_dispatch_layout + ep_dispatch (called as its two phases,
-ep_dispatch_notify and ep_dispatch_scatter) + ep_combine (bf16 out) over one
-batch of the DeepSeek-V3-shaped prefill workload (T=4096 tokens, H=7168 bf16,
-E=256 experts in G=8 groups, top-8, uniform routing).  Inputs and the
-stand-in expert outputs are resident in HBM before the timed region; the
-timed region is exactly K steps between two device synchronisations.  HIP
-events on the launch stream bracket the scatter and the combine kernels of
-every timed step (timing-only events without the system-scope cache fence,
+One step = ep_get_dispatch_layout_notify (the layout and the dispatch's
+notify phase of the same routing) + ep_dispatch_scatter + ep_combine (bf16
+out) over one batch of the DeepSeek-V3-shaped prefill workload (T=4096
+tokens, H=7168 bf16, E=256 experts in G=8 groups, top-8, uniform routing).
+Inputs and the stand-in expert outputs are resident in HBM before the timed
+region; the timed region is exactly K steps between two device
+synchronisations.  HIP events on the launch stream bracket the scatter kernel
+of every timed step (timing-only events without the system-scope cache fence,
 which a default event adds between the kernels it separates); the dominant
 kernel's algorithmic bytes over its mean duration give the roofline entry,
 with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
-when they were taken on the current kernel sources.  A second, untimed pass
-of K steps with events between every call gives the layout and notify
-phases.  The CPU oracle, timed on
-a bounded sample of the same workload on the host, is the reported baseline.
+when they were taken on the current kernel sources.  Untimed passes of K
+steps give the other phases: the separate calls (ep_get_dispatch_layout,
+ep_dispatch_notify, ep_dispatch_scatter, ep_combine) with events between every
+call, and the fused layout + notify call alone.  The CPU oracle, timed on a
+bounded sample of the same workload on the host, is the reported baseline.
 
 Further legs, reported beside the headline (each can be skipped): the other
 workloads (skewed routing, fp8 decode, Mixtral shape), quantise-on-dispatch
@@ -135,10 +136,23 @@ def run_gpu(cid, steps, warmup, dev):
 
     stream = torch.cuda.current_stream()
 
-    # one step = layout, dispatch (its two phases: notify = count kernel,
-    # scatter = scatter kernel), combine.  `ev` holds events recorded at the
-    # positions named in `at` (0 before the layout, 1 before notify, 2 before
-    # the scatter, 3 before the combine, 4 after it).
+    # The timed step: ep_get_dispatch_layout_notify (the layout and the
+    # dispatch's notify phase of the same routing, in two launches where the
+    # shape allows), ep_dispatch_scatter, ep_combine.  `ev` (optional) gets
+    # events before and after the scatter, the dominant kernel.
+    def step_fused(ev=None):
+        bufs.layout_notify(idx, stream)
+        if ev is not None:
+            ev[0].record(stream)
+        bufs.dispatch_scatter(x, xs, idx, w, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+
+    # The same step with the layout and the notify phase as separate calls,
+    # for the per-phase times (untimed passes).  `ev` holds events recorded at
+    # the positions named in `at` (0 before the layout, 1 before notify, 2
+    # before the scatter, 3 before the combine, 4 after it).
     def step(ev=None, at=()):
         if 0 in at:
             ev[0].record(stream)
@@ -156,23 +170,23 @@ def run_gpu(cid, steps, warmup, dev):
             ev[4].record(stream)
 
     for _ in range(warmup):
-        step()
+        step_fused()
     torch.cuda.synchronize()
-    # timed region: events bracket the scatter and the combine of every step
-    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
+    # timed region: events bracket the scatter of every step
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i], (2, 3, 4))
+        step_fused(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = bufs.status()
     if st:
         raise RuntimeError(f"device status {st} after timed steps on config {cid}")
     elapsed = t1 - t0
-    sct = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3  # us
-    com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
-    # untimed pass: events between every call, for the layout and notify phases
+    sct = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
+    # untimed pass: the separate calls with events between every call, for the
+    # layout, notify and combine phases
     evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
@@ -183,6 +197,18 @@ def run_gpu(cid, steps, warmup, dev):
         raise RuntimeError(f"device status {st} after the phase pass on config {cid}")
     lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
+    # untimed pass: the fused layout + notify call alone
+    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        evs[i][0].record(stream)
+        bufs.layout_notify(idx, stream)
+        evs[i][1].record(stream)
+        bufs.dispatch_scatter(x, xs, idx, w, stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+    torch.cuda.synchronize()
+    lnt = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     dis = ntf + sct
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
@@ -193,7 +219,7 @@ def run_gpu(cid, steps, warmup, dev):
         ms_per_step=ms_step, tokens_per_s=wl.T / (ms_step * 1e-3),
         step_gbps=B["step"] / (ms_step * 1e-3) / 1e9,
         layout_us=float(lay.mean()), dispatch_us=float(dis.mean()), combine_us=float(com.mean()),
-        notify_us=float(ntf.mean()), scatter_us=float(sct.mean()),
+        notify_us=float(ntf.mean()), scatter_us=float(sct.mean()), layout_notify_us=float(lnt.mean()),
         dispatch_us_min=float(dis.min()), combine_us_min=float(com.min()),
         dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
         combine_gbps=B["combine"] / (com.mean() * 1e-6) / 1e9,
@@ -575,13 +601,15 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, uniform top-k routing, softmax weights)",
         "config": {"workload": main_res["workload"], "T": main_res["T"], "H": main_res["H"], "E": main_res["E"],
                    "G": main_res["G"], "k": main_res["k"], "x_dtype": main_res["x_dtype"],
-                   "routing": main_res["routing"], "step": "layout+dispatch+combine", "parallelism": "none"},
+                   "routing": main_res["routing"], "step": "layout_notify+dispatch_scatter+combine",
+                   "parallelism": "none"},
         "hbm_gbps_step": main_res["step_gbps"],
         "hbm_frac_step": main_res["step_gbps"] / HBM_PEAK_GBPS,
         "dispatch_combine": {"us": main_res["dispatch_us"] + main_res["combine_us"],
                              "tokens_per_s": main_res["dc_tokens_per_s"], "gbps": main_res["dc_gbps"],
                              "frac": main_res["dc_frac"]},
-        "phases_us": {"layout": main_res["layout_us"], "dispatch": main_res["dispatch_us"],
+        "phases_us": {"layout_notify": main_res["layout_notify_us"], "layout": main_res["layout_us"],
+                      "dispatch": main_res["dispatch_us"],
                       "dispatch_notify": main_res["notify_us"], "dispatch_scatter": main_res["scatter_us"],
                       "combine": main_res["combine_us"], "dispatch_min": main_res["dispatch_us_min"],
                       "combine_min": main_res["combine_us_min"]},

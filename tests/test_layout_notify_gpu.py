@@ -45,7 +45,7 @@ def run_layout_notify(orc, wl, dev):
     assert st == (o["status"] | o["layout_status"]), f"device status {st} != oracle {o['status']}|{o['layout_status']}"
     g, _ = GH.fetch_dispatch(bufs, wl)
     GH.assert_dispatch_equal(g, o, wl)
-    return bufs, inp
+    return bufs, inp, o
 
 
 CASES = {
@@ -73,6 +73,27 @@ def test_layout_notify_parity(orc, dev, name):
     _say(f"[layout_notify] {name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k}")
     run_layout_notify(orc, wl, dev)
     _say(f"[layout_notify] {name} ok")
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_layout_notify_full_size(orc, dev, cid):
+    """The benchmark's call sequence at full size: layout_notify, scatter and
+    combine; dispatch bit-exact, combine to the bar on a seeded sample of
+    tokens (the last token always included)."""
+    wl = W.config(cid)
+    _say(f"[layout_notify-full] config {cid} {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k}")
+    bufs, _, o = run_layout_notify(orc, wl, dev)
+    R = int(o["expert_offsets"][-1])
+    eo_bits = GH.oracle_expert_out(wl, o)
+    eo = GH.upload_expert_out(eo_bits, wl.T * wl.k, wl.H, dev)
+    g32, g16, st = GH.gpu_combine(bufs, eo, wl, dev)
+    assert st == 0
+    rng = np.random.default_rng(cid)
+    toks = np.sort(rng.choice(wl.T, size=256, replace=False))
+    toks[-1] = wl.T - 1
+    o32, o16 = orc.combine(eo_bits, o["recv_weights"][:R], o["slot_to_row"][toks])
+    r = GH.assert_combine_close(g32[toks], g16[toks], o32, o16)
+    _say(f"[layout_notify-full] config {cid} ok R={R} max_ulp={r['max_ulp']}")
 
 
 def test_layout_notify_bad_and_repeated_ids(orc, dev):
