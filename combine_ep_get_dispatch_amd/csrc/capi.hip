@@ -28,6 +28,8 @@ static int check_shape(const moedisp_shape* s) {
         return MOEDISP_ERR_UNSUPPORTED;
     }
     if (row_bytes(*s) % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    // row byte offsets are 32-bit inside the kernels (buffer descriptors)
+    if (row_bytes(*s) >= (1ull << 31)) return MOEDISP_ERR_UNSUPPORTED;
     // receive row indices (T*k of them) are int32 with headroom
     const long long cap = (long long)s->num_tokens * s->topk;
     if (cap >= (1ll << 30)) return MOEDISP_ERR_UNSUPPORTED;

@@ -49,6 +49,8 @@ def test_workspace_bytes(lib):
     assert M.ep_workspace_bytes(shape(E=255)) == 0          # E % G != 0
     assert M.ep_workspace_bytes(shape(G=64, E=256)) == 0    # more groups than bitmap bits
     assert M.ep_workspace_bytes(shape(H=7)) == 0            # row not whole 16-byte units
+    assert M.ep_workspace_bytes(shape(T=8, H=1 << 30)) == 0  # 2 GiB rows: 32-bit row offsets
+    assert M.ep_workspace_bytes(shape(T=8, H=(1 << 30) - 8)) > 0
     assert M.ep_workspace_bytes(shape(dt=M.FP8_E4M3, sb=128)) > 0
     assert M.ep_workspace_bytes(shape(dt=M.FP8_E4M3, sb=100)) == 0
 

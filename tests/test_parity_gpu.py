@@ -86,6 +86,10 @@ EDGE = {
     "ragged_columns_k8": lambda: W.make_workload("ragged_cols_k8", 300, 7000, 64, 8, 8, seed=58),
     "ragged_columns_k4": lambda: W.make_workload("ragged_cols_k4", 200, 7000, 32, 4, 4, seed=59, mask_frac=0.2),
     "ragged_columns_k5": lambda: W.make_workload("ragged_cols_k5", 150, 7000, 40, 5, 5, seed=60, routing="zipf"),
+    # 2500 units per row and enough tokens that rows are not split into
+    # column ranges: more than one pass of the scatter's widest workgroup
+    # (1024 lanes x 2 units), with a ragged last pass
+    "wide_rows": lambda: W.make_workload("wide_rows", 1024, 20000, 16, 4, 4, seed=61),
 }
 
 
