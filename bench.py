@@ -15,8 +15,11 @@ with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
 when they were taken on the current kernel sources.  Untimed passes of K
 steps give the other phases: the separate calls (ep_get_dispatch_layout,
 ep_dispatch_notify, ep_dispatch_scatter, ep_combine) with events between every
-call, and the fused layout + notify call alone.  The CPU oracle, timed on a
-bounded sample of the same workload on the host, is the reported baseline.
+call, the fused layout + notify call alone, and a cold pass that writes
+512 MiB before each step (back to back, the source rows stay in the 256 MB
+MALL from one step to the next; the cold pass reports the step with nothing
+of its inputs cached).  The CPU oracle, timed on a bounded sample of the same
+workload on the host, is the reported baseline.
 
 Further legs, reported beside the headline (each can be skipped): the other
 workloads (skewed routing, fp8 decode, Mixtral shape), quantise-on-dispatch
@@ -44,6 +47,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at T=4096 H=7168 E=256 k=8"
+COLD_FLUSH_BYTES = 512 << 20  # written before each step of the cold pass: twice the MALL
 
 
 def log(msg):
@@ -107,8 +111,9 @@ def shape_of(M, W, wl):
     return M.moedisp_shape.make(wl.T, wl.H, wl.E, wl.G, wl.k, dt, wl.scale_block)
 
 
-def run_gpu(cid, steps, warmup, dev):
-    """Time `steps` layout+dispatch+combine steps of config `cid`."""
+def run_gpu(cid, steps, warmup, dev, cold=True):
+    """Time `steps` layout+dispatch+combine steps of config `cid` (and, with
+    `cold`, the cold pass)."""
     import torch
     import combine_ep_get_dispatch_amd as M
     from combine_ep_get_dispatch_amd import workloads as W
@@ -209,6 +214,30 @@ def run_gpu(cid, steps, warmup, dev):
         bufs.combine(eo, out, M.BF16, True, stream)
     torch.cuda.synchronize()
     lnt = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    # untimed pass, cold: 512 MiB written before each step, so nothing of the
+    # step's inputs is left in the 256 MB MALL or the L2s (back to back, the
+    # source rows x stay in the MALL from one step to the next)
+    flush = torch.empty(COLD_FLUSH_BYTES if cold else 0, dtype=torch.uint8, device=dev)
+    n_cold = min(steps, 50) if cold else 0
+    evs = [[TimingEvent() for _ in range(4)] for _ in range(n_cold)]
+    torch.cuda.synchronize()
+    for i in range(n_cold):
+        flush.zero_()
+        evs[i][0].record(stream)
+        bufs.layout_notify(idx, stream)
+        evs[i][1].record(stream)
+        bufs.dispatch_scatter(x, xs, idx, w, stream)
+        evs[i][2].record(stream)
+        bufs.combine(eo, out, M.BF16, True, stream)
+        evs[i][3].record(stream)
+    torch.cuda.synchronize()
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} after the cold pass on config {cid}")
+    cold_lnt = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    cold_sct = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    cold_com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
+    del flush
     dis = ntf + sct
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
@@ -228,6 +257,15 @@ def run_gpu(cid, steps, warmup, dev):
     )
     res["dc_gbps"] = B["dispatch_combine"] / ((dis.mean() + com.mean()) * 1e-6) / 1e9
     res["dc_frac"] = res["dc_gbps"] / HBM_PEAK_GBPS
+    sc_bytes = B["dispatch"] - B["notify"] + B["combine"]
+    res["cold"] = None if not n_cold else dict(
+        flush_bytes=COLD_FLUSH_BYTES, steps=n_cold,
+        layout_notify_us=float(cold_lnt.mean()), scatter_us=float(cold_sct.mean()),
+        combine_us=float(cold_com.mean()),
+        step_us=float((cold_lnt + cold_sct + cold_com).mean()),
+        tokens_per_s=wl.T / ((cold_lnt + cold_sct + cold_com).mean() * 1e-6),
+        scatter_combine_frac=sc_bytes / ((cold_sct.mean() + cold_com.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+    )
     del bufs, eo, out, x, xs, idx, w
     torch.cuda.empty_cache()
     return res
@@ -513,6 +551,8 @@ def main():
     ap.add_argument("--no-quant", action="store_true", help="skip the quantise-on-dispatch timings")
     ap.add_argument("--no-groups", action="store_true", help="skip the group-deduplicated path timings")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-latency timings")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold passes (512 MiB written before each step)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -527,7 +567,7 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     log(f"[bench] config {args.config}: {args.warmup} warmup + {args.steps} timed steps")
-    main_res = run_gpu(args.config, args.steps, args.warmup, dev)
+    main_res = run_gpu(args.config, args.steps, args.warmup, dev, cold=not args.no_cold)
     log(f"[bench] config {args.config}: {main_res['ms_per_step']*1e3:.1f} us/step, "
         f"dispatch {main_res['dispatch_us']:.1f} us, combine {main_res['combine_us']:.1f} us")
 
@@ -537,11 +577,11 @@ def main():
             if cid == args.config:
                 continue
             log(f"[bench] config {cid}")
-            r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev)
+            r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev, cold=not args.no_cold)
             others[r["workload"]] = {k: r[k] for k in ("T", "H", "E", "G", "k", "x_dtype", "routing", "R",
                                                        "tokens_per_s", "dc_tokens_per_s", "dc_gbps", "dc_frac",
                                                        "layout_us", "dispatch_us", "combine_us",
-                                                       "dispatch_gbps", "combine_gbps")}
+                                                       "dispatch_gbps", "combine_gbps", "cold")}
     quant = {}
     if not args.no_quant:
         import combine_ep_get_dispatch_amd as M
@@ -614,6 +654,7 @@ def main():
                       "combine": main_res["combine_us"], "dispatch_min": main_res["dispatch_us_min"],
                       "combine_min": main_res["combine_us_min"]},
         "phases_gbps": {"dispatch": main_res["dispatch_gbps"], "combine": main_res["combine_gbps"]},
+        "cold": main_res["cold"],
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": dom_us},

@@ -56,14 +56,14 @@ static void group_index_constants(int per_group, int* shift, uint32_t* magic) {
 
 // Scatter plan for rows of `units` lane units whose k copies write
 // `write_per_token` bytes; column ranges are whole multiples of `align` units;
-// a lane takes up to `max_per_lane` units per pass.
+// a lane takes up to `max_per_lane` units per pass; a workgroup copies tokens
+// until it stores at least `wg_bytes`.
 static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_token, int units, int align,
-                                 int max_per_lane) {
+                                 int max_per_lane, long long wg_bytes) {
     DispatchPlan p;
     const int T = s.num_tokens, k = s.topk;
-    // copy: >= 64 KiB of row stores per workgroup
     int bt = 1;
-    while (bt < kMaxBlockTokens && write_per_token * bt < 64 * 1024 && 2 * bt * k <= kMaxDispatchThreads) bt *= 2;
+    while (bt < kMaxBlockTokens && write_per_token * bt < wg_bytes && 2 * bt * k <= kMaxDispatchThreads) bt *= 2;
     // count tiles: 16 tokens (>= bt, as bt <= 16), doubled until there are at
     // most kMaxTiles (a slot's row sums one count per earlier tile); this
     // depends only on T and k
@@ -100,8 +100,16 @@ static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_tok
     return p;
 }
 
+// Copy workgroups of one token unless its k rows store less than 16 KiB:
+// more tokens per workgroup (the next token's row loaded while this one's is
+// stored) measured slower at T = 16384, H = 4096, k = 2 (4 tokens: +1.8 us
+// back to back, +14 us with the source rows not in the MALL) and no faster
+// at H = 7168, k = 8.
+constexpr long long kCopyWorkgroupBytes = 16 * 1024;
+
 DispatchPlan plan_dispatch(const moedisp_shape& s) {
-    return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1, 2);
+    return plan_scatter(s, (long long)s.topk * (long long)row_bytes(s), (int)(row_bytes(s) / 16), 1, 2,
+                        kCopyWorkgroupBytes);
 }
 
 // Group-deduplicated dispatch: the scatter over groups (k = E = G slots per
@@ -121,7 +129,8 @@ static DispatchPlan plan_group_permute(const moedisp_shape& s) {
     const moedisp_shape rs = group_rows_shape(s);
     const int per_row = (s.topk + (s.num_groups < s.topk ? s.num_groups : s.topk) - 1) /
                         (s.num_groups < s.topk ? s.num_groups : s.topk);
-    return plan_scatter(rs, (long long)per_row * (long long)row_bytes(rs), (int)(row_bytes(rs) / 16), 1, 2);
+    return plan_scatter(rs, (long long)per_row * (long long)row_bytes(rs), (int)(row_bytes(rs) / 16), 1, 2,
+                        64 * 1024);
 }
 
 // The group rows seen as tokens (T * min(G, k) of them, the capacity of the
@@ -136,7 +145,7 @@ moedisp_shape group_rows_shape(const moedisp_shape& s) {
 // bytes); column ranges are whole waves so that no scale block (<= 64 lanes)
 // straddles two of them.
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s) {
-    return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64, 1);
+    return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64, 1, kCopyWorkgroupBytes);
 }
 
 CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {
