@@ -255,6 +255,14 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
         dc_tokens_per_s=wl.T / ((dis.mean() + com.mean()) * 1e-6),
         bytes=B,
     )
+    # the pages' own byte conventions, for context: tokens x hidden per phase
+    # (their bench's per-rank count) and one row per routed copy
+    tok_row = wl.T * wl.H * x_elt
+    res["pages_convention_gbps"] = dict(
+        tokens_x_hidden=dict(dispatch=tok_row / (dis.mean() * 1e-6) / 1e9,
+                             combine=wl.T * wl.H * 2 / (com.mean() * 1e-6) / 1e9),
+        routed_rows_x_hidden=dict(dispatch=R * wl.H * x_elt / (dis.mean() * 1e-6) / 1e9,
+                                  combine=R * wl.H * 2 / (com.mean() * 1e-6) / 1e9))
     res["dc_gbps"] = B["dispatch_combine"] / ((dis.mean() + com.mean()) * 1e-6) / 1e9
     res["dc_frac"] = res["dc_gbps"] / HBM_PEAK_GBPS
     sc_bytes = B["dispatch"] - B["notify"] + B["combine"]
@@ -655,6 +663,7 @@ def main():
                       "combine_min": main_res["combine_us_min"]},
         "phases_gbps": {"dispatch": main_res["dispatch_gbps"], "combine": main_res["combine_gbps"]},
         "cold": main_res["cold"],
+        "pages_convention_gbps": main_res["pages_convention_gbps"],
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
                      "kernel_us": dom_us},

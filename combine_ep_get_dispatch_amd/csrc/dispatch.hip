@@ -31,10 +31,11 @@
 // The scatter then streams: each lane loads U 16-byte units of the source row
 // (U = 2 for column ranges of 512 units or more, such as the 448 lanes of a
 // 7168-wide bf16 row, else 1; up to 1024 lanes per workgroup) once - the first pass is
-// issued before the row computation - and stores them,
-// non-temporally, to each of the token's k destination rows (a token with no
-// receive row, such as a padding group row, is neither loaded past the first
-// pass nor stored).  Workgroups of
+// issued before the row computation - and stores them with the streaming
+// (sc0 sc1 nt) buffer store to each of the token's k destination rows (a
+// token with no receive row, such as a padding group row, is neither loaded
+// past the first pass nor stored).  The source loads stay plain: back to back
+// they hit the MALL, and non-temporal ones measured much slower.  Workgroups of
 // column range 0 write the handle (slot_to_row, recv_src_idx, recv_weights)
 // and fp8 scales.  Rows outside their expert's segment (or the buffer) are not
 // written and raise BAD_LAYOUT; workgroup 0 also checks that the routed slots
