@@ -15,7 +15,7 @@ with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
 when they were taken on the current kernel sources.  Untimed passes of K
 steps give the other phases: the separate calls (ep_get_dispatch_layout,
 ep_dispatch_notify, ep_dispatch_scatter, ep_combine) with events between every
-call, the fused layout + notify call alone, and a cold pass that reads
+call, full steps timing the fused layout + notify call, and a cold pass that reads
 512 MiB before each step (back to back, the source rows stay in the 256 MB
 MALL from one step to the next; the cold pass reports the step with nothing
 of its inputs cached).  The CPU oracle, timed on a bounded sample of the same
@@ -203,7 +203,8 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
     lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
     com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
-    # untimed pass: the fused layout + notify call alone
+    # untimed pass: full steps, with events around the fused layout + notify
+    # call only
     evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
