@@ -534,7 +534,7 @@ def cpu_baseline(budget_s: float = 12.0):
     del d
     times = []
     t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 8):
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 20):
         t0 = time.perf_counter()
         orc.layout(wl.topk_idx, wl.E, wl.G)
         dd = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
