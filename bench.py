@@ -15,7 +15,10 @@ with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
 when they were taken on the current kernel sources.  Untimed passes of K
 steps give the other phases: the separate calls (ep_get_dispatch_layout,
 ep_dispatch_notify, ep_dispatch_scatter, ep_combine) with events between every
-call, full steps timing the fused layout + notify call, and a cold pass that reads
+call, the same calls with events only around dispatch + combine (the
+dispatch_combine figure: the events between the calls add their own time to
+each phase), full steps timing the fused layout + notify call, and a cold
+pass that reads
 512 MiB before each step (back to back, the source rows stay in the 256 MB
 MALL from one step to the next; the cold pass reports the step with nothing
 of its inputs cached).  The CPU oracle, timed on a bounded sample of the same
@@ -203,6 +206,18 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
     lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
     ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
     com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
+    # untimed pass: dispatch + combine as one block, events only before the
+    # notify phase and after the combine (events between the calls add their
+    # own time to each phase)
+    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i], (1, 4))
+    torch.cuda.synchronize()
+    st = bufs.status()
+    if st:
+        raise RuntimeError(f"device status {st} after the dispatch + combine pass on config {cid}")
+    dcb = np.array([e[1].elapsed_time(e[4]) for e in evs]) * 1e3
     # untimed pass: full steps, with events around the fused layout + notify
     # call only
     evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
@@ -257,7 +272,9 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
         dispatch_us_min=float(dis.min()), combine_us_min=float(com.min()),
         dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
         combine_gbps=B["combine"] / (com.mean() * 1e-6) / 1e9,
-        dc_tokens_per_s=wl.T / ((dis.mean() + com.mean()) * 1e-6),
+        dc_us=float(dcb.mean()), dc_us_min=float(dcb.min()),
+        dc_phase_sum_us=float(dis.mean() + com.mean()),
+        dc_tokens_per_s=wl.T / (dcb.mean() * 1e-6),
         bytes=B,
     )
     # the pages' own byte conventions, for context: tokens x hidden per phase
@@ -268,7 +285,7 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
                              combine=wl.T * wl.H * 2 / (com.mean() * 1e-6) / 1e9),
         routed_rows_x_hidden=dict(dispatch=R * wl.H * x_elt / (dis.mean() * 1e-6) / 1e9,
                                   combine=R * wl.H * 2 / (com.mean() * 1e-6) / 1e9))
-    res["dc_gbps"] = B["dispatch_combine"] / ((dis.mean() + com.mean()) * 1e-6) / 1e9
+    res["dc_gbps"] = B["dispatch_combine"] / (dcb.mean() * 1e-6) / 1e9
     res["dc_frac"] = res["dc_gbps"] / HBM_PEAK_GBPS
     sc_bytes = B["dispatch"] - B["notify"] + B["combine"]
     res["cold"] = None if not n_cold else dict(
@@ -592,7 +609,7 @@ def main():
             log(f"[bench] config {cid}")
             r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev, cold=not args.no_cold)
             others[r["workload"]] = {k: r[k] for k in ("T", "H", "E", "G", "k", "x_dtype", "routing", "R",
-                                                       "tokens_per_s", "dc_tokens_per_s", "dc_gbps", "dc_frac",
+                                                       "tokens_per_s", "dc_us", "dc_tokens_per_s", "dc_gbps", "dc_frac",
                                                        "layout_us", "dispatch_us", "combine_us",
                                                        "dispatch_gbps", "combine_gbps", "cold")}
     quant = {}
@@ -658,9 +675,9 @@ def main():
                    "parallelism": "none"},
         "hbm_gbps_step": main_res["step_gbps"],
         "hbm_frac_step": main_res["step_gbps"] / HBM_PEAK_GBPS,
-        "dispatch_combine": {"us": main_res["dispatch_us"] + main_res["combine_us"],
+        "dispatch_combine": {"us": main_res["dc_us"], "us_min": main_res["dc_us_min"],
                              "tokens_per_s": main_res["dc_tokens_per_s"], "gbps": main_res["dc_gbps"],
-                             "frac": main_res["dc_frac"]},
+                             "frac": main_res["dc_frac"], "phase_sum_us": main_res["dc_phase_sum_us"]},
         "phases_us": {"layout_notify": main_res["layout_notify_us"], "layout": main_res["layout_us"],
                       "dispatch": main_res["dispatch_us"],
                       "dispatch_notify": main_res["notify_us"], "dispatch_scatter": main_res["scatter_us"],
