@@ -138,6 +138,80 @@ def _check(call: str, rc: int):
         raise MoeDispError(call, rc, ep_status_string(rc))
 
 
+# Element types a row argument may be viewed as: the library reads raw bytes,
+# so a row buffer may be handed over as its element type or as bytes.
+_U16 = tuple(d for d in (getattr(torch, "uint16", None),) if d is not None)
+_I32 = (torch.int32,) + tuple(d for d in (getattr(torch, "uint32", None),) if d is not None)
+_ROWS_BF16 = (torch.bfloat16, torch.int16, torch.uint8) + _U16
+_ROWS_FP8 = (torch.uint8, torch.int8, torch.float8_e4m3fn)
+_F32 = (torch.float32,)
+_INT32 = (torch.int32,)
+_BYTES = None  # any element type (workspaces, probe buffers)
+
+
+class _Args:
+    """Checks of the tensor arguments of one call, before any pointer crosses
+    the C ABI: each tensor must have an accepted element type, be contiguous
+    and hold at least the bytes the shape needs (need), and every tensor must
+    be a GPU tensor (done, checked after all the others so that a host-memory
+    test sees each size and type check).  A failed check raises MoeDispError
+    (invalid argument): no kernel is ever handed a buffer smaller than the
+    shape says, or an int64 table read as int32."""
+
+    def __init__(self, call: str):
+        self.call = call
+        self.tensors = []
+
+    def fail(self, msg: str):
+        raise MoeDispError(self.call, ERR_INVALID_ARG, msg)
+
+    def need(self, name: str, t, dtypes, nbytes: int, optional: bool = False):
+        if t is None:
+            if optional or nbytes == 0:
+                return
+            self.fail(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            self.fail(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+        if dtypes is not None and t.dtype not in dtypes:
+            want = ", ".join(str(d).replace("torch.", "") for d in dtypes)
+            self.fail(f"{name} has dtype {str(t.dtype).replace('torch.', '')}, expected one of: {want}")
+        if not t.is_contiguous():
+            self.fail(f"{name} must be contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            self.fail(f"{name} holds {have} bytes, the shape needs {nbytes}")
+        self.tensors.append((name, t))
+
+    def done(self):
+        for name, t in self.tensors:
+            if t.device.type != "cuda":
+                self.fail(f"{name} is on {t.device}, expected a GPU tensor")
+
+
+def _dims(shape: moedisp_shape):
+    """(T, H, E, G, k, row bytes, fp32 scales per row) of a shape."""
+    T, H, E, G, k = shape.num_tokens, shape.hidden, shape.num_experts, shape.num_groups, shape.topk
+    fp8 = shape.x_dtype == FP8_E4M3
+    nsc = H // shape.scale_block if fp8 and shape.scale_block > 0 else 0
+    return max(T, 0), max(H, 0), max(E, 0), max(G, 0), max(k, 0), H * (1 if fp8 else 2), nsc
+
+
+def _rows_dtypes(shape: moedisp_shape):
+    return _ROWS_FP8 if shape.x_dtype == FP8_E4M3 else _ROWS_BF16
+
+
+def _out_dtypes(out_dtype: int):
+    return _F32 if out_dtype == FP32 else _ROWS_BF16
+
+
+def _ws(A: _Args, ws):
+    A.need("ws", ws, _BYTES, 1)
+
+
+def _nb(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def ep_status_string(code: int) -> str:
     return load().ep_status_string(code).decode()
 
@@ -147,121 +221,283 @@ def ep_workspace_bytes(shape: moedisp_shape) -> int:
 
 
 def ep_workspace_init(ws: torch.Tensor, stream=None):
-    _check("ep_workspace_init", load().ep_workspace_init(_p(ws), ws.numel() * ws.element_size(), _s(stream)))
+    A = _Args("ep_workspace_init")
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_workspace_init(_p(ws), _nb(ws), _s(stream)))
+
+
+def _need_layout(A, shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws):
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("tokens_per_group", tokens_per_group, _INT32, 4 * G)
+    A.need("is_token_in_group", is_token_in_group, _I32, 4 * T)
+    _ws(A, ws)
 
 
 def ep_get_dispatch_layout(shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws,
                            stream=None):
-    _check("ep_get_dispatch_layout", load().ep_get_dispatch_layout(
+    A = _Args("ep_get_dispatch_layout")
+    _need_layout(A, shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws)
+    A.done()
+    _check(A.call, load().ep_get_dispatch_layout(
         C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group),
-        _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_get_dispatch_layout_notify(shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group,
                                   expert_offsets, ws, stream=None):
-    _check("ep_get_dispatch_layout_notify", load().ep_get_dispatch_layout_notify(
+    A = _Args("ep_get_dispatch_layout_notify")
+    _need_layout(A, shape, topk_idx, tokens_per_expert, tokens_per_group, is_token_in_group, ws)
+    A.need("expert_offsets", expert_offsets, _INT32, 4 * (_dims(shape)[2] + 1))
+    A.done()
+    _check(A.call, load().ep_get_dispatch_layout_notify(
         C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group),
-        _p(expert_offsets), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(expert_offsets), _p(ws), _nb(ws), _s(stream)))
+
+
+def _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws):
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    cap = T * k
+    A.need("x", x, _rows_dtypes(shape), T * rb)
+    A.need("x_scales", x_scales, _F32, 4 * T * nsc, optional=nsc == 0)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("topk_weights", topk_weights, _F32, 4 * T * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("recv_x", recv_x, _rows_dtypes(shape), cap * rb)
+    A.need("recv_scales", recv_scales, _F32, 4 * cap * nsc, optional=nsc == 0)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * cap)
+    A.need("recv_weights", recv_weights, _F32, 4 * cap)
+    A.need("expert_offsets", expert_offsets, _INT32, 4 * (E + 1))
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
+    _ws(A, ws)
 
 
 def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales, recv_src_idx,
                 recv_weights, expert_offsets, slot_to_row, ws, stream=None):
-    _check("ep_dispatch", load().ep_dispatch(
+    A = _Args("ep_dispatch")
+    _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch(
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
         _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
-        ws.numel() * ws.element_size(), _s(stream)))
+        _nb(ws), _s(stream)))
 
 
 def ep_dispatch_notify(shape, topk_idx, tokens_per_expert, expert_offsets, ws, stream=None):
-    _check("ep_dispatch_notify", load().ep_dispatch_notify(
-        C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(expert_offsets), _p(ws),
-        ws.numel() * ws.element_size(), _s(stream)))
+    A = _Args("ep_dispatch_notify")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("expert_offsets", expert_offsets, _INT32, 4 * (E + 1))
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch_notify(
+        C.byref(shape), _p(topk_idx), _p(tokens_per_expert), _p(expert_offsets), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_dispatch_scatter(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
                         recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
-    _check("ep_dispatch_scatter", load().ep_dispatch_scatter(
+    A = _Args("ep_dispatch_scatter")
+    _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch_scatter(
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
         _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
-        ws.numel() * ws.element_size(), _s(stream)))
+        _nb(ws), _s(stream)))
+
+
+def _need_quant(A, shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
+                recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws):
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    cap = T * k
+    blocks = H // int(quant_block) if int(quant_block) > 0 else 0
+    A.need("x", x, _ROWS_BF16, T * H * 2)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("topk_weights", topk_weights, _F32, 4 * T * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("recv_x", recv_x, _ROWS_FP8, cap * H)
+    if int(scale_fmt) == SCALE_FP32:
+        A.need("recv_scales", recv_scales, _F32, 4 * cap * blocks)
+    else:
+        A.need("recv_scales", recv_scales, (torch.uint8, torch.int8), cap * blocks)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * cap)
+    A.need("recv_weights", recv_weights, _F32, 4 * cap)
+    A.need("expert_offsets", expert_offsets, _INT32, 4 * (E + 1))
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
+    _ws(A, ws)
 
 
 def ep_dispatch_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
                       recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
-    _check("ep_dispatch_quant", load().ep_dispatch_quant(
+    A = _Args("ep_dispatch_quant")
+    _need_quant(A, shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch_quant(
         C.byref(shape), int(quant_block), int(scale_fmt), _p(x), _p(topk_idx), _p(topk_weights),
         _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
-        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_dispatch_scatter_quant(shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
                               recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws,
                               stream=None):
-    _check("ep_dispatch_scatter_quant", load().ep_dispatch_scatter_quant(
+    A = _Args("ep_dispatch_scatter_quant")
+    _need_quant(A, shape, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch_scatter_quant(
         C.byref(shape), int(quant_block), int(scale_fmt), _p(x), _p(topk_idx), _p(topk_weights),
         _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
-        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_layout_dispatch_small(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, tokens_per_group,
                              is_token_in_group, recv_x, recv_scales, recv_src_idx, recv_weights, expert_offsets,
                              slot_to_row, ws, stream=None):
-    _check("ep_layout_dispatch_small", load().ep_layout_dispatch_small(
+    A = _Args("ep_layout_dispatch_small")
+    _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws)
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    A.need("tokens_per_group", tokens_per_group, _INT32, 4 * G)
+    A.need("is_token_in_group", is_token_in_group, _I32, 4 * T)
+    A.done()
+    _check(A.call, load().ep_layout_dispatch_small(
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert),
         _p(tokens_per_group), _p(is_token_in_group), _p(recv_x), _p(recv_scales), _p(recv_src_idx),
-        _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_dispatch_groups(shape, x, x_scales, topk_idx, topk_weights, is_token_in_group, tokens_per_group, recv_x,
                        recv_scales, recv_src_idx, recv_topk_idx, recv_topk_weights, group_offsets, token_group_row, ws,
                        stream=None):
-    _check("ep_dispatch_groups", load().ep_dispatch_groups(
+    A = _Args("ep_dispatch_groups")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    cap = T * min(G, k)
+    A.need("x", x, _rows_dtypes(shape), T * rb)
+    A.need("x_scales", x_scales, _F32, 4 * T * nsc, optional=nsc == 0)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("topk_weights", topk_weights, _F32, 4 * T * k)
+    A.need("is_token_in_group", is_token_in_group, _I32, 4 * T)
+    A.need("tokens_per_group", tokens_per_group, _INT32, 4 * G)
+    A.need("recv_x", recv_x, _rows_dtypes(shape), cap * rb)
+    A.need("recv_scales", recv_scales, _F32, 4 * cap * nsc, optional=nsc == 0)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * cap)
+    A.need("recv_topk_idx", recv_topk_idx, _INT32, 4 * cap * k)
+    A.need("recv_topk_weights", recv_topk_weights, _F32, 4 * cap * k)
+    A.need("group_offsets", group_offsets, _INT32, 4 * (G + 1))
+    A.need("token_group_row", token_group_row, _INT32, 4 * T * G)
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_dispatch_groups(
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(is_token_in_group),
         _p(tokens_per_group), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_topk_idx),
-        _p(recv_topk_weights), _p(group_offsets), _p(token_group_row), _p(ws), ws.numel() * ws.element_size(),
-        _s(stream)))
+        _p(recv_topk_weights), _p(group_offsets), _p(token_group_row), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_group_permute(shape, group_x, group_scales, recv_topk_idx, recv_topk_weights, tokens_per_expert, recv_x,
                      recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, stream=None):
-    _check("ep_group_permute", load().ep_group_permute(
+    A = _Args("ep_group_permute")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    gr = T * min(G, k)  # group rows, each seen as a token of k slots
+    A.need("group_x", group_x, _rows_dtypes(shape), gr * rb)
+    A.need("group_scales", group_scales, _F32, 4 * gr * nsc, optional=nsc == 0)
+    A.need("recv_topk_idx", recv_topk_idx, _INT32, 4 * gr * k)
+    A.need("recv_topk_weights", recv_topk_weights, _F32, 4 * gr * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("recv_x", recv_x, _rows_dtypes(shape), T * k * rb)
+    A.need("recv_scales", recv_scales, _F32, 4 * T * k * nsc, optional=nsc == 0)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * T * k)
+    A.need("recv_weights", recv_weights, _F32, 4 * T * k)
+    A.need("expert_offsets", expert_offsets, _INT32, 4 * (E + 1))
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * gr * k)
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_group_permute(
         C.byref(shape), _p(group_x), _p(group_scales), _p(recv_topk_idx), _p(recv_topk_weights),
         _p(tokens_per_expert), _p(recv_x), _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets),
-        _p(slot_to_row), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
+
+
+def _out_bytes(rows: int, H: int, out_dtype: int) -> int:
+    return rows * H * (4 if int(out_dtype) == FP32 else 2)
 
 
 def ep_group_reduce(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, group_offsets, group_out, out_dtype,
                     ws, stream=None):
-    _check("ep_group_reduce", load().ep_group_reduce(
+    A = _Args("ep_group_reduce")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    gr = T * min(G, k)
+    A.need("expert_out", expert_out, _ROWS_BF16, T * k * H * 2)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * T * k, optional=True)
+    A.need("recv_weights", recv_weights, _F32, 4 * T * k)
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * gr * k)
+    A.need("group_offsets", group_offsets, _INT32, 4 * (G + 1))
+    A.need("group_out", group_out, _out_dtypes(int(out_dtype)), _out_bytes(gr, H, out_dtype))
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_group_reduce(
         C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(group_offsets),
-        _p(group_out), int(out_dtype), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        _p(group_out), int(out_dtype), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_combine_groups(shape, group_rows, recv_src_idx, token_group_row, out, out_dtype, ws, stream=None):
-    _check("ep_combine_groups", load().ep_combine_groups(
+    A = _Args("ep_combine_groups")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    gr = T * min(G, k)
+    A.need("group_rows", group_rows, _ROWS_BF16, gr * H * 2)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * gr, optional=True)
+    A.need("token_group_row", token_group_row, _INT32, 4 * T * G)
+    A.need("out", out, _out_dtypes(int(out_dtype)), _out_bytes(T, H, out_dtype))
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_combine_groups(
         C.byref(shape), _p(group_rows), _p(recv_src_idx), _p(token_group_row), _p(out), int(out_dtype), _p(ws),
-        ws.numel() * ws.element_size(), _s(stream)))
+        _nb(ws), _s(stream)))
 
 
 def ep_combine(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, out, out_dtype, ws, stream=None):
-    _check("ep_combine", load().ep_combine(
+    A = _Args("ep_combine")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    A.need("expert_out", expert_out, _ROWS_BF16, T * k * H * 2)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * T * k, optional=True)
+    A.need("recv_weights", recv_weights, _F32, 4 * T * k)
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
+    A.need("out", out, _out_dtypes(int(out_dtype)), _out_bytes(T, H, out_dtype))
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_combine(
         C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(out),
-        int(out_dtype), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+        int(out_dtype), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_check_status(ws, stream=None) -> int:
+    A = _Args("ep_check_status")
+    _ws(A, ws)
+    A.done()
     v = C.c_int32(0)
-    _check("ep_check_status", load().ep_check_status(_p(ws), ws.numel() * ws.element_size(), _s(stream),
-                                                     C.byref(v)))
+    _check(A.call, load().ep_check_status(_p(ws), _nb(ws), _s(stream), C.byref(v)))
     return int(v.value)
 
 
 def ep_probe_copy(dst, src, nbytes: int, stream=None):
-    _check("ep_probe_copy", load().ep_probe_copy(_p(dst), _p(src), int(nbytes), _s(stream)))
+    A = _Args("ep_probe_copy")
+    A.need("dst", dst, _BYTES, int(nbytes))
+    A.need("src", src, _BYTES, int(nbytes))
+    A.done()
+    _check(A.call, load().ep_probe_copy(_p(dst), _p(src), int(nbytes), _s(stream)))
 
 
 def ep_probe_fill(dst, nbytes: int, shuffled: bool = False, stream=None):
-    _check("ep_probe_fill", load().ep_probe_fill(_p(dst), int(nbytes), 1 if shuffled else 0, _s(stream)))
+    A = _Args("ep_probe_fill")
+    A.need("dst", dst, _BYTES, int(nbytes))
+    A.done()
+    _check(A.call, load().ep_probe_fill(_p(dst), int(nbytes), 1 if shuffled else 0, _s(stream)))
 
 
 class EpBuffers:

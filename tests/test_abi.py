@@ -244,3 +244,66 @@ def test_python_binding_raises_without_gpu_work(lib):
     s = shape(E=255)
     with pytest.raises(M.MoeDispError):
         B._check("ep_get_dispatch_layout", layout_rc(lib, s))
+
+
+def test_binding_rejects_bad_tensors_before_the_call():
+    """The Python binding checks every tensor against the shape before its
+    pointer reaches the library: element type, contiguity, size, device.  An
+    int64 routing table (torch.topk's index type), a strided view or a buffer
+    smaller than the shape needs raises MoeDispError; nothing is launched."""
+    import torch
+    s = shape(T=16, H=256, E=8, G=2, k=2)
+    T, H, E, G, k = 16, 256, 8, 2, 2
+    i32 = lambda n: torch.zeros(n, dtype=torch.int32)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8)
+
+    def layout(idx=None, tpe=None, tpg=None, bm=None):
+        M.ep_get_dispatch_layout(s, i32(T * k) if idx is None else idx, i32(E) if tpe is None else tpe,
+                                 i32(G) if tpg is None else tpg, i32(T) if bm is None else bm, ws)
+
+    def expect(fn, *words):
+        with pytest.raises(M.MoeDispError) as e:
+            fn()
+        assert e.value.code == B.ERR_INVALID_ARG
+        for w in words:
+            assert w in str(e.value), str(e.value)
+
+    expect(lambda: layout(idx=torch.zeros(T * k, dtype=torch.int64)), "topk_idx", "int64")
+    expect(lambda: layout(idx=i32(T * k - 1)), "topk_idx", "bytes")
+    expect(lambda: layout(idx=i32(2 * T * k)[::2]), "topk_idx", "contiguous")
+    expect(lambda: layout(tpe=i32(E - 1)), "tokens_per_expert")
+    expect(lambda: layout(idx=[0] * (T * k)), "torch.Tensor")
+    expect(lambda: layout(), "expected a GPU tensor")            # right sizes and types, but host memory
+
+    x = torch.zeros((T, H), dtype=torch.bfloat16)
+    def dispatch(**kw):
+        a = dict(x=x, x_scales=None, topk_idx=i32(T * k), topk_weights=f32(T * k), tokens_per_expert=i32(E),
+                 recv_x=torch.zeros((T * k, H), dtype=torch.bfloat16), recv_scales=None, recv_src_idx=i32(T * k),
+                 recv_weights=f32(T * k), expert_offsets=i32(E + 1), slot_to_row=i32(T * k), ws=ws)
+        a.update(kw)
+        M.ep_dispatch(s, **a)
+    expect(lambda: dispatch(x=torch.zeros((T, H), dtype=torch.float32)), "x", "float32")
+    expect(lambda: dispatch(recv_x=torch.zeros((T * k - 1, H), dtype=torch.bfloat16)), "recv_x", "bytes")
+    expect(lambda: dispatch(topk_weights=torch.zeros(T * k, dtype=torch.float64)), "topk_weights")
+    expect(lambda: dispatch(expert_offsets=i32(E)), "expert_offsets")
+    expect(lambda: dispatch(slot_to_row=None), "slot_to_row", "required")
+    expect(lambda: dispatch(), "expected a GPU tensor")
+
+    fp8 = shape(T=T, H=H, E=E, G=G, k=k, dt=M.FP8_E4M3, sb=128)
+    xq = torch.zeros((T, H), dtype=torch.uint8)
+    expect(lambda: M.ep_dispatch(fp8, xq, None, i32(T * k), f32(T * k), i32(E), torch.zeros((T * k, H), dtype=torch.uint8),
+                                 f32(T * k * 2), i32(T * k), f32(T * k), i32(E + 1), i32(T * k), ws),
+           "x_scales", "required")
+
+    eo = torch.zeros((T * k, H), dtype=torch.bfloat16)
+    def combine(out, out_dtype, eo=eo):
+        M.ep_combine(s, eo, None, f32(T * k), i32(T * k), out, out_dtype, ws)
+    # bf16 rows are too small for an fp32 output
+    expect(lambda: combine(torch.zeros((T, H), dtype=torch.bfloat16), M.FP32), "out", "bfloat16")
+    expect(lambda: combine(torch.zeros((T, H // 2), dtype=torch.float32), M.FP32), "out", "bytes")
+    expect(lambda: combine(torch.zeros((T, H), dtype=torch.bfloat16), M.BF16, eo=eo[:, : H // 2]), "expert_out")
+    expect(lambda: combine(torch.zeros((T, H), dtype=torch.bfloat16), M.BF16), "expected a GPU tensor")
+
+    expect(lambda: M.ep_probe_copy(torch.zeros(64, dtype=torch.uint8), torch.zeros(32, dtype=torch.uint8), 64),
+           "src", "bytes")
