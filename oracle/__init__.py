@@ -26,13 +26,38 @@ SCALE_UE8M0 = 1
 GCC_FLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
              "-Wall", "-Wextra"]
 
+# Address and undefined-behaviour sanitizers (host code only: the oracle is
+# plain C for the CPU).  Any report aborts the process.
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=all"]
 
-def compile_oracle(src: str, out: str) -> str:
-    """Compile one oracle source file into a shared library (single-threaded C)."""
+# Environment variable naming another oracle library to load instead of
+# liboracle.so (the sanitized build, for the sanitizer tests).
+LIB_ENV = "MOEDISP_ORACLE_LIB"
+
+
+def compile_oracle(src: str, out: str, sanitize: bool = False) -> str:
+    """Compile one oracle source file into a shared library (single-threaded C),
+    with the address and undefined-behaviour sanitizers if `sanitize`."""
     tmp = out + ".tmp"
-    subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+    flags = GCC_FLAGS + (SAN_FLAGS if sanitize else [])
+    subprocess.run(["gcc", *flags, "-o", tmp, src, "-lm"], check=True)
     os.replace(tmp, out)
     return out
+
+
+def sanitizer_env(lib: str) -> dict:
+    """Environment for a child Python process that loads the sanitized oracle
+    `lib`: the sanitizer runtime preloaded (it must come first in a process
+    whose main program is not instrumented), leak checks off (the interpreter
+    keeps its allocations at exit), and any report fatal."""
+    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                          check=True).stdout.strip()
+    env = dict(os.environ)
+    env.update({"LD_PRELOAD": asan, LIB_ENV: lib,
+                "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=0:exitcode=86",
+                "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1:exitcode=87"})
+    return env
 
 
 def build(force: bool = True) -> str:
@@ -255,9 +280,13 @@ def get() -> Oracle:
     """The oracle built from oracle.c (compiled on first use if missing)."""
     global _default
     if _default is None:
-        if not os.path.exists(LIB):
-            build()
-        _default = Oracle(LIB)
+        other = os.environ.get(LIB_ENV)
+        if other:
+            _default = Oracle(other)
+        else:
+            if not os.path.exists(LIB):
+                build()
+            _default = Oracle(LIB)
     return _default
 
 
