@@ -9,7 +9,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoedisp.so")
-SOURCES = ["capi.hip", "layout.hip", "dispatch.hip", "decode.hip", "combine.hip", "util.hip"]
+SOURCES = ["capi.hip", "layout.hip", "notify.hip", "dispatch.hip", "decode.hip", "combine.hip", "util.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -112,6 +112,49 @@ DispatchPlan plan_dispatch(const moedisp_shape& s) {
                         kCopyWorkgroupBytes);
 }
 
+// Receive rows per block-pull copy workgroup.  In the library's step at
+// T = 4096, H = 7168, k = 8 (notify, copy, combine) one row per workgroup
+// measured best both with nothing cached (copy 97 against 103 us for two
+// rows) and with the source rows in the MALL (96 against 95-100 us).
+#ifndef MOEDISP_PULL_ROWS_PER_WG
+#define MOEDISP_PULL_ROWS_PER_WG 1
+#endif
+
+// Block-pull plan: blocks of tb tokens whose source rows fit one XCD's L2,
+// as many blocks as XCDs or a multiple of it (every XCD gets the same number
+// of blocks; the last block may be shorter), each block sorted in LDS.
+PullPlan plan_pull(const moedisp_shape& s) {
+    PullPlan p;
+    memset(&p, 0, sizeof p);
+    const long long T = s.num_tokens, k = s.topk, E = s.num_experts;
+    const long long rb = (long long)row_bytes(s);
+    if (T <= 0 || E > kPullMaxExperts || rb <= 0) return p;
+    long long tbmax = kPullL2Bytes / rb;
+    if (tbmax > kPullMaxBlockSlots / k) tbmax = kPullMaxBlockSlots / k;
+    if (tbmax > 64 * (kPullMaskWords / E)) tbmax = 64 * (kPullMaskWords / E);  // token masks in LDS
+    if (tbmax < kPullMinBlockTokens) return p;
+    const long long rounds = (T + kXcds * tbmax - 1) / (kXcds * tbmax);
+    const long long tb = (T + kXcds * rounds - 1) / (kXcds * rounds);
+    const long long nblk = (T + tb - 1) / tb;
+    if (tb < kPullMinBlockTokens || nblk < kXcds || nblk > kPullMaxBlocks) return p;
+    const int row16 = (int)(rb / 16);
+    p.tb = (int)tb;
+    p.nblk = (int)nblk;
+    p.cap_b = (int)(tb * k);
+    p.cnt_stride = (p.nblk + 3) / 4 * 4;
+    p.units = 2;
+    int threads = ((row16 + p.units - 1) / p.units + 63) / 64 * 64;
+    if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
+    // an fp8 row's scales travel one per lane with the row
+    if (scales_per_row(s) > threads) return p;
+    p.threads = threads;
+    p.rpw = MOEDISP_PULL_ROWS_PER_WG;
+    p.wpb = (p.cap_b + p.rpw - 1) / p.rpw;
+    p.blocks = (long long)kXcds * p.wpb * ((p.nblk + kXcds - 1) / kXcds);
+    p.use = 1;
+    return p;
+}
+
 // Group-deduplicated dispatch: the scatter over groups (k = E = G slots per
 // token, from the layout's bitmap).
 static moedisp_shape group_shape(const moedisp_shape& s) {
@@ -189,7 +232,18 @@ WsPlan plan_workspace(const moedisp_shape& s) {
     const size_t rows = (size_t)plan_dispatch(group_rows_shape(s)).tile_stride * s.num_experts;
     size_t count_words = flat > groups ? flat : groups;
     if (rows > count_words) count_words = rows;
-    w.total = align256(w.counts_offset + count_words * sizeof(int32_t));
+    size_t end = align256(w.counts_offset + count_words * sizeof(int32_t));
+    // block-pull tables of the flat dispatch (the group paths use the push scatter)
+    const PullPlan pp = plan_pull(s);
+    w.pull_cnt_offset = w.pull_ls_offset = w.pull_n_offset = w.pull_ent_offset = end;
+    if (pp.use) {
+        w.pull_cnt_offset = end;
+        w.pull_ls_offset = align256(w.pull_cnt_offset + (size_t)s.num_experts * pp.cnt_stride * sizeof(int32_t));
+        w.pull_n_offset = align256(w.pull_ls_offset + (size_t)pp.nblk * s.num_experts * sizeof(int32_t));
+        w.pull_ent_offset = align256(w.pull_n_offset + (size_t)pp.nblk * sizeof(int32_t));
+        end = align256(w.pull_ent_offset + (size_t)pp.nblk * pp.cap_b * sizeof(PullEnt));
+    }
+    w.total = end;
     return w;
 }
 
@@ -271,6 +325,52 @@ int ep_get_dispatch_layout(const moedisp_shape* s, const int32_t* topk_idx, int3
     return hip_status(launch_layout(a, (hipStream_t)stream));
 }
 
+// The block-pull plan and tables of a flat dispatch (off: the push scatter).
+static void set_pull(DispatchArgs* a, const moedisp_shape& s, const WsPlan& w, void* ws, bool allow) {
+    memset(&a->pull, 0, sizeof a->pull);
+    a->pull_cnt = a->pull_ls = a->pull_n = nullptr;
+    a->pull_ent = nullptr;
+    if (!allow) return;
+    a->pull = plan_pull(s);
+    if (!a->pull.use) return;
+    a->pull_cnt = (int32_t*)((char*)ws + w.pull_cnt_offset);
+    a->pull_ls = (int32_t*)((char*)ws + w.pull_ls_offset);
+    a->pull_n = (int32_t*)((char*)ws + w.pull_n_offset);
+    a->pull_ent = (PullEnt*)((char*)ws + w.pull_ent_offset);
+}
+
+static int id_bits_of(int E) {
+    int b = 0;
+    while ((1 << b) < E) ++b;
+    return b;
+}
+
+// The notify launch of a block-pull dispatch: every block sorted, and
+// expert_offsets scanned from tokens_per_expert.  With `tiles`, every
+// dispatch tile is counted too (the push path's table, which the quantising
+// scatter reads after a separate notify phase), tile 0 writing the offsets.
+static hipError_t launch_pull_notify(const DispatchArgs& a, bool tiles, hipStream_t stream) {
+    NotifyArgs n;
+    memset(&n, 0, sizeof n);
+    n.d = a;
+    n.id_bits = id_bits_of(a.E);
+    n.sort_wgs = a.pull.nblk;
+    n.count_wgs = tiles ? a.plan.tiles : 0;
+    n.count_offsets = tiles ? 1 : 0;
+    n.reduce = tiles ? 0 : 2;
+    return launch_notify(n, stream);
+}
+
+// `tiles`: the phase may be followed by the quantising scatter (a separate
+// notify call), which reads the per-tile counts.
+static hipError_t launch_notify_phase(const DispatchArgs& a, bool tiles, hipStream_t stream) {
+    return a.pull.use ? launch_pull_notify(a, tiles, stream) : launch_dispatch_notify(a, stream);
+}
+
+static hipError_t launch_scatter_phase(const DispatchArgs& a, hipStream_t stream) {
+    return a.pull.use ? launch_scatter_pull(a, stream) : launch_dispatch_scatter(a, stream);
+}
+
 // Checks shared by the dispatch calls; fills the launch arguments.  Pointers
 // a phase does not use may be passed as NULL-equivalents by the caller of that
 // phase only through the phase-specific wrappers below.
@@ -280,7 +380,7 @@ static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_s
                          const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x,
                          float* recv_scales, int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                          int32_t* slot_to_row, void* ws, size_t ws_bytes, bool scatter, DispatchArgs* a,
-                         const moedisp_shape* ws_shape = nullptr) {
+                         const moedisp_shape* ws_shape = nullptr, bool allow_pull = true) {
     int st = check_shape(s);
     if (st) return st;
     const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
@@ -327,16 +427,18 @@ static int dispatch_args(const moedisp_shape* s, const void* x, const float* x_s
     a->slot_to_row = slot_to_row;
     a->hdr = (WsHeader*)ws;
     a->tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+    set_pull(a, *s, w, ws, allow_pull && ws_shape == s);
     return MOEDISP_OK;
 }
 
 int ep_dispatch_notify(const moedisp_shape* s, const int32_t* topk_idx, const int32_t* tokens_per_expert,
                        int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     const int st = dispatch_args(s, nullptr, nullptr, topk_idx, nullptr, tokens_per_expert, nullptr, nullptr, nullptr,
                                  nullptr, expert_offsets, nullptr, ws, ws_bytes, false, &a);
     if (st) return st;
-    return hip_status(launch_dispatch_notify(a, (hipStream_t)stream));
+    return hip_status(launch_notify_phase(a, true, (hipStream_t)stream));
 }
 
 // LDS a layout workgroup may use with the notify phase folded in.
@@ -358,11 +460,49 @@ int ep_get_dispatch_layout_notify(const moedisp_shape* s, const int32_t* topk_id
     const int tpb = a.tokens_per_block;
     const bool fused = s->num_tokens > 0 && (1 << shift) == P.tile_tokens && tpb % P.tile_tokens == 0 &&
                        layout_lds_bytes(a.E, a.G, a.k, tpb, tpb / P.tile_tokens) <= kLayoutNotifyLds;
+    const WsPlan w = plan_workspace(*s);
+    if (plan_pull(*s).use) {
+        // block-pull: the layout's partial counts (with the dispatch tiles'
+        // counts where they lie inside its workgroups) and the block sort in
+        // one launch, then the reduce of the partials (and the remaining
+        // tiles' counts)
+        DispatchArgs d;
+        if ((st = dispatch_args(s, nullptr, nullptr, topk_idx, nullptr, tokens_per_expert, nullptr, nullptr, nullptr,
+                                nullptr, expert_offsets, nullptr, ws, ws_bytes, false, &d)))
+            return st;
+        LayoutSortArgs ls;
+        memset(&ls, 0, sizeof ls);
+        ls.lay = a;
+        if (fused) {
+            ls.lay.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
+            ls.lay.tile_shift = shift;
+            ls.lay.tiles = P.tiles;
+            ls.lay.tile_stride = P.tile_stride;
+        }
+        ls.d = d;
+        ls.id_bits = id_bits_of(a.E);
+        ls.sort_wgs = d.pull.nblk;
+        LayoutArgs r = a;
+        r.expert_offsets = expert_offsets;
+        NotifyArgs n;
+        memset(&n, 0, sizeof n);
+        n.d = d;
+        n.lay = r;
+        n.id_bits = ls.id_bits;
+        n.count_wgs = P.tiles;
+        n.count_offsets = 0;
+        n.reduce = 1;
+        if (!grid_fits((long long)a.blocks + ls.sort_wgs, kLayoutThreads) ||
+            (!fused && !grid_fits((long long)n.count_wgs + 1, kNotifyThreads)))
+            return MOEDISP_ERR_UNSUPPORTED;
+        if ((st = hip_status(launch_layout_sort(ls, (hipStream_t)stream)))) return st;
+        if (fused) return hip_status(launch_layout_reduce(r, (hipStream_t)stream));
+        return hip_status(launch_notify(n, (hipStream_t)stream));
+    }
     if (!fused) {
         if ((st = hip_status(launch_layout(a, (hipStream_t)stream)))) return st;
         return ep_dispatch_notify(s, topk_idx, tokens_per_expert, expert_offsets, ws, ws_bytes, stream);
     }
-    const WsPlan w = plan_workspace(*s);
     a.tile_counts = (int32_t*)((char*)ws + w.counts_offset);
     a.tile_shift = shift;
     a.tiles = P.tiles;
@@ -376,10 +516,11 @@ int ep_dispatch_scatter(const moedisp_shape* s, const void* x, const float* x_sc
                         int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                         int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     const int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
                                  recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a);
     if (st) return st;
-    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+    return hip_status(launch_scatter_phase(a, (hipStream_t)stream));
 }
 
 int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
@@ -387,13 +528,15 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
                 int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row,
                 void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     const int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
                                  recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a);
     if (st) return st;
-    if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
-    const hipError_t e = launch_dispatch_notify(a, (hipStream_t)stream);
+    if (a.pull.use ? !grid_fits(a.pull.blocks, a.pull.threads) : !grid_fits(a.plan.blocks, a.plan.threads))
+        return MOEDISP_ERR_UNSUPPORTED;  // before either launch
+    const hipError_t e = launch_notify_phase(a, false, (hipStream_t)stream);
     if (e != hipSuccess) return MOEDISP_ERR_HIP;
-    return hip_status(launch_dispatch_scatter(a, (hipStream_t)stream));
+    return hip_status(launch_scatter_phase(a, (hipStream_t)stream));
 }
 
 // Checks of the quantising dispatch calls; fills the launch arguments.
@@ -458,6 +601,7 @@ int ep_dispatch_scatter_quant(const moedisp_shape* s, int32_t quant_block, int32
                               int32_t* recv_src_idx, float* recv_weights, const int32_t* expert_offsets,
                               int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     const int st = quant_args(s, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
                               recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, &a);
     if (st) return st;
@@ -469,6 +613,7 @@ int ep_dispatch_quant(const moedisp_shape* s, int32_t quant_block, int32_t scale
                       void* recv_x, void* recv_scales, int32_t* recv_src_idx, float* recv_weights,
                       int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     const int st = quant_args(s, quant_block, scale_fmt, x, topk_idx, topk_weights, tokens_per_expert, recv_x,
                               recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, &a);
     if (st) return st;
@@ -600,6 +745,7 @@ int ep_dispatch_groups(const moedisp_shape* s, const void* x, const float* x_sca
     if ((st = check_ws(s, ws, ws_bytes))) return st;
     const WsPlan w = plan_workspace(*s);
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     a.T = s->num_tokens;
     a.k = s->num_groups;
     a.E = s->num_groups;
@@ -642,6 +788,7 @@ int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* g
     if (st) return st;
     const moedisp_shape rs = group_rows_shape(*s);
     DispatchArgs a;
+    memset(&a, 0, sizeof a);
     // the workspace of the token shape also holds the group rows' tile counts
     st = dispatch_args(&rs, group_x, group_scales, recv_topk_idx, recv_topk_weights, tokens_per_expert, recv_x,
                        recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a, s);

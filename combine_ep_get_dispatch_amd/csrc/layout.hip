@@ -27,37 +27,15 @@
 // restricted to that range gives the tile count with no further ballots; the
 // counts are stored expert-major as the count kernel would, and the reduce
 // kernel also writes expert_offsets, the exclusive scan of the totals.
-#include "moedisp_internal.h"
+#include "kernels_common.h"
 
 namespace moedisp {
 namespace {
 
-// Lanes among `active` whose key equals this lane's key (keys < 2^nbits,
-// nbits <= 12).  Every lane of the wave must execute this (it issues nbits
-// ballots).
-__device__ inline uint64_t match_peers(uint32_t key, int nbits, uint64_t active) {
-    uint64_t peers = active;
-#pragma unroll
-    for (int b = 0; b < 12; ++b) {
-        if (b < nbits) {  // nbits is uniform
-            const bool bit = (key >> b) & 1u;
-            const uint64_t ones = __ballot(bit);
-            peers &= bit ? ones : ~ones;
-        }
-    }
-    return peers;
-}
-
-// x / d for a host-computed (shift, magic) pair: a shift when d is a power of
-// two, else a multiply-high (exact for the ranges the host checks).
-__device__ inline uint32_t div_const(uint32_t x, int shift, uint32_t magic) {
-    return shift >= 0 ? x >> shift : __umulhi(x, magic);
-}
-
-__global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
-    // LDS: counts [E + G], ids [tokens * k], token masks [tokens], and with
-    // the notify phase tile counts [tiles per workgroup][E]
-    extern __shared__ int32_t dyn[];
+// One layout workgroup (index wg) of kLayoutThreads lanes.  LDS (dyn):
+// counts [E + G], ids [tokens * k], token masks [tokens], and with the
+// notify phase tile counts [tiles per workgroup][E]; s_err one word.
+static __device__ void layout_body(const LayoutArgs& a, int wg, int32_t* dyn, uint32_t& s_err) {
     const int EG = a.E + a.G;
     const int k = a.k;
     const int tpb = a.tokens_per_block;
@@ -66,12 +44,11 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
     uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_ids + tpb * k);
     int32_t* s_tile = reinterpret_cast<int32_t*>(s_mask + tpb);
     const int tpw = a.tile_counts ? (tpb >> a.tile_shift) : 0;  // tiles per workgroup
-    __shared__ uint32_t s_err;
 
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
     const int lane = tid & 63;
-    const int t0 = blockIdx.x * tpb;
+    const int t0 = wg * tpb;
     const int nt = max(0, min(tpb, a.T - t0));
     const int ns = nt * k;
 
@@ -137,10 +114,10 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
     if (err) atomicOr(&s_err, err);
     __syncthreads();
 
-    int32_t* mine = a.partials + (size_t)blockIdx.x * EG;
+    int32_t* mine = a.partials + (size_t)wg * EG;
     for (int i = tid; i < EG; i += nth) mine[i] = s_cnt[i];
     if (tpw > 0) {  // expert-major, this workgroup's tiles contiguous per expert
-        const int tile0 = blockIdx.x * tpw;
+        const int tile0 = wg * tpw;
         const int ntl = min(tpw, a.tiles - tile0);
         for (int i = tid; i < a.E * ntl; i += nth) {
             const int e = i / ntl;
@@ -151,70 +128,66 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
     if (tid == 0 && s_err) atomicOr(&a.hdr->status, s_err);
 }
 
+// Both kernels name one dynamic LDS array (a function-scope extern declares
+// the same entity), so both declare it alike.
+__global__ __launch_bounds__(kLayoutThreads) void moedisp_layout(LayoutArgs a) {
+    extern __shared__ __attribute__((aligned(16))) int32_t dyn[];
+    __shared__ uint32_t s_err;
+    layout_body(a, blockIdx.x, dyn, s_err);
+}
+
+// The layout's workgroups and the block-pull sort's in one launch (both read
+// only topk_idx): workgroups [0, lay.blocks) are layout workgroups, the next
+// sort_wgs sort one token block each.
+__global__ __launch_bounds__(kLayoutThreads) void moedisp_layout_sort(LayoutSortArgs a) {
+    extern __shared__ __attribute__((aligned(16))) int32_t dyn[];  // the sort's 64-bit masks first
+    __shared__ uint32_t s_err;
+    if ((int)blockIdx.x < a.lay.blocks) {
+        layout_body(a.lay, blockIdx.x, dyn, s_err);
+        return;
+    }
+    if (threadIdx.x == 0) s_err = 0;
+    __syncthreads();
+    const uint32_t err = pull_sort(a.d, blockIdx.x - a.lay.blocks, dyn);
+    if (err) atomicOr(&s_err, err);
+    __syncthreads();
+    if (threadIdx.x == 0 && s_err) atomicOr(&a.d.hdr->status, s_err);
+}
+
 // Sum of the partial counts in workgroup order (one workgroup; the kernel
-// boundary orders it after every partial), 32 independent loads in flight:
-// one round trip for up to 32 partial rows.
+// boundary orders it after every partial), and expert_offsets when requested.
 __global__ __launch_bounds__(kThreads) void moedisp_layout_reduce(LayoutArgs a) {
     __shared__ int32_t s_tot[kMaxExperts];  // expert totals, for expert_offsets
     __shared__ int32_t s_wave[kThreads / 64];
-    const int EG = a.E + a.G;
-    constexpr int kBatch = 32;
-    for (int i = threadIdx.x; i < EG; i += kThreads) {
-        int32_t sum = 0;
-        for (int b0 = 0; b0 < a.blocks; b0 += kBatch) {
-            int32_t v[kBatch];
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q)
-                v[q] = (b0 + q < a.blocks) ? a.partials[(size_t)(b0 + q) * EG + i] : 0;
-#pragma unroll
-            for (int q = 0; q < kBatch; ++q) sum += v[q];
-        }
-        if (i < a.E) {
-            a.tokens_per_expert[i] = sum;
-            s_tot[i] = sum;
-        } else {
-            a.tokens_per_group[i - a.E] = sum;
-        }
-    }
-    if (!a.expert_offsets) return;  // uniform
-    // expert_offsets: exclusive scan of the totals, a contiguous run per lane
-    __syncthreads();
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (a.E + kThreads - 1) / kThreads;
-    const int lo = min(a.E, tid * per), hi = min(a.E, lo + per);
-    int32_t run = 0;
-    for (int i = lo; i < hi; ++i) run += s_tot[i];
-    int32_t incl = run;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int32_t off = incl - run, total = 0;
-    for (int w = 0; w < kThreads / 64; ++w) {
-        if (w < wave) off += s_wave[w];
-        total += s_wave[w];
-    }
-    for (int i = lo; i < hi; ++i) {
-        a.expert_offsets[i] = off;
-        off += s_tot[i];
-    }
-    if (tid == 0) {
-        a.expert_offsets[a.E] = total;
-        if (total > a.capacity) atomicOr(&a.hdr->status, (uint32_t)MOEDISP_DEV_BAD_LAYOUT);
-    }
+    layout_reduce(a, s_tot, s_wave);
 }
 
 }  // namespace
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
+hipError_t launch_layout_sort(const LayoutSortArgs& a, hipStream_t stream) {
+    const LayoutArgs& l = a.lay;
+    size_t lds = layout_lds_bytes(l.E, l.G, l.k, l.tokens_per_block,
+                                  l.tile_counts ? (l.tokens_per_block >> l.tile_shift) : 0);
+    const size_t sort = sort_lds_words(a.d.pull.tb, a.d.pull.cap_b, a.d.E) * sizeof(int32_t);
+    if (sort > lds) lds = sort;
+    const long long blocks = (long long)l.blocks + a.sort_wgs;
+    if (!grid_fits(blocks, kLayoutThreads)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(moedisp_layout_sort, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_reduce(const LayoutArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream, bool reduce) {
     const size_t lds = layout_lds_bytes(a.E, a.G, a.k, a.tokens_per_block,
                                         a.tile_counts ? (a.tokens_per_block >> a.tile_shift) : 0);
     if (!grid_fits(a.blocks, kLayoutThreads)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kLayoutThreads), lds, stream, a);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || !reduce) return e;
     hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

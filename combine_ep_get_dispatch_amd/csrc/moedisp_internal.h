@@ -72,6 +72,46 @@ struct DispatchPlan {
 
 constexpr int kMaxDispatchThreads = 1024;
 
+// Block-pull dispatch.  The tokens are cut into nblk blocks of tb tokens
+// (the last one may be shorter), and block b is copied by workgroups that the
+// hardware's round-robin dispatch places on XCD b % kXcds: a block's source
+// rows (tb * row bytes, kept below kPullL2Bytes) are read from HBM once and
+// then served by that XCD's L2 for each of their k copies, and the block's
+// receive rows are written in ascending address order, one run per expert.
+// The notify phase sorts each block's slots by (expert, slot) into a list of
+// cap_b = tb * k entries (routed entries first, then the masked ones); copy
+// workgroup j of a block writes the receive rows of list entries
+// [j * rpw, (j + 1) * rpw).  Shapes this does not fit (small T, many experts,
+// very large T) take the push scatter (DispatchPlan).
+struct PullPlan {
+    int use;          // 0: the push scatter serves this shape
+    int tb;           // tokens per block
+    int nblk;         // blocks (8 <= nblk <= kPullMaxBlocks)
+    int cap_b;        // list entries per block (tb * k <= kPullMaxBlockSlots)
+    int cnt_stride;   // ints per expert column of the per-block counts (>= nblk, multiple of 4)
+    int rpw;          // list entries (receive rows) per copy workgroup
+    int threads;      // copy workgroup lanes
+    int units;        // 16-byte units per lane and pass
+    int wpb;          // copy workgroups per block: ceil(cap_b / rpw)
+    long long blocks; // copy grid: kXcds * wpb * ceil(nblk / kXcds)
+};
+
+constexpr int kXcds = 8;                          // XCDs of an MI355X (round-robin workgroup dispatch)
+constexpr long long kPullL2Bytes = 3584 * 1024;   // source bytes per block: below one XCD's 4 MB L2
+constexpr int kPullMaxExperts = 512;              // per-wave expert tables of the sort fit LDS
+constexpr int kPullMaxBlockSlots = 4096;          // slots of one block sorted in LDS
+constexpr int kPullMaxBlocks = 256;               // a row's count prefix is one 16-byte load per lane of a wave
+constexpr int kPullMinBlockTokens = 32;
+constexpr int kPullMaskWords = 4096;              // the sort's token masks: E * ceil(tb / 64) 64-bit words at most
+constexpr int kNotifyThreads = 1024;              // lanes of a notify workgroup (16 waves)
+
+// One entry of a block's sorted list: flat slot t * k + j and its expert
+// (-1 for a masked or invalid slot).
+struct PullEnt {
+    int32_t slot;
+    int32_t expert;
+};
+
 struct CombinePlan {
     int col_splits;
     int blocks;
@@ -85,10 +125,15 @@ struct WsPlan {
     int layout_blocks;
     size_t partial_offset;   // int32 [layout_blocks][E + G]
     size_t counts_offset;    // int32 [E][tile_stride]: per-tile expert counts of the dispatch
+    size_t pull_cnt_offset;  // block-pull: int32 [E][cnt_stride] routed slots per (expert, block)
+    size_t pull_ls_offset;   // block-pull: int32 [nblk][E] first list entry of each expert in a block
+    size_t pull_n_offset;    // block-pull: int32 [nblk] routed entries per block
+    size_t pull_ent_offset;  // block-pull: PullEnt [nblk][cap_b] sorted lists
     size_t total;
 };
 
 DispatchPlan plan_dispatch(const moedisp_shape& s);
+PullPlan plan_pull(const moedisp_shape& s);
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s);
 DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
 moedisp_shape group_rows_shape(const moedisp_shape& s);
@@ -166,6 +211,37 @@ struct DispatchArgs {
     float* recv_topk_weights;
     WsHeader* hdr;
     int32_t* tile_counts;
+    // block-pull tables (pull.use != 0)
+    PullPlan pull;
+    int32_t* pull_cnt;
+    int32_t* pull_ls;
+    int32_t* pull_n;
+    PullEnt* pull_ent;
+};
+
+// The notify launch of the block-pull dispatch: one launch whose workgroups
+// take one of three roles by index: [0, sort_wgs) sort one block each;
+// [sort_wgs, sort_wgs + count_wgs) count one dispatch tile each (the tables
+// of the push path, which the quantising scatter reads), tile 0 also writing
+// expert_offsets when count_offsets is set; a last workgroup, if reduce is
+// set, sums the layout's partial counts (tokens_per_expert, tokens_per_group,
+// expert_offsets).  No role waits for another.
+struct NotifyArgs {
+    DispatchArgs d;
+    LayoutArgs lay;
+    int id_bits;        // bits of an expert id (ceil(log2 E))
+    int sort_wgs;
+    int count_wgs;
+    int count_offsets;
+    int reduce;         // last workgroup: 0 none, 1 the layout's reduce, 2 the offsets scan
+};
+
+// The layout's workgroups and the block-pull sort's in one launch.
+struct LayoutSortArgs {
+    LayoutArgs lay;
+    DispatchArgs d;
+    int id_bits;
+    int sort_wgs;
 };
 
 struct CombineArgs {
@@ -221,10 +297,16 @@ inline bool grid_fits(long long blocks, long long threads) {
     return blocks >= 1 && blocks <= 0x7FFFFFFFll && blocks * threads <= 0xFFFFFFFFll;
 }
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+// reduce = false: the partial counts only (moedisp_layout), no reduce launch
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream, bool reduce = true);
 hipError_t launch_dispatch_fused(const FusedArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_notify(const DispatchArgs& a, hipStream_t stream);
 hipError_t launch_dispatch_scatter(const DispatchArgs& a, hipStream_t stream);
+hipError_t launch_notify(const NotifyArgs& a, hipStream_t stream);
+hipError_t launch_layout_sort(const LayoutSortArgs& a, hipStream_t stream);
+hipError_t launch_layout_reduce(const LayoutArgs& a, hipStream_t stream);
+hipError_t launch_scatter_pull(const DispatchArgs& a, hipStream_t stream);
+size_t notify_lds_bytes(const NotifyArgs& a);
 hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);

@@ -78,8 +78,7 @@ def test_layout_notify_parity(orc, dev, name):
 @pytest.mark.parametrize("cid", [2, 3, 5])
 def test_layout_notify_full_size(orc, dev, cid):
     """The benchmark's call sequence at full size: layout_notify, scatter and
-    combine; dispatch bit-exact, combine to the bar on a seeded sample of
-    tokens (the last token always included)."""
+    combine; dispatch bit-exact, combine to the bar on every token."""
     wl = W.config(cid)
     _say(f"[layout_notify-full] config {cid} {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k}")
     bufs, _, o = run_layout_notify(orc, wl, dev)
@@ -88,11 +87,8 @@ def test_layout_notify_full_size(orc, dev, cid):
     eo = GH.upload_expert_out(eo_bits, wl.T * wl.k, wl.H, dev)
     g32, g16, st = GH.gpu_combine(bufs, eo, wl, dev)
     assert st == 0
-    rng = np.random.default_rng(cid)
-    toks = np.sort(rng.choice(wl.T, size=256, replace=False))
-    toks[-1] = wl.T - 1
-    o32, o16 = orc.combine(eo_bits, o["recv_weights"][:R], o["slot_to_row"][toks])
-    r = GH.assert_combine_close(g32[toks], g16[toks], o32, o16)
+    o32, o16 = orc.combine(eo_bits, o["recv_weights"][:R], o["slot_to_row"])
+    r = GH.assert_combine_close(g32, g16, o32, o16)
     _say(f"[layout_notify-full] config {cid} ok R={R} max_ulp={r['max_ulp']}")
 
 

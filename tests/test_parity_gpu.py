@@ -2,10 +2,11 @@
 
 Bit-exact: layout counts, bitmap, offsets, slot_to_row, recv_src_idx,
 recv_weights, received rows and scales.  Combine: max relative error 1e-3 in
-fp32 and at most one bf16 ulp after rounding, on every token of the small and
-mid-sized cases and on a seeded sample of tokens (always including the last)
-at the full sizes, which run in the same launch configuration as the
-benchmark.
+fp32 and at most one bf16 ulp after rounding, on every token of every case,
+the full sizes included (they run in the same launch configuration as the
+benchmark).  Shapes with at least 256 tokens and at most 512 experts take the
+block-pull dispatch (blocks of tokens per XCD, a sorted list per block);
+smaller ones take the push scatter; both are covered here.
 """
 import numpy as np
 import pytest
@@ -56,7 +57,7 @@ def test_parity_every_output(orc, dev, name):
 def test_parity_full_size(orc, dev, cid):
     wl = W.config(cid)
     _say(f"[parity-full] config {cid} {wl.name} T={wl.T} H={wl.H} E={wl.E} k={wl.k}")
-    r = GH.full_parity(orc, wl, dev, sample_tokens=384, seed=cid)
+    r = GH.full_parity(orc, wl, dev)
     _say(f"[parity-full] config {cid} ok R={r['R']} max_ulp={r['max_ulp']} exact_f32={r['exact_f32']:.4f}")
 
 
@@ -90,6 +91,19 @@ EDGE = {
     # column ranges: more than one pass of the scatter's widest workgroup
     # (1024 lanes x 2 units), with a ragged last pass
     "wide_rows": lambda: W.make_workload("wide_rows", 1024, 20000, 16, 4, 4, seed=61),
+    # block-pull boundaries: the smallest pulled T (8 blocks of 32 tokens,
+    # the last one shorter), 512 experts with k = 32 (the largest expert
+    # table and sorted list of the sort), fp8 rows with scales, masked
+    # slots, rows wider than one pass of the copy workgroup, and 256 blocks
+    # (a row's count prefix spans all 64 lanes of a wave)
+    "pull_T255": lambda: W.make_workload("pull_T255", 255, 512, 64, 8, 8, seed=62),
+    "pull_E512_k32": lambda: W.make_workload("pull_E512_k32", 2048, 256, 512, 32, 32, seed=63, routing="zipf",
+                                             mask_frac=0.05),
+    "pull_fp8": lambda: W.make_workload("pull_fp8", 1500, 7168, 256, 8, 8, seed=64, x_dtype=W.X_FP8,
+                                        scale_block=128),
+    "pull_masked": lambda: W.make_workload("pull_masked", 2000, 2048, 128, 8, 6, seed=65, mask_frac=0.3),
+    "pull_wide_rows": lambda: W.make_workload("pull_wide_rows", 2000, 40000, 16, 4, 2, seed=66),
+    "pull_256_blocks": lambda: W.make_workload("pull_256_blocks", 32768, 256, 64, 8, 32, seed=67),
 }
 
 
@@ -104,7 +118,9 @@ def test_parity_edge_cases(orc, dev, name):
 
 def test_dispatch_deterministic_under_repeats(orc, dev):
     """Skewed routing, 20 dispatches on one workspace: every output identical
-    (the look-back must not let scheduling order leak into the result)."""
+    (no scheduling order may leak into the result: the sorts rank slots by
+    ballots and popcounts of token masks; their atomics only add and OR,
+    which commute)."""
     wl = W.make_workload("det", 2048, 1024, 256, 8, 8, seed=61, routing="zipf", mask_frac=0.05)
     _say("[determinism] 20 repeats")
     bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)

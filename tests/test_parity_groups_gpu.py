@@ -42,7 +42,7 @@ def eq(g, o, what):
         raise AssertionError(f"{what} differs (shape {g.shape} vs {o.shape}), first at {None if bad is None else bad[:4]}")
 
 
-def run_groups(orc, wl, dev, sample_tokens=0, seed=0):
+def run_groups(orc, wl, dev):
     _say(f"[groups] {wl.name} T={wl.T} H={wl.H} E={wl.E} G={wl.G} k={wl.k} {wl.x_dtype}")
     h = K.ht_path(orc, wl)
     gd, pm, Rg, R = h["gd"], h["pm"], h["Rg"], h["R"]
@@ -99,12 +99,7 @@ def run_groups(orc, wl, dev, sample_tokens=0, seed=0):
     assert bufs.status() == 0
     g32 = of[:wl.T].cpu().numpy()
     g16 = ob[:wl.T].view(torch.int16).cpu().numpy().view(np.uint16)
-    if sample_tokens and wl.T > sample_tokens:
-        toks = np.sort(np.random.default_rng(seed).choice(wl.T, size=sample_tokens, replace=False))
-        toks[-1] = wl.T - 1
-        res = GH.assert_combine_close(g32[toks], g16[toks], h["out_f32"][toks], h["out_bf16"][toks])
-    else:
-        res = GH.assert_combine_close(g32, g16, h["out_f32"], h["out_bf16"])
+    res = GH.assert_combine_close(g32, g16, h["out_f32"], h["out_bf16"])
     _say(f"[groups] {wl.name} ok R_g={Rg} R={R} max_ulp={res['max_ulp']} exact_f32={res['exact_f32']:.4f}")
 
 
@@ -133,6 +128,6 @@ def test_group_path_parity(orc, dev, name):
 
 
 def test_group_path_parity_full_size(orc, dev):
-    """DeepSeek-V3 prefill shape: every group row, permuted row and partial,
-    combine on 384 sampled tokens (the last always included)."""
-    run_groups(orc, W.config(2), dev, sample_tokens=384, seed=2)
+    """DeepSeek-V3 prefill shape: every group row, permuted row, partial and
+    combined token."""
+    run_groups(orc, W.config(2), dev)

@@ -144,3 +144,34 @@ def test_quant_then_combine_round_trip(orc, dev):
     err = np.abs(o_f32.astype(np.float64) - x)[routed]
     amax = np.abs(x).reshape(wl.T, -1, 128).max(-1).repeat(128, axis=1)[routed]
     assert np.all(err <= np.abs(x[routed]) * 2.0 ** -4 + amax / 448 * 2.0 ** -9 + 1e-6)
+
+
+def amax_sweep_workload():
+    """One 32-channel block per token, token t's block having the largest
+    magnitude bf16 bits t + 1: every positive finite bf16 value (subnormals
+    included) is some block's amax.  The other 31 channels hold seeded bf16
+    values of random sign whose magnitude bits do not exceed the amax bits (so
+    they do not exceed the amax).  E = 1 and k = 1 keep the rows in token
+    order."""
+    n = 0x7F7F  # bits 0x0001 .. 0x7F7F
+    rng = np.random.default_rng(0xA3A3)
+    amax_bits = np.arange(1, n + 1, dtype=np.uint32)
+    frac = rng.random((n, 31))
+    mag = np.floor(frac * (amax_bits[:, None] + 1)).astype(np.uint32)  # 0 .. amax bits
+    sign = (rng.random((n, 31)) < 0.5).astype(np.uint32) << 15
+    x = np.empty((n, 32), np.uint16)
+    x[:, 0] = amax_bits | ((rng.random(n) < 0.5).astype(np.uint32) << 15)
+    x[:, 1:] = mag | sign
+    perm = rng.permuted(np.tile(np.arange(32), (n, 1)), axis=1)  # the amax anywhere in the block
+    x = np.take_along_axis(x, perm, axis=1)
+    wl = W.make_workload("amax_sweep", n, 32, 1, 1, 1, seed=42)
+    wl.x = np.ascontiguousarray(x)
+    return wl
+
+
+@pytest.mark.parametrize("fmt,two_phase", [(UE8M0, False), (FP32, False), (UE8M0, True), (FP32, True)])
+def test_quant_every_bf16_amax(orc, dev, fmt, two_phase):
+    """Scale and codes of a block whose amax is each positive finite bf16
+    value in turn, bit-exact against the oracle (whose UE8M0 exponent rule is
+    itself pinned by brute force over the same values)."""
+    run_case(orc, amax_sweep_workload(), dev, 32, fmt, two_phase)
