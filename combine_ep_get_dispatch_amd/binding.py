@@ -45,7 +45,9 @@ EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", 
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_layout_dispatch_small",
-           "ep_combine", "ep_check_status", "ep_status_string", "ep_probe_copy", "ep_probe_fill")
+           "ep_combine", "ep_check_status", "ep_status_string")
+# calibration probes (include/moedisp_calib.h), exported by the same library
+CALIB_EXPORTS = ("ep_probe_read", "ep_probe_copy", "ep_probe_fill")
 
 
 class MoeDispError(RuntimeError):
@@ -115,6 +117,8 @@ def load(path: str = LIB_PATH):
     L.ep_check_status.restype = C.c_int
     L.ep_status_string.argtypes = [C.c_int]
     L.ep_status_string.restype = C.c_char_p
+    L.ep_probe_read.argtypes = [P, C.c_size_t, P, P]
+    L.ep_probe_read.restype = C.c_int
     L.ep_probe_copy.argtypes = [P, P, C.c_size_t, P]
     L.ep_probe_copy.restype = C.c_int
     L.ep_probe_fill.argtypes = [P, C.c_size_t, C.c_int32, P]
@@ -483,6 +487,14 @@ def ep_check_status(ws, stream=None) -> int:
     v = C.c_int32(0)
     _check(A.call, load().ep_check_status(_p(ws), _nb(ws), _s(stream), C.byref(v)))
     return int(v.value)
+
+
+def ep_probe_read(src, nbytes: int, sink, stream=None):
+    A = _Args("ep_probe_read")
+    A.need("src", src, _BYTES, int(nbytes))
+    A.need("sink", sink, _BYTES, 16)
+    A.done()
+    _check(A.call, load().ep_probe_read(_p(src), int(nbytes), _p(sink), _s(stream)))
 
 
 def ep_probe_copy(dst, src, nbytes: int, stream=None):

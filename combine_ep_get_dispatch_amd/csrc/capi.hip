@@ -6,6 +6,7 @@
 // unsupported argument).
 #include <string.h>
 
+#include "moedisp_calib.h"
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -890,7 +891,14 @@ int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     if ((!dst || !src) && bytes) return MOEDISP_ERR_INVALID_ARG;
     if (bytes % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
     if (!aligned(dst, 16) || !aligned(src, 16)) return MOEDISP_ERR_MISALIGNED;
-    return hip_status(launch_copy((v4u*)dst, (const v4u*)src, bytes / 16, (hipStream_t)stream));
+    return hip_status(launch_probe_copy((v4u*)dst, (const v4u*)src, bytes / 16, (hipStream_t)stream));
+}
+
+int ep_probe_read(const void* src, size_t bytes, void* sink, void* stream) {
+    if ((!src && bytes) || !sink) return MOEDISP_ERR_INVALID_ARG;
+    if (bytes % 16 != 0) return MOEDISP_ERR_UNSUPPORTED;
+    if (!aligned(src, 16) || !aligned(sink, 16)) return MOEDISP_ERR_MISALIGNED;
+    return hip_status(launch_probe_read((const v4u*)src, bytes / 16, (v4u*)sink, (hipStream_t)stream));
 }
 
 int ep_probe_fill(void* dst, size_t bytes, int32_t shuffled, void* stream) {

@@ -311,7 +311,8 @@ hipError_t launch_dispatch_scatter_quant(const DispatchArgs& a, int scale_fmt, h
 hipError_t launch_combine(const CombineArgs& a, bool f32_out, hipStream_t stream);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream);
-hipError_t launch_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream);
+hipError_t launch_probe_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream);
+hipError_t launch_probe_read(const v4u* src, size_t n16, v4u* sink, hipStream_t stream);
 hipError_t launch_probe_fill(v4u* dst, size_t chunks, size_t mult, hipStream_t stream);
 
 }  // namespace moedisp

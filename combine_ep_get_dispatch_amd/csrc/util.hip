@@ -1,6 +1,6 @@
 // Small helper kernels: workspace fill, single-word store, and the
-// calibration probes of achievable HBM bandwidth: a plain 16-byte copy and a
-// 4 KiB-chunk write in address or permuted order.
+// calibration probes of achievable HBM bandwidth: a read-only stream, a
+// copy, and a 4 KiB-chunk write in address or permuted order.
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -14,20 +14,31 @@ __global__ void moedisp_set_word(uint32_t* p, uint32_t v) {
     if (threadIdx.x == 0) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Grid-stride copy, 4 units of 16 bytes in flight per lane.
-__global__ __launch_bounds__(kThreads) void moedisp_probe_copy(v4u* __restrict__ dst, const v4u* __restrict__ src,
-                                                               size_t n) {
-    constexpr int U = 4;
-    const size_t stride = (size_t)gridDim.x * kThreads;
-    size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
-    for (; i + (U - 1) * stride < n; i += U * stride) {
-        v4u v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + i + u * stride);
-    }
-    for (; i < n; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+// Read and copy probes: workgroup c of kProbeLanes lanes takes the 16 KiB
+// chunk c (kProbeChunk16 units, two per lane) and exits.
+constexpr int kProbeLanes = 512;
+constexpr int kProbeChunk16 = 1024;
+
+__global__ __launch_bounds__(kProbeLanes) void moedisp_probe_read(const v4u* __restrict__ src, size_t n16,
+                                                                  v4u* __restrict__ sink) {
+    const size_t i0 = (size_t)blockIdx.x * kProbeChunk16 + threadIdx.x;
+    const size_t i1 = i0 + kProbeLanes;
+    const v4u zero = {0u, 0u, 0u, 0u};
+    const v4u a = i0 < n16 ? __builtin_nontemporal_load(src + i0) : zero;
+    const v4u b = i1 < n16 ? __builtin_nontemporal_load(src + i1) : zero;
+    const v4u f = a ^ b;
+    if (f.x == 0x9E3779B9u && f.y == 0x7F4A7C15u) *sink = f;  // a use of every load
+}
+
+__global__ __launch_bounds__(kProbeLanes) void moedisp_probe_copy(v4u* __restrict__ dst, const v4u* __restrict__ src,
+                                                                  size_t n16) {
+    const size_t i0 = (size_t)blockIdx.x * kProbeChunk16 + threadIdx.x;
+    const size_t i1 = i0 + kProbeLanes;
+    const v4u zero = {0u, 0u, 0u, 0u};
+    const v4u a = i0 < n16 ? __builtin_nontemporal_load(src + i0) : zero;
+    const v4u b = i1 < n16 ? __builtin_nontemporal_load(src + i1) : zero;
+    if (i0 < n16) __builtin_nontemporal_store(a, dst + i0);
+    if (i1 < n16) __builtin_nontemporal_store(b, dst + i1);
 }
 
 // Write-order probe: workgroup b writes chunk (b * mult) mod nchunks of
@@ -68,12 +79,19 @@ hipError_t launch_set_word(uint32_t* p, uint32_t value, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream) {
+hipError_t launch_probe_copy(v4u* dst, const v4u* src, size_t n16, hipStream_t stream) {
     if (n16 == 0) return hipSuccess;
-    // 256 CUs x 8 workgroups, each lane moving 4 units per pass
-    const size_t want = (n16 + 4 * kThreads - 1) / (4 * kThreads);
-    const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
-    hipLaunchKernelGGL(moedisp_probe_copy, dim3(blocks), dim3(kThreads), 0, stream, dst, src, n16);
+    const long long blocks = (long long)((n16 + kProbeChunk16 - 1) / kProbeChunk16);
+    if (!grid_fits(blocks, kProbeLanes)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(moedisp_probe_copy, dim3((unsigned)blocks), dim3(kProbeLanes), 0, stream, dst, src, n16);
+    return hipGetLastError();
+}
+
+hipError_t launch_probe_read(const v4u* src, size_t n16, v4u* sink, hipStream_t stream) {
+    if (n16 == 0) return hipSuccess;
+    const long long blocks = (long long)((n16 + kProbeChunk16 - 1) / kProbeChunk16);
+    if (!grid_fits(blocks, kProbeLanes)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(moedisp_probe_read, dim3((unsigned)blocks), dim3(kProbeLanes), 0, stream, src, n16, sink);
     return hipGetLastError();
 }
 

@@ -24,13 +24,14 @@ from collections import defaultdict
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 
-KERNELS = ("moedisp_layout", "moedisp_layout_reduce", "moedisp_count", "moedisp_scatter", "moedisp_scatter_quant", "moedisp_combine",
-           "moedisp_probe_copy", "moedisp_probe_fill")
+KERNELS = ("moedisp_layout", "moedisp_layout_sort", "moedisp_layout_reduce", "moedisp_count", "moedisp_notify",
+           "moedisp_scatter", "moedisp_scatter_pull", "moedisp_scatter_quant", "moedisp_combine",
+           "moedisp_dispatch_fused", "moedisp_probe_read", "moedisp_probe_copy", "moedisp_probe_fill")
 _NAME = re.compile(r"\b(moedisp_\w+?)(<[^>(]*>)?\(")
 
 
 def source_hash() -> str:
-    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + [os.path.join(ROOT, "include", "moedisp.h")]
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*"))) + sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
     h = hashlib.sha256()
     for f in files:
         h.update(os.path.basename(f).encode())

@@ -306,22 +306,6 @@ int ep_check_status(void* ws, size_t ws_bytes, void* stream, int32_t* host_statu
 /* Text for a host return code. */
 const char* ep_status_string(int status);
 
-/* Calibration helper, not part of the path: a plain 16-byte-vector device
- * copy of `bytes` (a multiple of 16; both pointers 16-byte aligned), used to
- * measure the achievable HBM bandwidth and to scale hardware byte counters. */
-int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream);
-
-/* Calibration helper, not part of the path: writes `bytes` (a multiple of
- * 4096; dst 16-byte aligned) in 4 KiB chunks, one workgroup per chunk, the
- * chunks in address order (shuffled = 0) or in a fixed permuted order
- * (shuffled = 1).  16-byte unit i of the buffer receives the four 32-bit
- * words {i mod 2^32, i / 2^32, ~(i mod 2^32), 0x5EED}, whatever the order.
- * Measures the HBM write bandwidth of sequential against scattered write
- * streams, the two ends between which a row scatter's writes fall.  Returns
- * UNSUPPORTED for a size that is not a multiple of 4096 or a `shuffled`
- * other than 0 or 1. */
-int ep_probe_fill(void* dst, size_t bytes, int32_t shuffled, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

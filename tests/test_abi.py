@@ -12,6 +12,7 @@ from combine_ep_get_dispatch_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moedisp.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "moedisp_calib.h")
 
 
 @pytest.fixture(scope="module")
@@ -22,8 +23,8 @@ def lib():
     return M.load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(ep_\w+)\s*\(", text)))
 
@@ -31,7 +32,10 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) == set(B.EXPORTS), names
-    for n in names:
+    calib = declared_functions(CALIB_HEADER)
+    assert set(calib) == set(B.CALIB_EXPORTS), calib
+    assert not set(names) & set(calib)
+    for n in names + calib:
         assert hasattr(lib, n), f"{n} not exported"
 
 
@@ -235,6 +239,11 @@ def test_host_checks_misc(lib):
     assert lib.ep_probe_fill(p(), 4095, 0, None) == B.ERR_UNSUPPORTED
     assert lib.ep_probe_fill(p(), 4096, 2, None) == B.ERR_UNSUPPORTED
     assert lib.ep_probe_fill(p(8), 4096, 1, None) == B.ERR_MISALIGNED
+    assert lib.ep_probe_read(None, 16, p(), None) == B.ERR_INVALID_ARG
+    assert lib.ep_probe_read(p(), 16, None, None) == B.ERR_INVALID_ARG
+    assert lib.ep_probe_read(p(), 17, p(), None) == B.ERR_UNSUPPORTED
+    assert lib.ep_probe_read(p(8), 16, p(), None) == B.ERR_MISALIGNED
+    assert lib.ep_probe_read(p(), 16, p(4), None) == B.ERR_MISALIGNED
     for code in (0, -1, -2, -3, -4, -5):
         assert M.ep_status_string(code) != "unknown status"
     assert M.ep_status_string(-99) == "unknown status"

@@ -247,3 +247,32 @@ def test_probe_copy(dev):
     M.ep_probe_copy(dst, src, n)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+def test_probe_copy_ragged(dev):
+    """A size that ends inside a workgroup's chunk: every byte copied, none
+    past the end."""
+    n16 = 3 * 1024 + 7
+    src = torch.randint(0, 255, (n16 * 16,), dtype=torch.uint8, device=dev)
+    dst = torch.zeros(n16 * 16 + 4096, dtype=torch.uint8, device=dev)
+    M.ep_probe_copy(dst, src, n16 * 16)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n16 * 16], src)
+    assert not dst[n16 * 16:].any()
+
+
+def test_probe_read(dev):
+    """The read probe stores its lane's fold only when it equals the fixed
+    pattern: planted in the last, partial chunk, it reaches the sink."""
+    n16 = 3 * 1024 + 7
+    src = torch.zeros((n16, 4), dtype=torch.int64, device=dev)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    M.ep_probe_read(src.to(torch.int32), n16 * 16, sink)
+    torch.cuda.synchronize()
+    assert not sink.any()
+    want = [0x9E3779B9, 0x7F4A7C15, 11, 12]
+    src[3 * 1024 + 3] = torch.tensor(want, dtype=torch.int64)
+    s32 = torch.where(src >= 2**31, src - 2**32, src).to(torch.int32).contiguous()
+    M.ep_probe_read(s32, n16 * 16, sink)
+    torch.cuda.synchronize()
+    assert sink.cpu().numpy().view(np.uint32).tolist() == want
