@@ -41,7 +41,7 @@ DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
 
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_get_dispatch_layout_notify",
-           "ep_dispatch",
+           "ep_dispatch", "ep_dispatch_noalloc",
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_layout_dispatch_small",
@@ -92,6 +92,8 @@ def load(path: str = LIB_PATH):
     L.ep_get_dispatch_layout_notify.restype = C.c_int
     L.ep_dispatch.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch.restype = C.c_int
+    L.ep_dispatch_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P]
+    L.ep_dispatch_noalloc.restype = C.c_int
     L.ep_dispatch_notify.argtypes = [S, P, P, P, P, C.c_size_t, P]
     L.ep_dispatch_notify.restype = C.c_int
     L.ep_dispatch_scatter.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, C.c_size_t, P]
@@ -262,7 +264,7 @@ def ep_get_dispatch_layout_notify(shape, topk_idx, tokens_per_expert, tokens_per
 
 
 def _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
-                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws):
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws=None):
     T, H, E, G, k, rb, nsc = _dims(shape)
     cap = T * k
     A.need("x", x, _rows_dtypes(shape), T * rb)
@@ -276,7 +278,8 @@ def _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_exp
     A.need("recv_weights", recv_weights, _F32, 4 * cap)
     A.need("expert_offsets", expert_offsets, _INT32, 4 * (E + 1))
     A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
-    _ws(A, ws)
+    if ws is not None:
+        _ws(A, ws)
 
 
 def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales, recv_src_idx,
@@ -289,6 +292,21 @@ def ep_dispatch(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, r
         C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
         _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws),
         _nb(ws), _s(stream)))
+
+
+def ep_dispatch_noalloc(shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                        recv_src_idx, recv_weights, expert_offsets, slot_to_row, status, stream=None):
+    """ep_dispatch with the library's static per-device workspace; `status`
+    (one device int32) receives the call's status bits.  Allocates nothing."""
+    A = _Args("ep_dispatch_noalloc")
+    _need_dispatch(A, shape, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                   recv_src_idx, recv_weights, expert_offsets, slot_to_row)
+    A.need("status", status, _INT32, 4)
+    A.done()
+    _check(A.call, load().ep_dispatch_noalloc(
+        C.byref(shape), _p(x), _p(x_scales), _p(topk_idx), _p(topk_weights), _p(tokens_per_expert), _p(recv_x),
+        _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(status),
+        _s(stream)))
 
 
 def ep_dispatch_notify(shape, topk_idx, tokens_per_expert, expert_offsets, ws, stream=None):

@@ -4,7 +4,10 @@
 // never by an assertion (the reviewers of "Add pynccl all-gatherv and
 // reducescatterv #20154" ask for a raised error instead of an assert on an
 // unsupported argument).
+#include <stddef.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "moedisp_calib.h"
 #include "moedisp_internal.h"
@@ -260,6 +263,30 @@ static int check_ws(const moedisp_shape* s, void* ws, size_t ws_bytes) {
 static int hip_status(hipError_t e) {
     if (e == hipSuccess) return MOEDISP_OK;
     return e == hipErrorInvalidConfiguration ? MOEDISP_ERR_UNSUPPORTED : MOEDISP_ERR_HIP;
+}
+
+// Workspace of ep_dispatch_noalloc: one array per device, zero when the code
+// object loads and held until the process ends.  Host code never uses the
+// name `scratch` as an address (on the host it is a stand-in, not the device
+// array): it uses the address hipGetSymbolAddress returns for the current
+// device, looked up once per device and kept in scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kScratchDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+static void* scratch_ptr[kScratchDevices];
+static std::mutex scratch_mu;
+
+static int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return MOEDISP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOEDISP_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MOEDISP_OK;
 }
 
 }  // namespace moedisp
@@ -536,6 +563,41 @@ int ep_dispatch(const moedisp_shape* s, const void* x, const float* x_scales, co
     if (a.pull.use ? !grid_fits(a.pull.blocks, a.pull.threads) : !grid_fits(a.plan.blocks, a.plan.threads))
         return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     const hipError_t e = launch_notify_phase(a, false, (hipStream_t)stream);
+    if (e != hipSuccess) return MOEDISP_ERR_HIP;
+    return hip_status(launch_scatter_phase(a, (hipStream_t)stream));
+}
+
+int ep_dispatch_noalloc(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                        const float* topk_weights, const int32_t* tokens_per_expert, void* recv_x,
+                        float* recv_scales, int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets,
+                        int32_t* slot_to_row, int32_t* status, void* stream) {
+    if (!status) return MOEDISP_ERR_INVALID_ARG;
+    if (!aligned(status, 4)) return MOEDISP_ERR_MISALIGNED;
+    // every host check first, against a stand-in workspace address (aligned,
+    // never dereferenced) of the array's size: a shape whose workspace
+    // exceeds the array is WORKSPACE_TOO_SMALL before any HIP call
+    DispatchArgs a;
+    memset(&a, 0, sizeof a);
+    int st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                           recv_src_idx, recv_weights, expert_offsets, slot_to_row, (void*)(uintptr_t)256,
+                           kScratchBytes, true, &a);
+    if (st) return st;
+    if (a.pull.use ? !grid_fits(a.pull.blocks, a.pull.threads) : !grid_fits(a.plan.blocks, a.plan.threads))
+        return MOEDISP_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if ((st = scratch_of_current_device(&ws))) return st;
+    memset(&a, 0, sizeof a);
+    if ((st = dispatch_args(s, x, x_scales, topk_idx, topk_weights, tokens_per_expert, recv_x, recv_scales,
+                            recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, kScratchBytes, true, &a)))
+        return st;
+    // the kernels or their status bits into the header's first word, its
+    // only use: here that word is the caller's, cleared first (by a kernel,
+    // so that the call can be captured in a graph)
+    static_assert(offsetof(WsHeader, status) == 0, "status is the header's first word");
+    a.hdr = reinterpret_cast<WsHeader*>(status);
+    hipError_t e = launch_set_word(reinterpret_cast<uint32_t*>(status), 0u, (hipStream_t)stream);
+    if (e != hipSuccess) return MOEDISP_ERR_HIP;
+    e = launch_notify_phase(a, false, (hipStream_t)stream);
     if (e != hipSuccess) return MOEDISP_ERR_HIP;
     return hip_status(launch_scatter_phase(a, (hipStream_t)stream));
 }

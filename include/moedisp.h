@@ -133,6 +133,25 @@ int ep_dispatch(const moedisp_shape* shape, const void* x, const float* x_scales
                 int32_t* recv_src_idx, float* recv_weights, int32_t* expert_offsets,
                 int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream);
 
+/* ep_dispatch for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same kernels, with the workspace in a static device array of the library
+ * (8 MiB, one per device, held until the process ends) instead of `ws`: the
+ * call allocates nothing, and the caller passes only inputs and outputs.
+ * Shapes whose ep_workspace_bytes exceeds 8 MiB return
+ * MOEDISP_ERR_WORKSPACE_TOO_SMALL (at H = 7168, E = 256, k = 8: up to
+ * T = 65536) before any HIP call.  The current device must be the stream's.
+ * Arguments as for ep_dispatch, except:
+ *   status  int32 [1], device: overwritten with this call's status bits
+ *           (BAD_EXPERT_ID, BAD_LAYOUT), ready when the stream reaches the
+ *           end of the call; read it with an ordinary copy.
+ * All calls on one device share its array: calls that overlap on one device
+ * (two streams, two threads) race and may return wrong rows. */
+int ep_dispatch_noalloc(const moedisp_shape* shape, const void* x, const float* x_scales,
+                        const int32_t* topk_idx, const float* topk_weights, const int32_t* tokens_per_expert,
+                        void* recv_x, float* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                        int32_t* expert_offsets, int32_t* slot_to_row, int32_t* status, void* stream);
+
 /* The two phases of ep_dispatch, for callers that time or schedule them
  * apart (the page's high-throughput path likewise separates notify_dispatch,
  * which exchanges counts, from dispatch, which moves rows).

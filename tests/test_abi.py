@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import combine_ep_get_dispatch_amd as M
 from combine_ep_get_dispatch_amd import binding as B
@@ -74,6 +75,32 @@ def layout_rc(lib, s, ws_bytes=1 << 30, ws=None, idx=None, tpe=None, tpg=None, b
 def dispatch_rc(lib, s, x=None, xs=None, recv_x=None, rs=None, ws=None, ws_bytes=1 << 30, tpe=None):
     return lib.ep_dispatch(C.byref(s), x or p(), xs, p(), p(), tpe or p(), recv_x or p(), rs, p(), p(), p(), p(),
                            ws or p(), ws_bytes, None)
+
+
+def noalloc_rc(lib, s, status=None, x=None):
+    return lib.ep_dispatch_noalloc(C.byref(s), x or p(), None, p(), p(), p(), p(), None, p(), p(), p(), p(),
+                                   status, None)
+
+
+def test_host_checks_dispatch_noalloc(lib):
+    """The static-workspace dispatch rejects, before any HIP call: a missing
+    or misaligned status word, the usual bad arguments, and shapes whose
+    workspace exceeds its 8 MiB array."""
+    assert noalloc_rc(lib, shape(), status=None) == B.ERR_INVALID_ARG
+    assert noalloc_rc(lib, shape(), status=p(2)) == B.ERR_MISALIGNED
+    assert noalloc_rc(lib, shape(E=255), status=p()) == B.ERR_INVALID_ARG
+    assert noalloc_rc(lib, shape(), status=p(), x=p(8)) == B.ERR_MISALIGNED
+    for T, E, G in ((1000000, 256, 8), (65536, 4096, 32)):
+        s = shape(T=T, E=E, G=G)
+        assert lib.ep_workspace_bytes(C.byref(s)) > 8 << 20
+        assert noalloc_rc(lib, s, status=p()) == B.ERR_WORKSPACE_TOO_SMALL
+    # the status word is not a workspace: no size argument, checked as 4 bytes
+    with pytest.raises(M.MoeDispError, match="status"):
+        sh = shape(T=4, H=64, E=8, G=2, k=2)
+        z = lambda n, dt=None: torch.zeros(n, dtype=dt or torch.int32)
+        M.ep_dispatch_noalloc(sh, z(4 * 128, torch.uint8), None, z(8), z(8, torch.float32), z(8),
+                              z(8 * 128, torch.uint8), None, z(8), z(8, torch.float32), z(9), z(8),
+                              z(0))
 
 
 def combine_rc(lib, s, eo=None, out=None, out_dtype=M.BF16, ws_bytes=1 << 30):
