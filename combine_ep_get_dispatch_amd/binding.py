@@ -46,8 +46,9 @@ EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", 
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
            "ep_layout_dispatch_small",
            "ep_combine", "ep_check_status", "ep_status_string")
-# calibration probes (include/moedisp_calib.h), exported by the same library
-CALIB_EXPORTS = ("ep_probe_read", "ep_probe_copy", "ep_probe_fill")
+# tools (include/moedisp_tools.h): plan query and calibration probes, exported
+# by the same library
+CALIB_EXPORTS = ("ep_plan_query", "ep_probe_read", "ep_probe_copy", "ep_probe_fill")
 
 
 class MoeDispError(RuntimeError):
@@ -67,6 +68,45 @@ class moedisp_shape(C.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class moedisp_launch_info(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("blocks", "threads", "lds_bytes", "static_lds_bytes")]
+
+
+_L, _I = moedisp_launch_info, C.c_int64
+
+
+class moedisp_plan_info(C.Structure):
+    """What the entry points would launch for one shape (moedisp_tools.h)."""
+    _fields_ = [("struct_bytes", _I), ("layout", _L), ("layout_reduce", _L), ("layout_tokens_per_block", _I),
+                ("layout_notify_fused", _I), ("layout_notify", _L),
+                ("tile_tokens", _I), ("tiles", _I), ("tile_stride", _I),
+                ("block_tokens", _I), ("block_slots", _I), ("col_splits", _I), ("split_units", _I),
+                ("units_per_lane", _I), ("count", _L), ("scatter", _L),
+                ("pull", _I), ("pull_tb", _I), ("pull_nblk", _I), ("pull_cap_b", _I), ("pull_cnt_stride", _I),
+                ("pull_rows_per_wg", _I), ("pull_units", _I), ("pull_notify", _L), ("pull_copy", _L),
+                ("quant_block_slots", _I), ("scatter_quant", _L),
+                ("group_rows", _I), ("groups_tile_stride", _I), ("groups_tiles", _I), ("groups_block_slots", _I),
+                ("permute_tile_stride", _I), ("permute_tiles", _I), ("permute_block_slots", _I),
+                ("groups_count", _L), ("groups_scatter", _L), ("permute_count", _L), ("permute_scatter", _L),
+                ("group_reduce", _L), ("combine_groups", _L),
+                ("combine_col_splits", _I), ("combine_units_per_lane", _I), ("combine", _L),
+                ("small", _I), ("small_fused", _L),
+                ("ws_total", _I), ("ws_partial_offset", _I), ("ws_partial_bytes", _I), ("ws_counts_offset", _I),
+                ("ws_counts_bytes", _I), ("ws_counts_needed_flat", _I), ("ws_counts_needed_groups", _I),
+                ("ws_counts_needed_rows", _I), ("ws_pull_cnt_offset", _I), ("ws_pull_ls_offset", _I),
+                ("ws_pull_n_offset", _I), ("ws_pull_ent_offset", _I), ("ws_pull_end", _I),
+                ("max_block_slots", _I), ("max_tile_slots", _I), ("max_threads", _I),
+                ("pull_max_block_slots", _I), ("pull_max_blocks", _I)]
+
+
+def _as_dict(st):
+    out = {}
+    for n, t in st._fields_:
+        v = getattr(st, n)
+        out[n] = _as_dict(v) if isinstance(v, C.Structure) else int(v)
+    return out
 
 
 _lib = None
@@ -119,6 +159,8 @@ def load(path: str = LIB_PATH):
     L.ep_check_status.restype = C.c_int
     L.ep_status_string.argtypes = [C.c_int]
     L.ep_status_string.restype = C.c_char_p
+    L.ep_plan_query.argtypes = [S, C.POINTER(moedisp_plan_info), C.c_size_t]
+    L.ep_plan_query.restype = C.c_int
     L.ep_probe_read.argtypes = [P, C.c_size_t, P, P]
     L.ep_probe_read.restype = C.c_int
     L.ep_probe_copy.argtypes = [P, P, C.c_size_t, P]
@@ -505,6 +547,14 @@ def ep_check_status(ws, stream=None) -> int:
     v = C.c_int32(0)
     _check(A.call, load().ep_check_status(_p(ws), _nb(ws), _s(stream), C.byref(v)))
     return int(v.value)
+
+
+def ep_plan_query(shape) -> dict:
+    """The launch geometry, LDS and workspace layout of `shape` as a dict
+    (launches as nested dicts); raises for a shape the library rejects."""
+    info = moedisp_plan_info()
+    _check("ep_plan_query", load().ep_plan_query(C.byref(shape), C.byref(info), C.sizeof(info)))
+    return _as_dict(info)
 
 
 def ep_probe_read(src, nbytes: int, sink, stream=None):

@@ -9,7 +9,7 @@
 
 #include <mutex>
 
-#include "moedisp_calib.h"
+#include "moedisp_tools.h"
 #include "moedisp_internal.h"
 
 namespace moedisp {
@@ -83,6 +83,7 @@ static DispatchPlan plan_scatter(const moedisp_shape& s, long long write_per_tok
     while (token_blocks * splits < 1024 && units / (splits * 2) >= kThreads / 2) splits *= 2;
     int per = ceil_div(units, splits);
     per = ceil_div(per, align) * align;
+    if (per < 1) per = 1;  // rows of no whole unit are rejected by the callers
     p.split_units = per;
     p.col_splits = ceil_div(units, per);
     p.block_tokens = bt;
@@ -193,6 +194,47 @@ moedisp_shape group_rows_shape(const moedisp_shape& s) {
 // straddles two of them.
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s) {
     return plan_scatter(s, (long long)s.topk * (long long)s.hidden, s.hidden / 16, 64, 1, kCopyWorkgroupBytes);
+}
+
+// Small-batch path: every workgroup holds the routing table, two per-expert
+// arrays and the token masks in LDS (<= 60 KiB); rows are split into column
+// ranges while the grid is small, as for the scatter.
+SmallPlan plan_small(const moedisp_shape& s) {
+    SmallPlan p;
+    memset(&p, 0, sizeof p);
+    const long long n = (long long)s.num_tokens * s.topk;
+    p.lds_bytes = (size_t)(n + 2LL * s.num_experts + s.num_tokens) * sizeof(int32_t);
+    p.supported = n <= kFusedMaxSlots && p.lds_bytes <= 60 * 1024;
+    const int row16 = (int)(row_bytes(s) / 16);
+    int splits = 1;
+    while ((long long)s.num_tokens * splits < 1024 && row16 / (splits * 2) >= kThreads / 2) splits *= 2;
+    const int per = ceil_div(row16, splits);
+    p.split_units = per;
+    p.col_splits = ceil_div(row16, per);
+    int threads = (per + 63) / 64 * 64;
+    if (threads < kThreads) threads = kThreads;
+    if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
+    p.threads = threads;
+    p.blocks = (long long)s.num_tokens * p.col_splits + 1;  // + the layout workgroup
+    return p;
+}
+
+// LDS a layout workgroup may use with the notify phase folded in.
+constexpr size_t kLayoutNotifyLds = 64 * 1024;
+
+// Whether ep_get_dispatch_layout_notify folds the dispatch's tile counts into
+// the layout's workgroups: the tiles (a power of two of tokens) must lie
+// inside them and their counts fit the LDS budget with the layout's own.
+LayoutNotifyPlan plan_layout_notify(const moedisp_shape& s) {
+    LayoutNotifyPlan p;
+    const DispatchPlan P = plan_dispatch(s);
+    int shift = 0;
+    while ((1 << shift) < P.tile_tokens) ++shift;
+    const int tpb = layout_tokens_per_block(s);
+    p.tile_shift = shift;
+    p.fused = s.num_tokens > 0 && (1 << shift) == P.tile_tokens && tpb % P.tile_tokens == 0 &&
+              layout_lds_bytes(s.num_experts, s.num_groups, s.topk, tpb, tpb / P.tile_tokens) <= kLayoutNotifyLds;
+    return p;
 }
 
 CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {
@@ -469,9 +511,6 @@ int ep_dispatch_notify(const moedisp_shape* s, const int32_t* topk_idx, const in
     return hip_status(launch_notify_phase(a, true, (hipStream_t)stream));
 }
 
-// LDS a layout workgroup may use with the notify phase folded in.
-constexpr size_t kLayoutNotifyLds = 64 * 1024;
-
 int ep_get_dispatch_layout_notify(const moedisp_shape* s, const int32_t* topk_idx, int32_t* tokens_per_expert,
                                   int32_t* tokens_per_group, uint32_t* is_token_in_group, int32_t* expert_offsets,
                                   void* ws, size_t ws_bytes, void* stream) {
@@ -483,11 +522,9 @@ int ep_get_dispatch_layout_notify(const moedisp_shape* s, const int32_t* topk_id
     // the dispatch's tiles must lie inside the layout workgroups, and their
     // counts fit in LDS; otherwise the two calls, in order
     const DispatchPlan P = plan_dispatch(*s);
-    int shift = 0;
-    while ((1 << shift) < P.tile_tokens) ++shift;
-    const int tpb = a.tokens_per_block;
-    const bool fused = s->num_tokens > 0 && (1 << shift) == P.tile_tokens && tpb % P.tile_tokens == 0 &&
-                       layout_lds_bytes(a.E, a.G, a.k, tpb, tpb / P.tile_tokens) <= kLayoutNotifyLds;
+    const LayoutNotifyPlan lnp = plan_layout_notify(*s);
+    const int shift = lnp.tile_shift;
+    const bool fused = lnp.fused != 0;
     const WsPlan w = plan_workspace(*s);
     if (plan_pull(*s).use) {
         // block-pull: the layout's partial counts (with the dispatch tiles'
@@ -729,11 +766,7 @@ int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float*
     int st = check_shape(s);
     if (st) return st;
     const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
-    const long long n = (long long)s->num_tokens * s->topk;
-    // the routing table, two per-expert arrays and the token masks live in
-    // LDS (<= 60 KiB)
-    if (n > kFusedMaxSlots || (n + 2LL * s->num_experts + s->num_tokens) * 4 > 60 * 1024)
-        return MOEDISP_ERR_UNSUPPORTED;
+    if (!plan_small(*s).supported) return MOEDISP_ERR_UNSUPPORTED;
     if (!tokens_per_expert || !tokens_per_group || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
     if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !is_token_in_group || !recv_x || !recv_src_idx ||
                               !recv_weights || !slot_to_row))
@@ -746,6 +779,7 @@ int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float*
         !aligned(slot_to_row, 4))
         return MOEDISP_ERR_MISALIGNED;
     if ((st = check_ws(s, ws, ws_bytes))) return st;
+    const SmallPlan sp = plan_small(*s);
     FusedArgs a;
     a.T = s->num_tokens;
     a.k = s->topk;
@@ -756,16 +790,9 @@ int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float*
     a.row16 = (int)(row_bytes(*s) / 16);
     a.scale_words = fp8 ? scales_per_row(*s) : 0;
     a.capacity = s->num_tokens * s->topk;
-    // column ranges: split rows while the grid is small, as for the scatter
-    int splits = 1;
-    while ((long long)s->num_tokens * splits < 1024 && a.row16 / (splits * 2) >= kThreads / 2) splits *= 2;
-    const int per = ceil_div(a.row16, splits);
-    a.split_units = per;
-    a.col_splits = ceil_div(a.row16, per);
-    int threads = (per + 63) / 64 * 64;
-    if (threads < kThreads) threads = kThreads;
-    if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
-    a.threads = threads;
+    a.split_units = sp.split_units;
+    a.col_splits = sp.col_splits;
+    a.threads = sp.threads;
     a.x = (const v4u*)x;
     a.x_scales = fp8 ? x_scales : nullptr;
     a.topk_idx = topk_idx;
@@ -947,6 +974,141 @@ const char* ep_status_string(int status) {
         case MOEDISP_ERR_HIP: return "HIP runtime error";
         default: return "unknown status";
     }
+}
+
+// Upper bounds of the kernels' static LDS (their __shared__ declarations).
+constexpr int64_t kStaticLdsLayout = 16, kStaticLdsReduce = kMaxExperts * 4 + 16, kStaticLdsCount = 48,
+                  kStaticLdsNotify = 144, kStaticLdsFused = 464;
+
+static moedisp_launch_info launch_info(long long blocks, long long threads, size_t lds, int64_t static_lds) {
+    moedisp_launch_info l;
+    l.blocks = blocks;
+    l.threads = threads;
+    l.lds_bytes = (int64_t)lds;
+    l.static_lds_bytes = static_lds;
+    return l;
+}
+
+static moedisp_launch_info push_count(const DispatchPlan& p, int E) {
+    return launch_info(p.tiles, kThreads, (size_t)E * sizeof(int32_t), kStaticLdsCount);
+}
+
+static moedisp_launch_info push_scatter(const DispatchPlan& p, int k) {
+    return launch_info(p.blocks, p.threads, (size_t)p.tile_tokens * k * sizeof(int32_t), (int64_t)sizeof(ScatterSmem));
+}
+
+int ep_plan_query(const moedisp_shape* s, moedisp_plan_info* info, size_t info_bytes) {
+    if (!info || info_bytes != sizeof(moedisp_plan_info)) return MOEDISP_ERR_INVALID_ARG;
+    memset(info, 0, sizeof *info);
+    info->struct_bytes = (int64_t)sizeof(moedisp_plan_info);
+    const int st = check_shape(s);
+    if (st) return st;
+    const int T = s->num_tokens, E = s->num_experts, G = s->num_groups, k = s->topk;
+    const WsPlan w = plan_workspace(*s);
+    // layout
+    const int tpb = layout_tokens_per_block(*s);
+    info->layout_tokens_per_block = tpb;
+    info->layout = launch_info(w.layout_blocks, kLayoutThreads, layout_lds_bytes(E, G, k, tpb, 0), kStaticLdsLayout);
+    info->layout_reduce = launch_info(1, kThreads, 0, kStaticLdsReduce);
+    // flat dispatch
+    const DispatchPlan P = plan_dispatch(*s);
+    info->tile_tokens = P.tile_tokens;
+    info->tiles = P.tiles;
+    info->tile_stride = P.tile_stride;
+    info->block_tokens = P.block_tokens;
+    info->block_slots = (int64_t)P.block_tokens * k;
+    info->col_splits = P.col_splits;
+    info->split_units = P.split_units;
+    info->units_per_lane = P.units_per_lane;
+    info->count = push_count(P, E);
+    info->scatter = push_scatter(P, k);
+    const PullPlan pp = plan_pull(*s);
+    const LayoutNotifyPlan lnp = plan_layout_notify(*s);
+    info->layout_notify_fused = lnp.fused;
+    size_t lay_lds = layout_lds_bytes(E, G, k, tpb, lnp.fused ? (tpb >> lnp.tile_shift) : 0);
+    long long lay_blocks = w.layout_blocks;
+    if (pp.use) {
+        info->pull = 1;
+        info->pull_tb = pp.tb;
+        info->pull_nblk = pp.nblk;
+        info->pull_cap_b = pp.cap_b;
+        info->pull_cnt_stride = pp.cnt_stride;
+        info->pull_rows_per_wg = pp.rpw;
+        info->pull_units = pp.units;
+        const size_t sort = sort_lds_words(pp.tb, pp.cap_b, E) * sizeof(int32_t);
+        // ep_dispatch's notify launch: the sorts and the offsets scan
+        info->pull_notify = launch_info((long long)pp.nblk + 1, kNotifyThreads, sort > (size_t)E * 4 ? sort : (size_t)E * 4,
+                                        kStaticLdsNotify);
+        info->pull_copy = launch_info(pp.blocks, pp.threads, 0, 0);
+        if (sort > lay_lds) lay_lds = sort;
+        lay_blocks += pp.nblk;
+    }
+    info->layout_notify = launch_info(lay_blocks, kLayoutThreads, lay_lds, kStaticLdsLayout);
+    // quantising scatter (bf16 rows of whole 32-channel blocks, the smallest
+    // block ep_dispatch_quant takes)
+    if (s->x_dtype == MOEDISP_BF16 && s->hidden % 32 == 0) {
+        const DispatchPlan Q = plan_dispatch_quant(*s);
+        info->quant_block_slots = (int64_t)Q.block_tokens * k;
+        info->scatter_quant = push_scatter(Q, k);
+    }
+    // group path
+    const moedisp_shape rs = group_rows_shape(*s);
+    info->group_rows = rs.num_tokens;
+    const DispatchPlan GP = plan_dispatch_groups(*s);
+    info->groups_tile_stride = GP.tile_stride;
+    info->groups_tiles = GP.tiles;
+    info->groups_block_slots = (int64_t)GP.block_tokens * G;
+    info->groups_count = push_count(GP, G);
+    info->groups_scatter = push_scatter(GP, G);
+    const DispatchPlan RP = plan_group_permute(*s);
+    info->permute_tile_stride = RP.tile_stride;
+    info->permute_tiles = RP.tiles;
+    info->permute_block_slots = (int64_t)RP.block_tokens * k;
+    info->permute_count = push_count(RP, E);
+    info->permute_scatter = push_scatter(RP, k);
+    // combines (no LDS)
+    if (T > 0) {
+        const CombinePlan C = plan_combine(*s, k);
+        info->combine_col_splits = C.col_splits;
+        info->combine_units_per_lane = C.units_per_lane;
+        info->combine = launch_info(C.blocks, C.threads, 0, 0);
+        const int m = G < k ? G : k;
+        moedisp_shape cs = *s;
+        cs.num_tokens = rs.num_tokens;
+        const CombinePlan RC = plan_combine(cs, (k + m - 1) / m);
+        info->group_reduce = launch_info(RC.blocks, RC.threads, 0, 0);
+        cs = *s;
+        cs.topk = G;
+        const CombinePlan GC = plan_combine(cs, G);
+        info->combine_groups = launch_info(GC.blocks, GC.threads, 0, 0);
+    }
+    // small path
+    const SmallPlan sp = plan_small(*s);
+    if (sp.supported) {
+        info->small = 1;
+        info->small_fused = launch_info(sp.blocks, sp.threads, sp.lds_bytes, kStaticLdsFused);
+    }
+    // workspace
+    info->ws_total = (int64_t)w.total;
+    info->ws_partial_offset = (int64_t)w.partial_offset;
+    info->ws_partial_bytes = (int64_t)w.layout_blocks * (E + G) * (int64_t)sizeof(int32_t);
+    info->ws_counts_offset = (int64_t)w.counts_offset;
+    info->ws_counts_bytes = (int64_t)(w.pull_cnt_offset - w.counts_offset);
+    info->ws_counts_needed_flat = (int64_t)P.tile_stride * E * 4;
+    info->ws_counts_needed_groups = (int64_t)GP.tile_stride * G * 4;
+    info->ws_counts_needed_rows = (int64_t)plan_dispatch(rs).tile_stride * E * 4;
+    info->ws_pull_cnt_offset = (int64_t)w.pull_cnt_offset;
+    info->ws_pull_ls_offset = (int64_t)w.pull_ls_offset;
+    info->ws_pull_n_offset = (int64_t)w.pull_n_offset;
+    info->ws_pull_ent_offset = (int64_t)w.pull_ent_offset;
+    info->ws_pull_end = pp.use ? (int64_t)(w.pull_ent_offset + (size_t)pp.nblk * pp.cap_b * sizeof(PullEnt))
+                               : (int64_t)w.pull_ent_offset;
+    info->max_block_slots = kMaxBlockSlots;
+    info->max_tile_slots = kMaxTileSlots;
+    info->max_threads = kMaxDispatchThreads;
+    info->pull_max_block_slots = kPullMaxBlockSlots;
+    info->pull_max_blocks = kPullMaxBlocks;
+    return MOEDISP_OK;
 }
 
 int ep_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {

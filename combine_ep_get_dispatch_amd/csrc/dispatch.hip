@@ -56,18 +56,6 @@ __global__ __launch_bounds__(kThreads) void moedisp_count(DispatchArgs a) {
     if (threadIdx.x == 0 && s_err) atomicOr(&a.hdr->status, s_err);
 }
 
-// LDS of a scatter workgroup besides the staged routing ids.
-struct ScatterSmem {
-    int32_t pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
-    int32_t base[kMaxBlockSlots];  // expert_offsets[e]
-    int32_t len[kMaxBlockSlots];   // tokens_per_expert[e]
-    int32_t rows[kMaxBlockSlots + 8];  // receive row of each slot of the workgroup, -1 if none
-                                       // (8 spare entries: the stores read rows 8 at a time)
-    int32_t routed_tok[kMaxBlockTokens];  // nonzero if the token has a receive row
-    int32_t routed;
-    uint32_t err;
-};
-
 // Which tokens and columns a scatter workgroup owns.
 struct ScatterBlock {
     int blk_t0, blk_nt, blk_slots;

@@ -213,16 +213,6 @@ static __device__ inline void layout_reduce(const LayoutArgs& a, int32_t* s_tot,
 // barriers.
 constexpr int kNotifyWaves = kNotifyThreads / 64;
 
-__host__ __device__ inline int sort_mask_words(int tb) { return (tb + 63) / 64; }
-
-// LDS words of the sort: token masks [E][mask words] (64-bit; one word of
-// padding so that they start 8-byte aligned wherever the area starts), ids
-// [cap_b], expert counts [E], masked counts per 64 slots [cap_b / 64 + 1],
-// the routed total and a repeat flag.
-__host__ __device__ inline size_t sort_lds_words(int tb, int cap_b, int E) {
-    return 1 + 2 * (size_t)E * sort_mask_words(tb) + (size_t)cap_b + (size_t)E + (size_t)cap_b / 64 + 3;
-}
-
 // Exclusive scan of v[0..n) in place by one wave (n <= 64 * 64), returning
 // the total in every lane.
 static __device__ inline int32_t wave_exclusive_scan(int32_t* v, int n) {

@@ -72,6 +72,18 @@ struct DispatchPlan {
 
 constexpr int kMaxDispatchThreads = 1024;
 
+// Static LDS of a push scatter workgroup (both scatter kernels).
+struct ScatterSmem {
+    int32_t pre[kMaxBlockSlots];   // counts of the slot's expert in earlier tiles
+    int32_t base[kMaxBlockSlots];  // expert_offsets[e]
+    int32_t len[kMaxBlockSlots];   // tokens_per_expert[e]
+    int32_t rows[kMaxBlockSlots + 8];  // receive row of each slot of the workgroup, -1 if none
+                                       // (8 spare entries: the stores read rows 8 at a time)
+    int32_t routed_tok[kMaxBlockTokens];  // nonzero if the token has a receive row
+    int32_t routed;
+    uint32_t err;
+};
+
 // Block-pull dispatch.  The tokens are cut into nblk blocks of tb tokens
 // (the last one may be shorter), and block b is copied by workgroups that the
 // hardware's round-robin dispatch places on XCD b % kXcds: a block's source
@@ -104,6 +116,16 @@ constexpr int kPullMaxBlocks = 256;               // a row's count prefix is one
 constexpr int kPullMinBlockTokens = 32;
 constexpr int kPullMaskWords = 4096;              // the sort's token masks: E * ceil(tb / 64) 64-bit words at most
 constexpr int kNotifyThreads = 1024;              // lanes of a notify workgroup (16 waves)
+
+__host__ __device__ inline int sort_mask_words(int tb) { return (tb + 63) / 64; }
+
+// LDS words of the sort: token masks [E][mask words] (64-bit; one word of
+// padding so that they start 8-byte aligned wherever the area starts), ids
+// [cap_b], expert counts [E], masked counts per 64 slots [cap_b / 64 + 1],
+// the routed total and a repeat flag.
+__host__ __device__ inline size_t sort_lds_words(int tb, int cap_b, int E) {
+    return 1 + 2 * (size_t)E * sort_mask_words(tb) + (size_t)cap_b + (size_t)E + (size_t)cap_b / 64 + 3;
+}
 
 // One entry of a block's sorted list: flat slot t * k + j and its expert
 // (-1 for a masked or invalid slot).
@@ -139,6 +161,20 @@ DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
 moedisp_shape group_rows_shape(const moedisp_shape& s);
 CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row);
 WsPlan plan_workspace(const moedisp_shape& s);
+
+struct SmallPlan {
+    int supported;    // T * k and the LDS tables within the path's bounds
+    int col_splits, split_units, threads;
+    long long blocks;
+    size_t lds_bytes;
+};
+SmallPlan plan_small(const moedisp_shape& s);
+
+struct LayoutNotifyPlan {
+    int fused;       // tile counts in the layout's workgroups (else two calls)
+    int tile_shift;  // log2 of the dispatch tile
+};
+LayoutNotifyPlan plan_layout_notify(const moedisp_shape& s);
 inline int layout_tokens_per_block(const moedisp_shape& s) { return kLayoutThreads / s.topk; }
 // LDS of a layout workgroup (tiles_per_block > 0 with the notify phase folded in)
 inline size_t layout_lds_bytes(int E, int G, int k, int tokens_per_block, int tiles_per_block) {

@@ -13,7 +13,7 @@ from combine_ep_get_dispatch_amd import binding as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moedisp.h")
-CALIB_HEADER = os.path.join(ROOT, "include", "moedisp_calib.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "moedisp_tools.h")
 
 
 @pytest.fixture(scope="module")
