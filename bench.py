@@ -6,30 +6,45 @@ notify phase of the same routing) + ep_dispatch_scatter + ep_combine (bf16
 out) over one batch of the DeepSeek-V3-shaped prefill workload (T=4096
 tokens, H=7168 bf16, E=256 experts in G=8 groups, top-8, uniform routing).
 Inputs and the stand-in expert outputs are resident in HBM before the timed
-region; the timed region is exactly K steps between two device
-synchronisations.  HIP events on the launch stream bracket the scatter kernel
-of every timed step (timing-only events without the system-scope cache fence,
-which a default event adds between the kernels it separates); the dominant
-kernel's algorithmic bytes over its mean duration give the roofline entry,
-with the HBM bytes measured by rocprofv3 counters (profiles/hbm_traffic.json)
-when they were taken on the current kernel sources.  Untimed passes of K
-steps give the other phases: the separate calls (ep_get_dispatch_layout,
-ep_dispatch_notify, ep_dispatch_scatter, ep_combine) with events between every
-call, the same calls with events only around dispatch + combine (the
-dispatch_combine figure: the events between the calls add their own time to
-each phase), full steps timing the fused layout + notify call, and a cold
-pass that reads
-512 MiB before each step (back to back, the source rows stay in the 256 MB
-MALL from one step to the next; the cold pass reports the step with nothing
-of its inputs cached).  The CPU oracle, timed on a bounded sample of the same
-workload on the host, is the reported baseline.
+region.
 
-Further legs, reported beside the headline (each can be skipped): the other
-workloads (skewed routing, fp8 decode, Mixtral shape), quantise-on-dispatch
-(FP32 and UE8M0 block scales), the group-deduplicated path, decode-step
-latency (four calls, the small-batch path, and that path from a HIP graph),
-a plain-copy bandwidth probe, and a write probe (4 KiB chunks in address
-order and permuted) that brackets the scatter's achievable write rate.
+Cache policy of the headline: cold.  Before every step, warm-up and timed
+alike, the GPU reads a 512 MiB buffer (twice the 256 MB MALL), so nothing of
+the step's inputs is left in the MALL or the L2s; the read lies outside the
+step's events.  (A read, not a write: written flush data would sit dirty in
+the MALL and be written back during the step.)  Back to back, the source
+rows x (58.7 MB) stay in the MALL from one step to the next: those warm
+figures are reported beside the cold ones, under "warm".
+
+Timing.  Timing-only HIP events (created without the system-scope cache
+fence, which a default event adds between the kernels it separates) on the
+launch stream at four points of every step: before the layout + notify call,
+before the scatter, before the combine and after it.  Every figure is the
+median over the K timed steps, with the min and the mean beside it.
+value = T / median step time; ms_per_step = that median.  The timed region
+is exactly K steps, each with its flush read, between two device
+synchronisations; its wall time is timed_region_ms.
+
+dispatch_combine = the scatter and the combine (the dispatch's notify phase
+runs inside the layout call), between the events before the scatter and
+after the combine; its bytes are the two calls' algorithmic bytes (one copy
+per routed slot in each direction).
+
+roofline: the step's dominant kernel (the scatter's or the combine's, the
+longer one), its algorithmic bytes over its mean duration from the events
+around it, against the 8 TB/s peak; traffic = the HBM bytes rocprofv3's
+FETCH_SIZE and WRITE_SIZE counters measured for it (profiles/hbm_traffic.json)
+while they were taken on the current kernel sources.  Ceilings: the read,
+copy and 4 KiB-chunk write probes of include/moedisp_tools.h, timed in the
+same run; each bulk kernel is also reported against the time its read and
+write bytes take at the read probe's and the address-ordered write probe's
+rates.
+
+Further legs, each of which can be skipped: the other workloads (skewed
+routing, fp8 decode, Mixtral shape; cold and warm), quantise-on-dispatch (FP32
+and UE8M0 block scales), the group-deduplicated path, decode-step latency
+(four calls, the small-batch path, and that path from a HIP graph).  The CPU
+oracle, per phase on the host, is the reported baseline.
 
 Prints one JSON line.  `--gpus` above 1 is refused: the library runs one
 GPU's share of the path on one GPU.
@@ -39,6 +54,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import socket
 import subprocess
 import sys
 import time
@@ -50,7 +66,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "dispatch+combine tokens/s and HBM GB/s (% of peak) at T=4096 H=7168 E=256 k=8"
-COLD_FLUSH_BYTES = 512 << 20  # read before each step of the cold pass: twice the MALL
+COLD_FLUSH_BYTES = 512 << 20  # read before each step: twice the MALL
+TARGET_FRAC = 0.70            # dispatch + combine against the 8 TB/s peak
+PROFILE = "profiles/dsv3_prefill_bench_trace.md"  # rocprofv3 summary of `bench.py --profile-run`
 
 
 def log(msg):
@@ -104,9 +122,42 @@ class TimingEvent:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
+    def close(self):
+        e, self.e = getattr(self, "e", None), None
+        if e and TimingEvent._hip is not None:
+            TimingEvent._hip.hipEventDestroy(e)
+
     def __del__(self):
-        if TimingEvent._hip is not None and self.e:
-            TimingEvent._hip.hipEventDestroy(self.e)
+        # at interpreter exit the runtime or the class may already be gone
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class EventGrid:
+    """rows x cols timing events, destroyed together."""
+
+    def __init__(self, rows, cols):
+        self.ev = [[TimingEvent() for _ in range(cols)] for _ in range(rows)]
+
+    def __getitem__(self, i):
+        return self.ev[i]
+
+    def us(self, a, b) -> np.ndarray:
+        """Microseconds from column a to column b, per row."""
+        return np.array([r[a].elapsed_time(r[b]) for r in self.ev]) * 1e3
+
+    def close(self):
+        for r in self.ev:
+            for e in r:
+                e.close()
+        self.ev = []
+
+
+def stats(a) -> dict:
+    a = np.asarray(a, dtype=np.float64)
+    return {"median": float(np.median(a)), "min": float(a.min()), "mean": float(a.mean()), "n": int(a.size)}
 
 
 def shape_of(M, W, wl):
@@ -114,13 +165,27 @@ def shape_of(M, W, wl):
     return M.moedisp_shape.make(wl.T, wl.H, wl.E, wl.G, wl.k, dt, wl.scale_block)
 
 
-def run_gpu(cid, steps, warmup, dev, cold=True):
-    """Time `steps` layout+dispatch+combine steps of config `cid` (and, with
-    `cold`, the cold pass)."""
+def box_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    uuid = getattr(p, "uuid", None)
+    return {"host": socket.gethostname(), "gpu": torch.cuda.get_device_name(0),
+            "arch": getattr(p, "gcnArchName", "?"), "uuid": str(uuid) if uuid is not None else None,
+            "cus": p.multi_processor_count}
+
+
+def scatter_kernel_name(M, shape) -> str:
+    return "moedisp_scatter_pull" if M.ep_plan_query(shape)["pull"] else "moedisp_scatter"
+
+
+def run_gpu(cid, steps, warmup, dev, warm=True, split=True):
+    """Cold steps of config `cid` (the timed region), then untimed passes:
+    warm steps back to back, and cold steps of the separate calls (layout,
+    notify, scatter, combine) for the per-call figures."""
     import torch
     import combine_ep_get_dispatch_amd as M
     from combine_ep_get_dispatch_amd import workloads as W
-    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS, algorithmic_bytes
+    from combine_ep_get_dispatch_amd.traffic import algorithmic_bytes
 
     wl = W.config(cid)
     shape = shape_of(M, W, wl)
@@ -136,173 +201,120 @@ def run_gpu(cid, steps, warmup, dev, cold=True):
         raise RuntimeError(f"device status {st} on config {cid}")
     R = int(bufs.expert_offsets[-1].item())
     offs = bufs.expert_offsets.cpu().numpy()
-    row_expert = W.row_experts(offs)
     eo = torch.zeros((wl.T * wl.k, wl.H), dtype=torch.bfloat16, device=dev)
     rs = bufs.recv_scales[:R] if bufs.recv_scales is not None else None
-    eo[:R] = W.expert_outputs(wl, bufs.recv_x[:R], rs, row_expert, device=dev)
+    eo[:R] = W.expert_outputs(wl, bufs.recv_x[:R], rs, W.row_experts(offs), device=dev)
     del rs
 
     stream = torch.cuda.current_stream()
+    flush = torch.ones(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev).view(torch.int32)
+    sink = torch.empty((), dtype=torch.int32, device=dev)
 
-    # The timed step: ep_get_dispatch_layout_notify (the layout and the
-    # dispatch's notify phase of the same routing, in two launches where the
-    # shape allows), ep_dispatch_scatter, ep_combine.  `ev` (optional) gets
-    # events before and after the scatter, the dominant kernel.
-    def step_fused(ev=None):
+    def flush_caches():
+        torch.amax(flush, dim=0, out=sink)
+
+    # the step; `ev` (optional) gets events before layout_notify, before the
+    # scatter, before the combine and after it
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
         bufs.layout_notify(idx, stream)
         if ev is not None:
-            ev[0].record(stream)
+            ev[1].record(stream)
         bufs.dispatch_scatter(x, xs, idx, w, stream)
         if ev is not None:
-            ev[1].record(stream)
-        bufs.combine(eo, out, M.BF16, True, stream)
-
-    # The same step with the layout and the notify phase as separate calls,
-    # for the per-phase times (untimed passes).  `ev` holds events recorded at
-    # the positions named in `at` (0 before the layout, 1 before notify, 2
-    # before the scatter, 3 before the combine, 4 after it).
-    def step(ev=None, at=()):
-        if 0 in at:
-            ev[0].record(stream)
-        bufs.layout(idx, stream)
-        if 1 in at:
-            ev[1].record(stream)
-        bufs.dispatch_notify(idx, stream)
-        if 2 in at:
             ev[2].record(stream)
-        bufs.dispatch_scatter(x, xs, idx, w, stream)
-        if 3 in at:
-            ev[3].record(stream)
         bufs.combine(eo, out, M.BF16, True, stream)
-        if 4 in at:
-            ev[4].record(stream)
+        if ev is not None:
+            ev[3].record(stream)
 
+    def phases(g: EventGrid) -> dict:
+        d = {"layout_notify_us": g.us(0, 1), "scatter_us": g.us(1, 2), "combine_us": g.us(2, 3),
+             "dc_us": g.us(1, 3), "step_us": g.us(0, 3)}
+        return {k: stats(v) for k, v in d.items()}
+
+    # --- timed region: cold steps ---------------------------------------
     for _ in range(warmup):
-        step_fused()
+        flush_caches()
+        step()
     torch.cuda.synchronize()
-    # timed region: events bracket the scatter of every step
-    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
+    g = EventGrid(steps, 4)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step_fused(evs[i])
+        flush_caches()
+        step(g[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     st = bufs.status()
     if st:
-        raise RuntimeError(f"device status {st} after timed steps on config {cid}")
-    elapsed = t1 - t0
-    sct = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3  # us
-    # untimed pass: the separate calls with events between every call, for the
-    # layout, notify and combine phases
-    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(evs[i], (0, 1, 2, 3, 4))
-    torch.cuda.synchronize()
+        raise RuntimeError(f"device status {st} after the timed steps on config {cid}")
+    cold = phases(g)
+    g.close()
+    res_warm = None
+    if warm:  # untimed: back to back
+        for _ in range(max(2, warmup // 2)):
+            step()
+        g = EventGrid(steps, 4)
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step(g[i])
+        torch.cuda.synchronize()
+        res_warm = phases(g)
+        g.close()
+    calls = None
+    if split:  # untimed, cold: the separate calls, events between every call
+        n = min(steps, 50)
+        g = EventGrid(n, 5)
+        torch.cuda.synchronize()
+        for i in range(n):
+            flush_caches()
+            g[i][0].record(stream)
+            bufs.layout(idx, stream)
+            g[i][1].record(stream)
+            bufs.dispatch_notify(idx, stream)
+            g[i][2].record(stream)
+            bufs.dispatch_scatter(x, xs, idx, w, stream)
+            g[i][3].record(stream)
+            bufs.combine(eo, out, M.BF16, True, stream)
+            g[i][4].record(stream)
+        torch.cuda.synchronize()
+        calls = {"layout_us": stats(g.us(0, 1)), "dispatch_notify_us": stats(g.us(1, 2)),
+                 "dispatch_scatter_us": stats(g.us(2, 3)), "combine_us": stats(g.us(3, 4)),
+                 "dispatch_us": stats(g.us(1, 3))}
+        g.close()
     st = bufs.status()
     if st:
-        raise RuntimeError(f"device status {st} after the phase pass on config {cid}")
-    lay = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    ntf = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    com = np.array([e[3].elapsed_time(e[4]) for e in evs]) * 1e3
-    # untimed pass: dispatch + combine as one block, events only before the
-    # notify phase and after the combine (events between the calls add their
-    # own time to each phase)
-    evs = [[TimingEvent() for _ in range(5)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        step(evs[i], (1, 4))
-    torch.cuda.synchronize()
-    st = bufs.status()
-    if st:
-        raise RuntimeError(f"device status {st} after the dispatch + combine pass on config {cid}")
-    dcb = np.array([e[1].elapsed_time(e[4]) for e in evs]) * 1e3
-    # untimed pass: full steps, with events around the fused layout + notify
-    # call only
-    evs = [[TimingEvent() for _ in range(2)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        evs[i][0].record(stream)
-        bufs.layout_notify(idx, stream)
-        evs[i][1].record(stream)
-        bufs.dispatch_scatter(x, xs, idx, w, stream)
-        bufs.combine(eo, out, M.BF16, True, stream)
-    torch.cuda.synchronize()
-    lnt = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    # untimed pass, cold: 512 MiB read before each step, so nothing of the
-    # step's inputs is left in the 256 MB MALL or the L2s (back to back, the
-    # source rows x stay in the MALL from one step to the next).  A read, not
-    # a write: written flush data would sit dirty in the MALL and be written
-    # back during the step, which measured 12 us (config 2) to 20 us
-    # (config 5) on the scatter that a clean cache does not cost.
-    flush = torch.ones(COLD_FLUSH_BYTES if cold else 0, dtype=torch.uint8, device=dev).view(torch.int32)
-    sink = torch.empty((), dtype=torch.int32, device=dev)
-    n_cold = min(steps, 50) if cold else 0
-    evs = [[TimingEvent() for _ in range(4)] for _ in range(n_cold)]
-    torch.cuda.synchronize()
-    for i in range(n_cold):
-        torch.amax(flush, dim=0, out=sink)
-        evs[i][0].record(stream)
-        bufs.layout_notify(idx, stream)
-        evs[i][1].record(stream)
-        bufs.dispatch_scatter(x, xs, idx, w, stream)
-        evs[i][2].record(stream)
-        bufs.combine(eo, out, M.BF16, True, stream)
-        evs[i][3].record(stream)
-    torch.cuda.synchronize()
-    st = bufs.status()
-    if st:
-        raise RuntimeError(f"device status {st} after the cold pass on config {cid}")
-    cold_lnt = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    cold_sct = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
-    cold_com = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e3
-    del flush
-    dis = ntf + sct
+        raise RuntimeError(f"device status {st} after the untimed passes on config {cid}")
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
-    ms_step = elapsed / steps * 1e3
-    res = dict(
-        config=cid, workload=wl.name, T=wl.T, H=wl.H, E=wl.E, G=wl.G, k=wl.k, x_dtype=wl.x_dtype, R=R,
-        routing=wl.meta["routing"], mask_frac=wl.meta["mask_frac"],
-        ms_per_step=ms_step, tokens_per_s=wl.T / (ms_step * 1e-3),
-        step_gbps=B["step"] / (ms_step * 1e-3) / 1e9,
-        layout_us=float(lay.mean()), dispatch_us=float(dis.mean()), combine_us=float(com.mean()),
-        notify_us=float(ntf.mean()), scatter_us=float(sct.mean()), layout_notify_us=float(lnt.mean()),
-        dispatch_us_min=float(dis.min()), combine_us_min=float(com.min()),
-        dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
-        combine_gbps=B["combine"] / (com.mean() * 1e-6) / 1e9,
-        dc_us=float(dcb.mean()), dc_us_min=float(dcb.min()),
-        dc_phase_sum_us=float(dis.mean() + com.mean()),
-        dc_tokens_per_s=wl.T / (dcb.mean() * 1e-6),
-        bytes=B,
-    )
-    # the pages' own byte conventions, for context: tokens x hidden per phase
-    # (their bench's per-rank count) and one row per routed copy
-    tok_row = wl.T * wl.H * x_elt
-    res["pages_convention_gbps"] = dict(
-        tokens_x_hidden=dict(dispatch=tok_row / (dis.mean() * 1e-6) / 1e9,
-                             combine=wl.T * wl.H * 2 / (com.mean() * 1e-6) / 1e9),
-        routed_rows_x_hidden=dict(dispatch=R * wl.H * x_elt / (dis.mean() * 1e-6) / 1e9,
-                                  combine=R * wl.H * 2 / (com.mean() * 1e-6) / 1e9))
-    res["dc_gbps"] = B["dispatch_combine"] / (dcb.mean() * 1e-6) / 1e9
-    res["dc_frac"] = res["dc_gbps"] / HBM_PEAK_GBPS
-    sc_bytes = B["dispatch"] - B["notify"] + B["combine"]
-    res["cold"] = None if not n_cold else dict(
-        flush_bytes=COLD_FLUSH_BYTES, steps=n_cold,
-        layout_notify_us=float(cold_lnt.mean()), scatter_us=float(cold_sct.mean()),
-        combine_us=float(cold_com.mean()),
-        step_us=float((cold_lnt + cold_sct + cold_com).mean()),
-        tokens_per_s=wl.T / ((cold_lnt + cold_sct + cold_com).mean() * 1e-6),
-        scatter_combine_frac=sc_bytes / ((cold_sct.mean() + cold_com.mean()) * 1e-6) / 1e9 / HBM_PEAK_GBPS,
-    )
-    del bufs, eo, out, x, xs, idx, w
+    res = dict(config=cid, workload=wl.name, T=wl.T, H=wl.H, E=wl.E, G=wl.G, k=wl.k, x_dtype=wl.x_dtype, R=R,
+               routing=wl.meta["routing"], mask_frac=wl.meta["mask_frac"], bytes=B,
+               kernels={"scatter": scatter_kernel_name(M, shape), "combine": "moedisp_combine"},
+               cold=cold, warm=res_warm, calls_cold=calls, timed_region_ms=(t1 - t0) * 1e3)
+    del bufs, eo, out, x, xs, idx, w, flush, sink
     torch.cuda.empty_cache()
     return res
 
 
+def dc_summary(res, which="cold"):
+    """dispatch_combine figures of one pass of run_gpu."""
+    from combine_ep_get_dispatch_amd.traffic import HBM_PEAK_GBPS
+    B = res["bytes"]
+    ph = res[which]
+    dc_bytes = B["dispatch"] - B["notify"] + B["combine"]
+    us = ph["dc_us"]["median"]
+    gbps = dc_bytes / (us * 1e-6) / 1e9
+    return {"us": us, "us_min": ph["dc_us"]["min"], "us_mean": ph["dc_us"]["mean"],
+            "tokens_per_s": res["T"] / (us * 1e-6), "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+            "frac_at_min": dc_bytes / (ph["dc_us"]["min"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, "bytes": dc_bytes,
+            "scatter_us": ph["scatter_us"]["median"], "combine_us": ph["combine_us"]["median"],
+            "calls": "ep_dispatch_scatter + ep_combine (the notify phase runs in ep_get_dispatch_layout_notify)"}
+
+
 def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
-    """Time quantise-on-dispatch (notify + quantising scatter) on config `cid`."""
+    """Quantise-on-dispatch (notify + quantising scatter) on config `cid`,
+    back to back; medians over `steps`."""
     import torch
     import combine_ep_get_dispatch_amd as M
     from combine_ep_get_dispatch_amd import workloads as W
@@ -313,34 +325,31 @@ def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
     x, _, idx, w = make_inputs(wl, dev)
     bufs.layout(idx)
     bufs.dispatch_quant(x, idx, w)
-    st = bufs.status()
-    if st:
-        raise RuntimeError(f"device status {st} on quantised config {cid}")
+    if bufs.status():
+        raise RuntimeError(f"device status on quantised config {cid}")
     R = int(bufs.expert_offsets[-1].item())
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         bufs.dispatch_notify(idx, stream)
         bufs.dispatch_scatter_quant(x, idx, w, stream)
-    evs = [[TimingEvent() for _ in range(3)] for _ in range(steps)]
+    g = EventGrid(steps, 3)
     torch.cuda.synchronize()
     for i in range(steps):
-        evs[i][0].record(stream)
+        g[i][0].record(stream)
         bufs.dispatch_notify(idx, stream)
-        evs[i][1].record(stream)
+        g[i][1].record(stream)
         bufs.dispatch_scatter_quant(x, idx, w, stream)
-        evs[i][2].record(stream)
+        g[i][2].record(stream)
     torch.cuda.synchronize()
     if bufs.status():
         raise RuntimeError(f"device status after quantised steps on config {cid}")
-    ntf = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    sct = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    ntf, sct, dis = np.median(g.us(0, 1)), np.median(g.us(1, 2)), np.median(g.us(0, 2))
+    g.close()
     B = algorithmic_bytes_quant(wl.T, wl.H, wl.E, wl.k, R, block, 4 if fmt == M.SCALE_FP32 else 1)
-    dis = ntf + sct
     res = dict(workload=wl.name, block=block, scale_fmt="fp32" if fmt == M.SCALE_FP32 else "ue8m0", R=R,
-               notify_us=float(ntf.mean()), scatter_us=float(sct.mean()), dispatch_us=float(dis.mean()),
-               dispatch_tokens_per_s=wl.T / (dis.mean() * 1e-6),
-               dispatch_gbps=B["dispatch"] / (dis.mean() * 1e-6) / 1e9,
-               scatter_gbps=B["scatter"] / (sct.mean() * 1e-6) / 1e9, bytes=B)
+               cache="warm", notify_us=float(ntf), scatter_us=float(sct), dispatch_us=float(dis),
+               dispatch_tokens_per_s=wl.T / (dis * 1e-6), dispatch_gbps=B["dispatch"] / (dis * 1e-6) / 1e9,
+               scatter_gbps=B["scatter"] / (sct * 1e-6) / 1e9, bytes=B)
     res["scatter_frac"] = res["scatter_gbps"] / HBM_PEAK_GBPS
     del bufs, x, idx, w
     torch.cuda.empty_cache()
@@ -348,8 +357,9 @@ def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
 
 
 def run_gpu_groups(cid, steps, warmup, dev):
-    """Time the group-deduplicated path on config `cid`: layout, group
-    dispatch, local expert permutation, local reduce, group combine."""
+    """The group-deduplicated path on config `cid`: layout, group dispatch,
+    local expert permutation, local reduce, group combine; back to back,
+    medians over `steps`."""
     import torch
     import combine_ep_get_dispatch_amd as M
     from combine_ep_get_dispatch_amd import workloads as W
@@ -377,25 +387,27 @@ def run_gpu_groups(cid, steps, warmup, dev):
     for _ in range(warmup):
         for c in calls:
             c()
-    evs = [[TimingEvent() for _ in range(len(calls) + 1)] for _ in range(steps)]
+    g = EventGrid(steps, len(calls) + 1)
     torch.cuda.synchronize()
     for i in range(steps):
         for j, c in enumerate(calls):
-            evs[i][j].record(stream)
+            g[i][j].record(stream)
             c()
-        evs[i][-1].record(stream)
+        g[i][-1].record(stream)
     torch.cuda.synchronize()
     if bufs.status():
         raise RuntimeError(f"device status after the group path steps, config {cid}")
-    us = np.array([[e[j].elapsed_time(e[j + 1]) * 1e3 for j in range(len(calls))] for e in evs]).mean(axis=0)
+    us = np.array([np.median(g.us(j, j + 1)) for j in range(len(calls))])
+    total = float(np.median(g.us(1, len(calls))))
+    g.close()
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
     B = algorithmic_bytes_groups(wl.T, wl.H, wl.E, wl.G, wl.k, R, Rg, x_elt, wl.scale_block)
     names = ["layout", "dispatch_groups", "permute", "reduce", "combine_groups"]
-    res = dict(workload=wl.name, R=R, R_g=Rg, us={n: float(u) for n, u in zip(names, us)})
+    res = dict(workload=wl.name, R=R, R_g=Rg, cache="warm", us={n: float(u) for n, u in zip(names, us)})
     res["gbps"] = {n: B[n] / (res["us"][n] * 1e-6) / 1e9 for n in names[1:]}
-    res["frac"] = {n: g / HBM_PEAK_GBPS for n, g in res["gbps"].items()}
-    res["dispatch_combine_us"] = float(us[1:].sum())
-    res["tokens_per_s"] = wl.T / (us[1:].sum() * 1e-6)
+    res["frac"] = {n: v / HBM_PEAK_GBPS for n, v in res["gbps"].items()}
+    res["dispatch_combine_us"] = total
+    res["tokens_per_s"] = wl.T / (total * 1e-6)
     del bufs, gb, x, xs, idx, w, eo, part, out
     torch.cuda.empty_cache()
     return res
@@ -443,9 +455,12 @@ def run_gpu_decode(cid, steps, warmup, dev):
             fn(stream)
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / steps
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        e0.close()
+        e1.close()
+        return us
 
-    res = dict(workload=wl.name, T=wl.T, R=R)
+    res = dict(workload=wl.name, T=wl.T, R=R, cache="warm")
     res["four_calls_us"] = per_step(four)
     res["small_us"] = per_step(small)
     side = torch.cuda.Stream()
@@ -464,13 +479,14 @@ def run_gpu_decode(cid, steps, warmup, dev):
     res["small_graph_us"] = per_step(lambda stream: graph.replay()) / per_graph
     # the small-batch dispatch alone, events around each call
     stream = torch.cuda.current_stream()
-    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
-    for a, b in ev:
-        a.record(stream)
+    g = EventGrid(steps, 2)
+    for i in range(steps):
+        g[i][0].record(stream)
         bufs.layout_dispatch_small(x, xs, idx, w, stream)
-        b.record(stream)
+        g[i][1].record(stream)
     torch.cuda.synchronize()
-    res["small_dispatch_us"] = float(np.median([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    res["small_dispatch_us"] = float(np.median(g.us(0, 1)))
+    g.close()
     if bufs.status():
         raise RuntimeError(f"device status after the decode steps, config {cid}")
     x_elt = 1 if wl.x_dtype == W.X_FP8 else 2
@@ -482,60 +498,58 @@ def run_gpu_decode(cid, steps, warmup, dev):
     return res
 
 
-def probe_fill_gbps(dev, nbytes=32768 * 14336, reps=20):
-    """HBM write bandwidth of 4 KiB chunks written in address order and in a
-    permuted order (ep_probe_fill), over a buffer the size of the
-    T=4096 H=7168 k=8 receive rows: the two ends between which the scatter's
-    row writes (one moving write front per expert segment) fall."""
+def probe_ceilings(dev, reps=20):
+    """Achievable HBM bandwidth in this run: the read-only stream and the
+    copy of 1 GiB, and 4 KiB-chunk writes in address order and permuted over
+    the size of the T=4096 H=7168 k=8 receive rows (GB/s, read + write bytes
+    for the copy).  Medians of `reps` launches, events around each."""
     import torch
     import combine_ep_get_dispatch_amd as M
-    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    fill_n = 32768 * 14336
     stream = torch.cuda.current_stream()
-    res = {"bytes": nbytes}
-    for shuffled, tag in ((False, "sequential_4k"), (True, "shuffled_4k")):
+
+    def rate(fn, nbytes):
         for _ in range(3):
-            M.ep_probe_fill(dst, nbytes, shuffled)
-        s, e = TimingEvent(), TimingEvent()
+            fn()
+        g = EventGrid(reps, 2)
         torch.cuda.synchronize()
-        s.record(stream)
-        for _ in range(reps):
-            M.ep_probe_fill(dst, nbytes, shuffled)
-        e.record(stream)
+        for i in range(reps):
+            g[i][0].record(stream)
+            fn()
+            g[i][1].record(stream)
         torch.cuda.synchronize()
-        us = s.elapsed_time(e) * 1e3 / reps
-        res[tag] = nbytes / (us * 1e-6) / 1e9
-    del dst
+        us = float(np.median(g.us(0, 1)))
+        g.close()
+        return nbytes / (us * 1e-6) / 1e9
+
+    res = {"read_gbps": rate(lambda: M.ep_probe_read(src, n, sink), n),
+           "copy_gbps": rate(lambda: M.ep_probe_copy(dst, src, n), 2 * n),
+           "write_seq_4k_gbps": rate(lambda: M.ep_probe_fill(dst, fill_n, False), fill_n),
+           "write_perm_4k_gbps": rate(lambda: M.ep_probe_fill(dst, fill_n, True), fill_n),
+           "bytes": {"read": n, "copy": 2 * n, "write": fill_n}}
+    del src, dst, sink
     torch.cuda.empty_cache()
     return res
 
 
-def probe_copy_gbps(dev, nbytes=1 << 30, reps=20):
-    """Achievable HBM copy bandwidth (read + write bytes) with the library's
-    plain 16-byte copy kernel."""
-    import torch
-    import combine_ep_get_dispatch_amd as M
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        M.ep_probe_copy(dst, src, nbytes)
-    s, e = TimingEvent(), TimingEvent()
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    s.record(stream)
-    for _ in range(reps):
-        M.ep_probe_copy(dst, src, nbytes)
-    e.record(stream)
-    torch.cuda.synchronize()
-    us = s.elapsed_time(e) * 1e3 / reps
-    del src, dst
-    torch.cuda.empty_cache()
-    return 2 * nbytes / (us * 1e-6) / 1e9
+def kernel_rw_bytes(B, T, H, k, R, x_elt, scale_block):
+    """Read and write bytes of the scatter and the combine (the algorithmic
+    accounting of traffic.algorithmic_bytes, split by direction)."""
+    row = H * x_elt + ((H // scale_block) * 4 if scale_block else 0)
+    scat_w = R * row + 2 * R * 4 + T * k * 4
+    comb_w = T * H * 2
+    scat = B["dispatch"] - B["notify"]
+    return {"scatter": (scat - scat_w, scat_w), "combine": (B["combine"] - comb_w, comb_w)}
 
 
-def cpu_baseline(budget_s: float = 12.0):
-    """The CPU oracle (single-threaded C) on the same DeepSeek-V3-shaped
-    workload, full steps of layout + dispatch + combine until about
-    `budget_s` seconds of oracle time have run (at least one step)."""
+def cpu_baseline(reps: int = 3):
+    """The CPU oracle (single-threaded C) on the DeepSeek-V3-shaped workload,
+    each phase (layout, dispatch, combine) once untimed and then `reps`
+    times; medians per phase, tokens/s of their sum."""
     import oracle
     from combine_ep_get_dispatch_amd import workloads as W
     import torch
@@ -548,25 +562,32 @@ def cpu_baseline(budget_s: float = 12.0):
     R = int(d["expert_offsets"][-1])
     eo = W.expert_outputs(wl, d["recv_x"][:R], None, W.row_experts(d["expert_offsets"]))
     eo_bits = eo.view(torch.int16).numpy().view(np.uint16)
+    weights, s2r = d["recv_weights"][:R].copy(), d["slot_to_row"].copy()
     del d
-    times = []
-    t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 20):
-        t0 = time.perf_counter()
-        orc.layout(wl.topk_idx, wl.E, wl.G)
-        dd = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
-        orc.combine(eo_bits, dd["recv_weights"][:R], dd["slot_to_row"], want_f32=False, want_bf16=True)
-        times.append(time.perf_counter() - t0)
-        del dd
-    per_step = float(np.median(times))
+
+    def timed(fn):
+        fn()
+        t = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            t.append(time.perf_counter() - t0)
+        return {"median": float(np.median(t)), "min": float(np.min(t))}
+
+    ph = {"layout": timed(lambda: orc.layout(wl.topk_idx, wl.E, wl.G)),
+          "dispatch": timed(lambda: orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)),
+          "combine": timed(lambda: orc.combine(eo_bits, weights, s2r, want_f32=False, want_bf16=True))}
+    per_step = sum(p["median"] for p in ph.values())
     try:
         cpu = subprocess.run(["lscpu"], capture_output=True, text=True).stdout
         model = next((l.split(":", 1)[1].strip() for l in cpu.splitlines() if l.startswith("Model name")), "?")
     except Exception:
         model = "?"
     return dict(value=wl.T / per_step, unit="tokens/s", cores=1, kind="oracle",
-                sample=(f"{len(times)} full steps (layout+dispatch+combine) of the T=4096 H=7168 E=256 k=8 "
-                        f"workload, median {per_step:.2f} s/step; 1 thread of {os.cpu_count()} host cores ({model})"))
+                sample=(f"the T=4096 H=7168 E=256 k=8 workload, each phase 1 untimed + {reps} timed runs, "
+                        f"median per phase ({per_step:.2f} s per step); 1 thread of {os.cpu_count()} host cores "
+                        f"({model})"),
+                phases_s=ph, host_cores=os.cpu_count(), cpu_model=model)
 
 
 def main():
@@ -577,13 +598,18 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload for the headline line (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true")
-    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip the bandwidth ceiling probes")
     ap.add_argument("--no-quant", action="store_true", help="skip the quantise-on-dispatch timings")
     ap.add_argument("--no-groups", action="store_true", help="skip the group-deduplicated path timings")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-latency timings")
-    ap.add_argument("--no-cold", action="store_true",
-                    help="skip the cold passes (512 MiB read before each step)")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm (back-to-back) pass")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="the headline config's cold steps only (every leg and pass above off): the command "
+                         "whose rocprofv3 kernel trace the roofline entry is checked against")
     args = ap.parse_args()
+    if args.profile_run:
+        args.no_cpu_baseline = args.no_other_workloads = args.no_probe = True
+        args.no_quant = args.no_groups = args.no_decode = args.no_warm = True
 
     if args.gpus != 1:
         print(f"bench.py runs one GPU's share of the path on one GPU; --gpus {args.gpus} is not supported "
@@ -596,10 +622,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    log(f"[bench] config {args.config}: {args.warmup} warmup + {args.steps} timed steps")
-    main_res = run_gpu(args.config, args.steps, args.warmup, dev, cold=not args.no_cold)
-    log(f"[bench] config {args.config}: {main_res['ms_per_step']*1e3:.1f} us/step, "
-        f"dispatch {main_res['dispatch_us']:.1f} us, combine {main_res['combine_us']:.1f} us")
+    log(f"[bench] config {args.config}: {args.warmup} warmup + {args.steps} timed cold steps")
+    main_res = run_gpu(args.config, args.steps, args.warmup, dev, warm=not args.no_warm,
+                       split=not args.profile_run)
+    cold = main_res["cold"]
+    step_us = cold["step_us"]["median"]
+    log(f"[bench] config {args.config}: cold step {step_us:.1f} us (median), scatter "
+        f"{cold['scatter_us']['median']:.1f} us, combine {cold['combine_us']['median']:.1f} us")
 
     others = {}
     if not args.no_other_workloads:
@@ -607,11 +636,15 @@ def main():
             if cid == args.config:
                 continue
             log(f"[bench] config {cid}")
-            r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev, cold=not args.no_cold)
-            others[r["workload"]] = {k: r[k] for k in ("T", "H", "E", "G", "k", "x_dtype", "routing", "R",
-                                                       "tokens_per_s", "dc_us", "dc_tokens_per_s", "dc_gbps", "dc_frac",
-                                                       "layout_us", "dispatch_us", "combine_us",
-                                                       "dispatch_gbps", "combine_gbps", "cold")}
+            r = run_gpu(cid, max(20, args.steps // 4), max(5, args.warmup // 4), dev, warm=not args.no_warm,
+                        split=False)
+            others[r["workload"]] = {
+                **{k: r[k] for k in ("T", "H", "E", "G", "k", "x_dtype", "routing", "R", "kernels")},
+                "tokens_per_s": r["T"] / (r["cold"]["step_us"]["median"] * 1e-6),
+                "step_us": r["cold"]["step_us"]["median"],
+                "dispatch_combine": dc_summary(r), "phases_us": {k: v["median"] for k, v in r["cold"].items()},
+                "warm": None if r["warm"] is None else {"dispatch_combine": dc_summary(r, "warm"),
+                                                        "step_us": r["warm"]["step_us"]["median"]}}
     quant = {}
     if not args.no_quant:
         import combine_ep_get_dispatch_amd as M
@@ -627,43 +660,53 @@ def main():
     if not args.no_decode:
         log("[bench] decode latency (config 4)")
         decode = run_gpu_decode(4, max(50, args.steps), max(10, args.warmup), dev)
-    probe = None if args.no_probe else probe_copy_gbps(dev)
-    if probe:
-        log(f"[bench] probe copy {probe:.0f} GB/s")
-    probe_w = None if args.no_probe else probe_fill_gbps(dev)
-    if probe_w:
-        log(f"[bench] probe write {probe_w['sequential_4k']:.0f} GB/s in address order, "
-            f"{probe_w['shuffled_4k']:.0f} GB/s permuted")
+    ceil = None
+    if not args.no_probe:
+        ceil = probe_ceilings(dev)
+        log(f"[bench] ceilings: read {ceil['read_gbps']:.0f}, copy {ceil['copy_gbps']:.0f}, 4 KiB writes "
+            f"{ceil['write_seq_4k_gbps']:.0f} in order / {ceil['write_perm_4k_gbps']:.0f} permuted GB/s")
 
-    # dominant kernel: the longer of the scatter kernel (which moves all of the
-    # dispatch's row bytes) and the combine kernel
+    # dominant kernel: the longer of the scatter (all of the dispatch's row
+    # bytes) and the combine; its mean duration from the events around it
     B = main_res["bytes"]
-    if main_res["scatter_us"] >= main_res["combine_us"]:
-        dom, dom_us = "moedisp_scatter", main_res["scatter_us"]
-        dom_bytes = B["dispatch"] - B["notify"]
-    else:
-        dom, dom_us, dom_bytes = "moedisp_combine", main_res["combine_us"], B["combine"]
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    x_elt = 1 if main_res["x_dtype"] == "fp8_e4m3" else 2
+    from combine_ep_get_dispatch_amd import workloads as W
+    wl_sb = W.config(args.config).scale_block
+    rw = kernel_rw_bytes(B, main_res["T"], main_res["H"], main_res["k"], main_res["R"], x_elt, wl_sb)
+    kern = {"scatter": (main_res["kernels"]["scatter"], cold["scatter_us"], sum(rw["scatter"])),
+            "combine": ("moedisp_combine", cold["combine_us"], sum(rw["combine"]))}
+    dom = max(kern, key=lambda n: kern[n][1]["mean"])
+    dom_name, dom_us, dom_bytes = kern[dom]
+    achieved = dom_bytes / (dom_us["mean"] * 1e-6) / 1e9
     from combine_ep_get_dispatch_amd.profiling import kernel_traffic, load_traffic
     measured = load_traffic(os.path.join(ROOT, "profiles", "hbm_traffic.json"))
     traffic = None
-    kt = kernel_traffic(measured, dom) if measured and measured.get("workload") == main_res["workload"] else None
+    kt = kernel_traffic(measured, dom_name) if measured and measured.get("workload") == main_res["workload"] else None
     if kt:
         traffic = kt["fetch_bytes"] + kt["write_bytes"]
+    vs_ceiling = None
+    if ceil:
+        vs_ceiling = {}
+        for n, (name, us, nbytes) in kern.items():
+            rd, wr = rw[n]
+            c_us = (rd / (ceil["read_gbps"] * 1e9) + wr / (ceil["write_seq_4k_gbps"] * 1e9)) * 1e6
+            vs_ceiling[n] = {"kernel": name, "ceiling_us": c_us, "us": us["median"], "frac": c_us / us["median"],
+                             "read_bytes": rd, "write_bytes": wr}
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
+        log("[bench] cpu baseline (oracle, per phase)")
         cpu = cpu_baseline()
 
+    dc = dc_summary(main_res)
     line = {
         "metric": METRIC,
-        "value": main_res["tokens_per_s"],
+        "value": main_res["T"] / (step_us * 1e-6),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_res["ms_per_step"],
+        "ms_per_step": step_us * 1e-3,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -673,24 +716,31 @@ def main():
                    "G": main_res["G"], "k": main_res["k"], "x_dtype": main_res["x_dtype"],
                    "routing": main_res["routing"], "step": "layout_notify+dispatch_scatter+combine",
                    "parallelism": "none"},
-        "hbm_gbps_step": main_res["step_gbps"],
-        "hbm_frac_step": main_res["step_gbps"] / HBM_PEAK_GBPS,
-        "dispatch_combine": {"us": main_res["dc_us"], "us_min": main_res["dc_us_min"],
-                             "tokens_per_s": main_res["dc_tokens_per_s"], "gbps": main_res["dc_gbps"],
-                             "frac": main_res["dc_frac"], "phase_sum_us": main_res["dc_phase_sum_us"]},
-        "phases_us": {"layout_notify": main_res["layout_notify_us"], "layout": main_res["layout_us"],
-                      "dispatch": main_res["dispatch_us"],
-                      "dispatch_notify": main_res["notify_us"], "dispatch_scatter": main_res["scatter_us"],
-                      "combine": main_res["combine_us"], "dispatch_min": main_res["dispatch_us_min"],
-                      "combine_min": main_res["combine_us_min"]},
-        "phases_gbps": {"dispatch": main_res["dispatch_gbps"], "combine": main_res["combine_gbps"]},
-        "cold": main_res["cold"],
-        "pages_convention_gbps": main_res["pages_convention_gbps"],
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic, "algorithmic_bytes": dom_bytes,
-                     "kernel_us": dom_us},
-        "probe_copy_gbps": probe,
-        "probe_write_gbps": probe_w,
+        "timing": {"statistic": "median over the timed steps (min, mean beside)",
+                   "cache": f"cold: {COLD_FLUSH_BYTES >> 20} MiB read before every step, outside its events",
+                   "events": "timing-only HIP events on the launch stream at the step's call boundaries",
+                   "timed_region_ms": main_res["timed_region_ms"], "box": box_info()},
+        "hbm_gbps_step": B["step"] / (step_us * 1e-6) / 1e9,
+        "hbm_frac_step": B["step"] / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+        "dispatch_combine": {**dc, "target_frac": TARGET_FRAC, "meets_target": dc["frac"] >= TARGET_FRAC},
+        "cold": {"step_us": step_us, "layout_notify_us": cold["layout_notify_us"]["median"],
+                 "scatter_us": cold["scatter_us"]["median"], "combine_us": cold["combine_us"]["median"],
+                 "dc_us": cold["dc_us"]["median"], "all": cold},
+        "warm": None if main_res["warm"] is None else {
+            "step_us": main_res["warm"]["step_us"]["median"],
+            "tokens_per_s": main_res["T"] / (main_res["warm"]["step_us"]["median"] * 1e-6),
+            "dispatch_combine": dc_summary(main_res, "warm"), "all": main_res["warm"]},
+        "calls_cold_us": main_res["calls_cold"],
+        "kernels": main_res["kernels"],
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes": dom_bytes, "kernel_us": dom_us["mean"],
+                     "kernel_us_median": dom_us["median"], "kernel_us_min": dom_us["min"],
+                     "kernel_us_source": ("mean of the HIP-event intervals around the kernel's call on its "
+                                          "launch stream over the timed cold steps"),
+                     "profile": PROFILE},
+        "ceilings_gbps": ceil,
+        "vs_ceiling": vs_ceiling,
         "other_workloads": others,
         "quant_dispatch": quant,
         "group_path": groups,
