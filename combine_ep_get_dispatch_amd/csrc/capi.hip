@@ -117,13 +117,17 @@ DispatchPlan plan_dispatch(const moedisp_shape& s) {
                         kCopyWorkgroupBytes);
 }
 
-// Receive rows per block-pull copy workgroup.  In the library's step at
-// T = 4096, H = 7168, k = 8 (notify, copy, combine) one row per workgroup
-// measured best both with nothing cached (copy 97 against 103 us for two
-// rows) and with the source rows in the MALL (96 against 95-100 us).
-#ifndef MOEDISP_PULL_ROWS_PER_WG
-#define MOEDISP_PULL_ROWS_PER_WG 1
-#endif
+// Block-pull copy workgroups: one receive row each, `units` 16-byte units
+// per lane.  Measured in the library's cold step (512 MiB read before each)
+// at T = 4096, H = 7168, k = 8: 3 units (320 lanes, 5 waves per row) copied
+// in 89 us, 2 units (448 lanes) in 94 us, 4 and 5 units (256 and 192 lanes)
+// in 98-100 us, 1 unit (896 lanes) in 172 us, and a wave per row (all 14
+// units of a lane in one pass, 20 rows per CU in flight) in 103-105 us: the
+// more rows a CU writes at once, the further the write stream strays from
+// address order, and the fewer, the more each row's dependent loads show.
+// With skewed routing (same shape) 3 units took 82.5 against 90.7 us.  Rows
+// of at most 512 units (H = 4096 bf16: 72.0 us against 72.8) keep 2 units.
+// Two rows per workgroup measured 3 us slower than one.
 
 // Block-pull plan: blocks of tb tokens whose source rows fit one XCD's L2,
 // as many blocks as XCDs or a multiple of it (every XCD gets the same number
@@ -147,13 +151,13 @@ PullPlan plan_pull(const moedisp_shape& s) {
     p.nblk = (int)nblk;
     p.cap_b = (int)(tb * k);
     p.cnt_stride = (p.nblk + 3) / 4 * 4;
-    p.units = 2;
+    p.units = row16 > 512 ? 3 : 2;
     int threads = ((row16 + p.units - 1) / p.units + 63) / 64 * 64;
     if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
     // an fp8 row's scales travel one per lane with the row
     if (scales_per_row(s) > threads) return p;
     p.threads = threads;
-    p.rpw = MOEDISP_PULL_ROWS_PER_WG;
+    p.rpw = 1;
     p.wpb = (p.cap_b + p.rpw - 1) / p.rpw;
     p.blocks = (long long)kXcds * p.wpb * ((p.nblk + kXcds - 1) / kXcds);
     p.use = 1;

@@ -622,10 +622,13 @@ hipError_t launch_scatter_pull(const DispatchArgs& a, hipStream_t stream) {
     const PullPlan& p = a.pull;
     if (!grid_fits(p.blocks, p.threads)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)p.blocks), block(p.threads);
-    if (p.rpw == 1)
+    if (p.rpw != 1) return hipErrorInvalidConfiguration;
+    if (p.units == 3)
+        hipLaunchKernelGGL((moedisp_scatter_pull<3, 1>), grid, block, 0, stream, a);
+    else if (p.units == 2)
         hipLaunchKernelGGL((moedisp_scatter_pull<2, 1>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((moedisp_scatter_pull<2, 2>), grid, block, 0, stream, a);
+        return hipErrorInvalidConfiguration;
     return hipGetLastError();
 }
 

@@ -101,9 +101,9 @@ struct PullPlan {
     int nblk;         // blocks (8 <= nblk <= kPullMaxBlocks)
     int cap_b;        // list entries per block (tb * k <= kPullMaxBlockSlots)
     int cnt_stride;   // ints per expert column of the per-block counts (>= nblk, multiple of 4)
-    int rpw;          // list entries (receive rows) per copy workgroup
+    int rpw;          // list entries (receive rows) per copy workgroup (1)
     int threads;      // copy workgroup lanes
-    int units;        // 16-byte units per lane and pass
+    int units;        // 16-byte units per lane and pass (2, or 3 for rows over 512 units)
     int wpb;          // copy workgroups per block: ceil(cap_b / rpw)
     long long blocks; // copy grid: kXcds * wpb * ceil(nblk / kXcds)
 };
