@@ -207,8 +207,8 @@ SmallPlan plan_small(const moedisp_shape& s) {
     SmallPlan p;
     memset(&p, 0, sizeof p);
     const long long n = (long long)s.num_tokens * s.topk;
-    p.lds_bytes = (size_t)(n + 2LL * s.num_experts + s.num_tokens) * sizeof(int32_t);
-    p.supported = n <= kFusedMaxSlots && p.lds_bytes <= 60 * 1024;
+    p.lds_bytes = (size_t)(2LL * s.num_experts) * sizeof(int32_t);  // the layout workgroup's tables
+    p.supported = n <= kFusedMaxSlots && (size_t)(n + 2LL * s.num_experts + s.num_tokens) * 4 <= 60 * 1024;
     const int row16 = (int)(row_bytes(s) / 16);
     int splits = 1;
     while ((long long)s.num_tokens * splits < 1024 && row16 / (splits * 2) >= kThreads / 2) splits *= 2;
@@ -982,7 +982,7 @@ const char* ep_status_string(int status) {
 
 // Upper bounds of the kernels' static LDS (their __shared__ declarations).
 constexpr int64_t kStaticLdsLayout = 16, kStaticLdsReduce = kMaxExperts * 4 + 16, kStaticLdsCount = 48,
-                  kStaticLdsNotify = 144, kStaticLdsFused = 464;
+                  kStaticLdsNotify = 144, kStaticLdsFused = 2816;
 
 static moedisp_launch_info launch_info(long long blocks, long long threads, size_t lds, int64_t static_lds) {
     moedisp_launch_info l;

@@ -30,6 +30,25 @@ static __device__ inline uint32_t div_const(uint32_t x, int shift, uint32_t magi
 }
 
 // Sum of v over the 64 lanes of the wave (every lane gets the sum).
+// Inclusive scan over the wave with DPP moves (no LDS round trip): sums
+// inside each 16-lane row (row_shr 1, 2, 4, 8), then row 0's total into
+// rows 1 and 3 and row 1's running total into rows 2 and 3 (row_bcast 15
+// and 31).  Lane i gets the sum of lanes 0..i; the wave sum is lane 63's.
+// Whole wave, all lanes active.
+static __device__ inline int32_t wave_inclusive_scan_dpp(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
+static __device__ inline int32_t wave_sum_dpp(int32_t v) {
+    return __builtin_amdgcn_readlane(wave_inclusive_scan_dpp(v), 63);
+}
+
 static __device__ inline int32_t wave_sum(int32_t v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
