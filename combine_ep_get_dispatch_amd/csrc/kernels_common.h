@@ -220,9 +220,10 @@ static __device__ inline void layout_reduce(const LayoutArgs& a, int32_t* s_tot,
 // of the block with the same expert.  With a bitmask per expert of the
 // block's tokens that route to it (LDS, built by 64-bit ORs), that number is
 // the popcount of the mask below the slot's token.  A token that repeats an
-// expert (invalid routing, which the layout reports) breaks that count; a
-// block with such a token counts each slot's earlier same-expert slots one
-// by one instead (slow, but the same order).  ls_b is one scan over the experts by
+// expert (invalid routing, which the layout reports) breaks that count; the
+// OR that finds the token's bit already set flags the block, which then
+// counts each slot's earlier same-expert slots one by one instead (slow, but
+// the same order).  ls_b is one scan over the experts by
 // one wave; a masked slot's position follows the routed ones, from one
 // ballot per 64 slots and one scan over those counts.  No atomic decides any
 // order (the ORs and the histogram adds commute), so the lists are
@@ -304,9 +305,9 @@ static __device__ inline uint32_t pull_sort(const DispatchArgs& a, int b, int32_
         if (e >= 0) {
             const int t = i / k;
             atomicAdd(&s_cnt[e], 1);
-            atomicOr(reinterpret_cast<unsigned long long*>(&s_mask[e * mw + (t >> 6)]), 1ull << (t & 63));
-            for (int q = t * k; q < i; ++q)
-                if (s_id[q] == e) *s_rep = 1;
+            // the token's bit already set: it repeats the expert
+            const unsigned long long bit = 1ull << (t & 63);
+            if (atomicOr(reinterpret_cast<unsigned long long*>(&s_mask[e * mw + (t >> 6)]), bit) & bit) *s_rep = 1;
         }
         const uint64_t masked = __ballot(valid && e < 0);
         if (lane == 0 && base + wave * 64 < ns) s_mc[(base >> 6) + wave] = (int32_t)__popcll(masked);
