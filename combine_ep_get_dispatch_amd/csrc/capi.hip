@@ -981,7 +981,7 @@ const char* ep_status_string(int status) {
 }
 
 // Upper bounds of the kernels' static LDS (their __shared__ declarations).
-constexpr int64_t kStaticLdsLayout = 16, kStaticLdsReduce = kMaxExperts * 4 + 16, kStaticLdsCount = 48,
+constexpr int64_t kStaticLdsLayout = 16, kStaticLdsReduce = kMaxExperts * 4 + kReduceThreads / 16, kStaticLdsCount = 48,
                   kStaticLdsNotify = 144, kStaticLdsFused = 2816;
 
 static moedisp_launch_info launch_info(long long blocks, long long threads, size_t lds, int64_t static_lds) {
@@ -1013,7 +1013,7 @@ int ep_plan_query(const moedisp_shape* s, moedisp_plan_info* info, size_t info_b
     const int tpb = layout_tokens_per_block(*s);
     info->layout_tokens_per_block = tpb;
     info->layout = launch_info(w.layout_blocks, kLayoutThreads, layout_lds_bytes(E, G, k, tpb, 0), kStaticLdsLayout);
-    info->layout_reduce = launch_info(1, kThreads, 0, kStaticLdsReduce);
+    info->layout_reduce = launch_info(1, kReduceThreads, 0, kStaticLdsReduce);
     // flat dispatch
     const DispatchPlan P = plan_dispatch(*s);
     info->tile_tokens = P.tile_tokens;

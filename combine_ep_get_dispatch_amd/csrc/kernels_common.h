@@ -186,11 +186,7 @@ static __device__ inline void layout_reduce(const LayoutArgs& a, int32_t* s_tot,
     const int lo = min(a.E, tid * per), hi = min(a.E, lo + per);
     int32_t run = 0;
     for (int i = lo; i < hi; ++i) run += s_tot[i];
-    int32_t incl = run;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    const int32_t incl = wave_inclusive_scan_dpp(run);
     if (lane == 63) s_wave[wave] = incl;
     __syncthreads();
     int32_t off = incl - run, total = 0;
@@ -241,18 +237,14 @@ static __device__ inline int32_t wave_exclusive_scan(int32_t* v, int n) {
     const int lo = min(n, lane * per), hi = min(n, lo + per);
     int32_t run = 0;
     for (int i = lo; i < hi; ++i) run += v[i];
-    int32_t incl = run;
-    for (int d = 1; d < 64; d <<= 1) {
-        const int32_t o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-    }
+    const int32_t incl = wave_inclusive_scan_dpp(run);
     int32_t off = incl - run;
     for (int i = lo; i < hi; ++i) {
         const int32_t c = v[i];
         v[i] = off;
         off += c;
     }
-    return __shfl(incl, 63);
+    return __builtin_amdgcn_readlane(incl, 63);
 }
 
 static __device__ inline uint32_t pull_sort(const DispatchArgs& a, int b, int32_t* lds) {

@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kLayoutThreads) void moedisp_layout_sort(LayoutSort
 
 // Sum of the partial counts in workgroup order (one workgroup; the kernel
 // boundary orders it after every partial), and expert_offsets when requested.
-__global__ __launch_bounds__(kThreads) void moedisp_layout_reduce(LayoutArgs a) {
+__global__ __launch_bounds__(kReduceThreads) void moedisp_layout_reduce(LayoutArgs a) {
     __shared__ int32_t s_tot[kMaxExperts];  // expert totals, for expert_offsets
-    __shared__ int32_t s_wave[kThreads / 64];
+    __shared__ int32_t s_wave[kReduceThreads / 64];
     layout_reduce(a, s_tot, s_wave);
 }
 
@@ -177,7 +177,7 @@ hipError_t launch_layout_sort(const LayoutSortArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_layout_reduce(const LayoutArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kReduceThreads), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -188,7 +188,7 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream, bool reduce) {
     hipLaunchKernelGGL(moedisp_layout, dim3(a.blocks), dim3(kLayoutThreads), lds, stream, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || !reduce) return e;
-    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(moedisp_layout_reduce, dim3(1), dim3(kReduceThreads), 0, stream, a);
     return hipGetLastError();
 }
 

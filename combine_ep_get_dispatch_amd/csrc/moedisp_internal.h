@@ -32,6 +32,7 @@ __device__ inline void stream_store(v4u v, v4u* row, uint32_t row_bytes, int uni
 
 constexpr int kThreads = 256;              // threads per workgroup (4 wave64s)
 constexpr int kLayoutThreads = 1024;       // layout: one lane per slot, kLayoutThreads / k tokens per workgroup
+constexpr int kReduceThreads = 512;        // layout reduce: one column of the partials per lane at E + G <= 512
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxGroups = 32;

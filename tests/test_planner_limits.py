@@ -179,11 +179,12 @@ def test_plan_struct_matches_header():
     h = open(os.path.join(root, "include", "moedisp_tools.h")).read()
     body = h[h.index("typedef struct moedisp_plan_info {"):h.index("} moedisp_plan_info;")]
     body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    body = body[body.index("{") + 1:]
     fields = []
-    for line in body.splitlines()[1:]:
-        line = line.strip().rstrip(";")
-        if line:
-            typ, rest = line.split(None, 1)
+    for decl in body.split(";"):
+        decl = " ".join(decl.split())
+        if decl:
+            typ, rest = decl.split(None, 1)
             fields += [(typ, n.strip()) for n in rest.split(",")]
     mine = [("moedisp_launch_info" if t is B.moedisp_launch_info else "int64_t", n)
             for n, t in B.moedisp_plan_info._fields_]
