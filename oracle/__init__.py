@@ -1,7 +1,8 @@
 """Python access to the CPU oracle (test infrastructure only).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
-this package.  It loads liboracle.so, built from oracle.c with gcc, and wraps
+this package.  It loads liboracle.so, built from oracle.cpp with g++ (C++17),
+and wraps
 each function with numpy arrays.  Nothing here touches a GPU.
 """
 from __future__ import annotations
@@ -13,7 +14,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(_HERE, "oracle.c")
+SRC = os.path.join(_HERE, "oracle.cpp")
 LIB = os.path.join(_HERE, "liboracle.so")
 
 ERR_BAD_EXPERT = 1
@@ -23,11 +24,11 @@ ERR_DUP_EXPERT = 2
 SCALE_FP32 = 0
 SCALE_UE8M0 = 1
 
-GCC_FLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+GCC_FLAGS = ["-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
              "-Wall", "-Wextra"]
 
 # Address and undefined-behaviour sanitizers (host code only: the oracle is
-# plain C for the CPU).  Any report aborts the process.
+# plain C++ for the CPU).  Any report aborts the process.
 SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
              "-fno-sanitize-recover=all"]
 
@@ -37,11 +38,11 @@ LIB_ENV = "MOEDISP_ORACLE_LIB"
 
 
 def compile_oracle(src: str, out: str, sanitize: bool = False) -> str:
-    """Compile one oracle source file into a shared library (single-threaded C),
-    with the address and undefined-behaviour sanitizers if `sanitize`."""
+    """Compile one oracle source file (C++17) into a shared library, with the
+    address and undefined-behaviour sanitizers if `sanitize`."""
     tmp = out + ".tmp"
     flags = GCC_FLAGS + (SAN_FLAGS if sanitize else [])
-    subprocess.run(["gcc", *flags, "-o", tmp, src, "-lm"], check=True)
+    subprocess.run(["g++", *flags, "-x", "c++", "-o", tmp, src, "-lm"], check=True)
     os.replace(tmp, out)
     return out
 
@@ -51,7 +52,7 @@ def sanitizer_env(lib: str) -> dict:
     `lib`: the sanitizer runtime preloaded (it must come first in a process
     whose main program is not instrumented), leak checks off (the interpreter
     keeps its allocations at exit), and any report fatal."""
-    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+    asan = subprocess.run(["g++", "-print-file-name=libasan.so"], capture_output=True, text=True,
                           check=True).stdout.strip()
     env = dict(os.environ)
     env.update({"LD_PRELOAD": asan, LIB_ENV: lib,
@@ -277,7 +278,7 @@ _default = None
 
 
 def get() -> Oracle:
-    """The oracle built from oracle.c (compiled on first use if missing)."""
+    """The oracle built from oracle.cpp (compiled on first use if missing)."""
     global _default
     if _default is None:
         other = os.environ.get(LIB_ENV)

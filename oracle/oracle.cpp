@@ -4,9 +4,11 @@
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
  * baseline leg of the benchmark load this code; the library under test never
- * does.  It is plain, single-threaded C99 written straight from the
- * definitions, shares no source with the GPU path, and is meant to be checked
- * by eye against the passages cited below.
+ * does.  It is plain, single-threaded C++17 (in its C subset: loops, arrays
+ * and the C math library, no templates or containers) written straight from
+ * the definitions, shares no source with the GPU path, and is meant to be
+ * checked by eye against the passages cited below.  Every function is
+ * exported with C linkage for the ctypes loader.
  *
  * Source: "MSCCLPP EP implementation - #852" (MSCCL++ pull request page).
  *   - PR description, "Scope": the layout call, intranode dispatch and
@@ -62,6 +64,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+extern "C" {
 
 #define ORACLE_ERR_BAD_EXPERT 1
 #define ORACLE_ERR_DUP_EXPERT 2
@@ -499,3 +503,5 @@ int oracle_combine_groups(int T, int G, int H, int64_t Rg, const uint16_t* group
     }
     return 0;
 }
+
+}  // extern "C"

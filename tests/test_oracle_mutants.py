@@ -1,5 +1,5 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and check that
-the pins catch every one.  Each mutant is a single textual edit of oracle.c,
+the pins catch every one.  Each mutant is a single textual edit of oracle.cpp,
 compiled into a temporary library; the real oracle is never modified."""
 import os
 
@@ -112,7 +112,7 @@ def test_pins_catch_mutant(name, tmp_path):
     old, new = MUTANTS[name]
     src = open(oracle.SRC).read()
     assert src.count(old) == 1, f"mutation site for {name} must occur exactly once"
-    path = os.path.join(tmp_path, "mutant.c")
+    path = os.path.join(tmp_path, "mutant.cpp")
     with open(path, "w") as f:
         f.write(src.replace(old, new))
     lib = oracle.compile_oracle(path, os.path.join(tmp_path, f"libmutant_{name}.so"))

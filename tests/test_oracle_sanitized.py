@@ -32,12 +32,12 @@ def test_oracle_pins_pass_under_asan_and_ubsan(tmp_path):
 
 def test_sanitized_oracle_catches_a_planted_overflow(tmp_path):
     """A one-past-the-end write in the layout's counter reset, planted in a
-    copy of oracle.c: the sanitized build must abort with a heap overflow
+    copy of oracle.cpp: the sanitized build must abort with a heap overflow
     report when the layout runs on arrays numpy allocated."""
     src = open(oracle.SRC).read()
     old = "for (int e = 0; e < E; ++e) tokens_per_expert[e] = 0;"
     assert src.count(old) == 1
-    bad = tmp_path / "oracle_overflow.c"
+    bad = tmp_path / "oracle_overflow.cpp"
     bad.write_text(src.replace(old, "for (int e = 0; e <= E; ++e) tokens_per_expert[e] = 0;"))
     lib = oracle.compile_oracle(str(bad), str(tmp_path / "liboracle_bad.so"), sanitize=True)
     env = oracle.sanitizer_env(lib)
