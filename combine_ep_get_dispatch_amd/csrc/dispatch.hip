@@ -380,15 +380,20 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull(Disp
     const int i0 = (j - m * P.wpb) * RPW;
     if (i0 < ns) {
         const PullEnt* list = a.pull_ent + (size_t)b * P.cap_b;
-        int slot[RPW], ex[RPW], tok[RPW], row[RPW];
+        int slot[RPW], raw[RPW], ex[RPW], tok[RPW], row[RPW];
         float wt[RPW];
+        const int slot0 = t0 * k;  // the block's first slot; ns > 0 here
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-            const PullEnt en = (i0 + r < ns) ? list[i0 + r] : PullEnt{0, -2};
-            slot[r] = en.slot;
+            const PullEnt en = (i0 + r < ns) ? list[i0 + r] : PullEnt{slot0, -2};
+            // every address below comes from a slot clamped into the block and
+            // an expert clamped into [0, E); whether the entry itself was valid
+            // is checked after the loads are issued
+            raw[r] = en.slot;
+            slot[r] = min(max(en.slot, slot0), slot0 + ns - 1);
             ex[r] = en.expert;
-            tok[r] = en.slot / k;
-            wt[r] = a.topk_weights[en.slot];  // a valid slot even past the block's entries; scalar
+            tok[r] = slot[r] / k;
+            wt[r] = a.topk_weights[slot[r]];  // scalar
         }
         // the count prefix loads first, then the first pass of the source
         // units, every load unconditional (clamped addresses): the vector
@@ -396,9 +401,10 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull(Disp
         // the prefix loads only, not for the rows
         int4 quad[RPW];
 #pragma unroll
-        for (int r = 0; r < RPW; ++r)
-            quad[r] = count_quad_load(a.pull_cnt + (size_t)(ex[r] >= 0 ? ex[r] : 0) * P.cnt_stride,
-                                      ex[r] >= 0 ? b : 0);
+        for (int r = 0; r < RPW; ++r) {
+            const bool live = (unsigned)ex[r] < (unsigned)a.E;
+            quad[r] = count_quad_load(a.pull_cnt + (size_t)(live ? ex[r] : 0) * P.cnt_stride, live ? b : 0);
+        }
         v4u v[RPW][U];
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
@@ -407,6 +413,16 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull(Disp
             for (int u = 0; u < U; ++u) v[r][u] = src[min(tid + u * nth, a.row16 - 1)];
         }
         __builtin_amdgcn_sched_barrier(0);
+        // an entry must name a slot of this block and an expert id or -1
+        // (masked): a list left by other routing is reported, never followed
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            if (i0 + r >= ns) continue;  // past the block's entries
+            if (slot[r] != raw[r] || ex[r] < -1 || ex[r] >= a.E) {
+                err |= MOEDISP_DEV_BAD_LAYOUT;
+                ex[r] = -2;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
             row[r] = -1;

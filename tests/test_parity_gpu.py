@@ -212,6 +212,34 @@ def test_inconsistent_layout_is_reported(dev):
     assert s2r.max() < wl.T * wl.k  # every written row stayed inside the buffer
 
 
+def test_corrupt_pull_list_is_reported_and_skipped(orc, dev):
+    """Block-pull scatter over a list that does not belong to this routing
+    (entries naming slots of another block, or experts past E): reported as
+    BAD_LAYOUT, the bad entries are neither followed nor written, and every
+    entry of the untouched blocks is still copied exactly."""
+    wl = W.make_workload("bad_list", 700, 512, 64, 8, 4, seed=84)
+    shape = GH.shape_of(wl)
+    q = M.ep_plan_query(shape)
+    assert q["pull"] == 1 and q["pull_nblk"] >= 2
+    inputs = GH.GpuInputs(wl, dev)
+    b = M.EpBuffers(shape, dev)
+    b.layout_notify(inputs.topk_idx)
+    ent = b.ws[q["ws_pull_ent_offset"]:q["ws_pull_end"]].view(torch.int32).view(-1, 2)
+    tb = q["pull_tb"]
+    ent[0, 0] = wl.T * wl.k + 7        # a slot past the routed ones
+    ent[1, 0] = tb * wl.k              # block 1's first slot, listed in block 0
+    ent[2, 1] = wl.E + 3               # an expert id past E
+    b.slot_to_row.fill_(-7)
+    b.dispatch_scatter(inputs.x, inputs.x_scales, inputs.topk_idx, inputs.topk_weights)
+    assert b.status() & M.binding.DEV_BAD_LAYOUT
+    o = GH.oracle_run(orc, wl)
+    s2r = b.slot_to_row.cpu().numpy().reshape(-1)
+    want = o["slot_to_row"].reshape(-1)
+    later = slice(tb * wl.k, wl.T * wl.k)  # blocks 1.. are untouched
+    assert np.array_equal(s2r[later], want[later])
+    assert s2r.max() < wl.T * wl.k
+
+
 def test_bad_handle_is_reported_and_skipped(dev):
     wl = W.make_workload("bad_handle", 64, 64, 8, 2, 2, seed=83)
     bufs, inputs, st = GH.gpu_layout_dispatch(wl, dev)
