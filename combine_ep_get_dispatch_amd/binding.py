@@ -91,12 +91,17 @@ class moedisp_plan_info(C.Structure):
                 ("permute_tile_stride", _I), ("permute_tiles", _I), ("permute_block_slots", _I),
                 ("groups_count", _L), ("groups_scatter", _L), ("permute_count", _L), ("permute_scatter", _L),
                 ("group_reduce", _L), ("combine_groups", _L),
+                ("permute_pull", _I), ("permute_pull_tb", _I), ("permute_pull_nblk", _I), ("permute_pull_cap_b", _I),
+                ("permute_pull_cnt_stride", _I), ("permute_pull_units", _I), ("permute_pull_wgs_per_xcd", _I),
+                ("permute_pull_notify", _L), ("permute_pull_copy", _L),
                 ("combine_col_splits", _I), ("combine_units_per_lane", _I), ("combine", _L),
                 ("small", _I), ("small_fused", _L),
                 ("ws_total", _I), ("ws_partial_offset", _I), ("ws_partial_bytes", _I), ("ws_counts_offset", _I),
                 ("ws_counts_bytes", _I), ("ws_counts_needed_flat", _I), ("ws_counts_needed_groups", _I),
                 ("ws_counts_needed_rows", _I), ("ws_pull_cnt_offset", _I), ("ws_pull_ls_offset", _I),
                 ("ws_pull_n_offset", _I), ("ws_pull_ent_offset", _I), ("ws_pull_end", _I),
+                ("ws_permute_pull_cnt_offset", _I), ("ws_permute_pull_ls_offset", _I),
+                ("ws_permute_pull_n_offset", _I), ("ws_permute_pull_ent_offset", _I), ("ws_permute_pull_end", _I),
                 ("max_block_slots", _I), ("max_tile_slots", _I), ("max_threads", _I),
                 ("pull_max_block_slots", _I), ("pull_max_blocks", _I)]
 

@@ -132,7 +132,10 @@ DispatchPlan plan_dispatch(const moedisp_shape& s) {
 // Block-pull plan: blocks of tb tokens whose source rows fit one XCD's L2,
 // as many blocks as XCDs or a multiple of it (every XCD gets the same number
 // of blocks; the last block may be shorter), each block sorted in LDS.
-PullPlan plan_pull(const moedisp_shape& s) {
+// compact_entries > 0: compact lists (routed entries only) and a copy grid of
+// kXcds * wq workgroups sized for that many routed entries plus 1/8 (the
+// copy loops where an XCD has more).
+PullPlan plan_pull(const moedisp_shape& s, long long compact_entries) {
     PullPlan p;
     memset(&p, 0, sizeof p);
     const long long T = s.num_tokens, k = s.topk, E = s.num_experts;
@@ -151,17 +154,37 @@ PullPlan plan_pull(const moedisp_shape& s) {
     p.nblk = (int)nblk;
     p.cap_b = (int)(tb * k);
     p.cnt_stride = (p.nblk + 3) / 4 * 4;
-    p.units = row16 > 512 ? 3 : 2;
+    // compact lists: 4 units per lane (more rows in flight per compute unit)
+    p.units = compact_entries > 0 ? kPullCompactUnits : (row16 > 512 ? 3 : 2);
     int threads = ((row16 + p.units - 1) / p.units + 63) / 64 * 64;
     if (threads > kMaxDispatchThreads) threads = kMaxDispatchThreads;
     // an fp8 row's scales travel one per lane with the row
-    if (scales_per_row(s) > threads) return p;
+    const int spr = scales_per_row(s);
+    if (spr > kMaxDispatchThreads || (compact_entries <= 0 && spr > threads)) return p;
+    if (spr > threads) threads = (spr + 63) / 64 * 64;
     p.threads = threads;
     p.rpw = 1;
     p.wpb = (p.cap_b + p.rpw - 1) / p.rpw;
     p.blocks = (long long)kXcds * p.wpb * ((p.nblk + kXcds - 1) / kXcds);
+    if (compact_entries > 0) {
+        long long wq = ceil_div(compact_entries, kXcds) + ceil_div(compact_entries, 8LL * kXcds);
+        const long long most = (long long)p.cap_b * ((p.nblk + kXcds - 1) / kXcds);  // entries one XCD can hold
+        if (wq > most) wq = most;
+        p.compact = 1;
+        p.wq = (int)wq;
+        p.blocks = (long long)kXcds * wq;
+    }
     p.use = 1;
     return p;
+}
+
+// The group rows' local expert permutation: compact lists over blocks of
+// group rows, a copy grid sized for the T * k routed slots the group rows
+// carry (each routed slot of a token lies in exactly one of its group rows).
+// Each group row carries only a few of its k slots, so full lists would
+// give mostly empty copy workgroups.
+PullPlan plan_pull_permute(const moedisp_shape& s) {
+    return plan_pull(group_rows_shape(s), (long long)s.num_tokens * s.topk);
 }
 
 // Group-deduplicated dispatch: the scatter over groups (k = E = G slots per
@@ -268,6 +291,18 @@ CombinePlan plan_combine(const moedisp_shape& s, int loads_per_row) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Offsets of one block-pull plan's tables from `base` (all `base` when the
+// plan is not used): counts [E][cnt_stride], ls [nblk][E], n [nblk], lists
+// [nblk][cap_b]; returns the end of the lists.
+static size_t pull_tables(size_t base, const PullPlan& p, int E, size_t off[4]) {
+    off[0] = off[1] = off[2] = off[3] = base;
+    if (!p.use) return base;
+    off[1] = align256(off[0] + (size_t)E * p.cnt_stride * sizeof(int32_t));
+    off[2] = align256(off[1] + (size_t)p.nblk * E * sizeof(int32_t));
+    off[3] = align256(off[2] + (size_t)p.nblk * sizeof(int32_t));
+    return align256(off[3] + (size_t)p.nblk * p.cap_b * sizeof(PullEnt));
+}
+
 WsPlan plan_workspace(const moedisp_shape& s) {
     WsPlan w;
     w.layout_blocks = s.num_tokens > 0 ? ceil_div(s.num_tokens, layout_tokens_per_block(s)) : 1;
@@ -283,17 +318,20 @@ WsPlan plan_workspace(const moedisp_shape& s) {
     size_t count_words = flat > groups ? flat : groups;
     if (rows > count_words) count_words = rows;
     size_t end = align256(w.counts_offset + count_words * sizeof(int32_t));
-    // block-pull tables of the flat dispatch (the group paths use the push scatter)
-    const PullPlan pp = plan_pull(s);
-    w.pull_cnt_offset = w.pull_ls_offset = w.pull_n_offset = w.pull_ent_offset = end;
-    if (pp.use) {
-        w.pull_cnt_offset = end;
-        w.pull_ls_offset = align256(w.pull_cnt_offset + (size_t)s.num_experts * pp.cnt_stride * sizeof(int32_t));
-        w.pull_n_offset = align256(w.pull_ls_offset + (size_t)pp.nblk * s.num_experts * sizeof(int32_t));
-        w.pull_ent_offset = align256(w.pull_n_offset + (size_t)pp.nblk * sizeof(int32_t));
-        end = align256(w.pull_ent_offset + (size_t)pp.nblk * pp.cap_b * sizeof(PullEnt));
-    }
-    w.total = end;
+    // block-pull tables of the flat dispatch and of the group rows' local
+    // expert permutation, from one base
+    size_t t[4];
+    const size_t end_flat = pull_tables(end, plan_pull(s), s.num_experts, t);
+    w.pull_cnt_offset = t[0];
+    w.pull_ls_offset = t[1];
+    w.pull_n_offset = t[2];
+    w.pull_ent_offset = t[3];
+    const size_t end_perm = pull_tables(end, plan_pull_permute(s), s.num_experts, t);
+    w.perm_cnt_offset = t[0];
+    w.perm_ls_offset = t[1];
+    w.perm_n_offset = t[2];
+    w.perm_ent_offset = t[3];
+    w.total = end_flat > end_perm ? end_flat : end_perm;
     return w;
 }
 
@@ -888,6 +926,20 @@ int ep_group_permute(const moedisp_shape* s, const void* group_x, const float* g
                        recv_scales, recv_src_idx, recv_weights, expert_offsets, slot_to_row, ws, ws_bytes, true, &a, s);
     if (st) return st;
     a.capacity = s->num_tokens * s->topk;  // the receive buffers hold T*k rows
+    const PullPlan qp = plan_pull_permute(*s);
+    if (qp.use) {
+        // block-pull over the group rows: block sorts (compact lists) with
+        // the offsets scan, then the copy
+        const WsPlan w = plan_workspace(*s);
+        a.pull = qp;
+        a.pull_cnt = (int32_t*)((char*)ws + w.perm_cnt_offset);
+        a.pull_ls = (int32_t*)((char*)ws + w.perm_ls_offset);
+        a.pull_n = (int32_t*)((char*)ws + w.perm_n_offset);
+        a.pull_ent = (PullEnt*)((char*)ws + w.perm_ent_offset);
+        if (!grid_fits(qp.blocks, qp.threads)) return MOEDISP_ERR_UNSUPPORTED;
+        if (launch_pull_notify(a, false, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
+        return hip_status(launch_scatter_pull(a, (hipStream_t)stream));
+    }
     a.plan = plan_group_permute(*s);       // same tiles as plan_dispatch(rs), more rows per workgroup
     if (!grid_fits(a.plan.blocks, a.plan.threads)) return MOEDISP_ERR_UNSUPPORTED;  // before either launch
     if (launch_dispatch_notify(a, (hipStream_t)stream) != hipSuccess) return MOEDISP_ERR_HIP;
@@ -1064,12 +1116,27 @@ int ep_plan_query(const moedisp_shape* s, moedisp_plan_info* info, size_t info_b
     info->groups_block_slots = (int64_t)GP.block_tokens * G;
     info->groups_count = push_count(GP, G);
     info->groups_scatter = push_scatter(GP, G);
-    const DispatchPlan RP = plan_group_permute(*s);
-    info->permute_tile_stride = RP.tile_stride;
-    info->permute_tiles = RP.tiles;
-    info->permute_block_slots = (int64_t)RP.block_tokens * k;
-    info->permute_count = push_count(RP, E);
-    info->permute_scatter = push_scatter(RP, k);
+    const PullPlan qp = plan_pull_permute(*s);
+    if (qp.use) {
+        info->permute_pull = 1;
+        info->permute_pull_tb = qp.tb;
+        info->permute_pull_nblk = qp.nblk;
+        info->permute_pull_cap_b = qp.cap_b;
+        info->permute_pull_cnt_stride = qp.cnt_stride;
+        info->permute_pull_units = qp.units;
+        info->permute_pull_wgs_per_xcd = qp.wq;
+        const size_t sort = sort_lds_words(qp.tb, qp.cap_b, E) * sizeof(int32_t);
+        info->permute_pull_notify = launch_info((long long)qp.nblk + 1, kNotifyThreads,
+                                                sort > (size_t)E * 4 ? sort : (size_t)E * 4, kStaticLdsNotify);
+        info->permute_pull_copy = launch_info(qp.blocks, qp.threads, 0, 0);
+    } else {
+        const DispatchPlan RP = plan_group_permute(*s);
+        info->permute_tile_stride = RP.tile_stride;
+        info->permute_tiles = RP.tiles;
+        info->permute_block_slots = (int64_t)RP.block_tokens * k;
+        info->permute_count = push_count(RP, E);
+        info->permute_scatter = push_scatter(RP, k);
+    }
     // combines (no LDS)
     if (T > 0) {
         const CombinePlan C = plan_combine(*s, k);
@@ -1107,6 +1174,12 @@ int ep_plan_query(const moedisp_shape* s, moedisp_plan_info* info, size_t info_b
     info->ws_pull_ent_offset = (int64_t)w.pull_ent_offset;
     info->ws_pull_end = pp.use ? (int64_t)(w.pull_ent_offset + (size_t)pp.nblk * pp.cap_b * sizeof(PullEnt))
                                : (int64_t)w.pull_ent_offset;
+    info->ws_permute_pull_cnt_offset = (int64_t)w.perm_cnt_offset;
+    info->ws_permute_pull_ls_offset = (int64_t)w.perm_ls_offset;
+    info->ws_permute_pull_n_offset = (int64_t)w.perm_n_offset;
+    info->ws_permute_pull_ent_offset = (int64_t)w.perm_ent_offset;
+    info->ws_permute_pull_end = qp.use ? (int64_t)(w.perm_ent_offset + (size_t)qp.nblk * qp.cap_b * sizeof(PullEnt))
+                                       : (int64_t)w.perm_ent_offset;
     info->max_block_slots = kMaxBlockSlots;
     info->max_tile_slots = kMaxTileSlots;
     info->max_threads = kMaxDispatchThreads;

@@ -359,121 +359,175 @@ __device__ inline int32_t count_quad_sum(int4 c, int b) {
     return (i0 < b ? c.x : 0) + (i0 + 1 < b ? c.y : 0) + (i0 + 2 < b ? c.z : 0) + (i0 + 3 < b ? c.w : 0);
 }
 
+// Copies list entries [i0, i0 + RPW) of block b (those below `nent`, the
+// entries the list holds) to their receive rows.  Every entry must name a slot
+// of block b; the block's slots are [b * tb * k, (b * tb + nt) * k).
 template <int U, int RPW>
-__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull(DispatchArgs a) {
+__device__ __forceinline__ void pull_copy(const DispatchArgs& a, int b, int i0, int nent, uint32_t& err) {
     const PullPlan& P = a.pull;
     const int tid = threadIdx.x;
     const int nth = blockDim.x;
     const int k = a.k;
+    const int t0 = b * P.tb;
+    const int ns = max(0, min(P.tb, a.T - t0)) * k;  // the block's slots
+    const PullEnt* list = a.pull_ent + (size_t)b * P.cap_b;
+    int slot[RPW], raw[RPW], ex[RPW], tok[RPW], row[RPW];
+    float wt[RPW];
+    const int slot0 = t0 * k;  // the block's first slot; ns > 0 here
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const PullEnt en = (i0 + r < nent) ? list[i0 + r] : PullEnt{slot0, -2};
+        // every address below comes from a slot clamped into the block and
+        // an expert clamped into [0, E); whether the entry itself was valid
+        // is checked after the loads are issued
+        raw[r] = en.slot;
+        slot[r] = min(max(en.slot, slot0), slot0 + ns - 1);
+        ex[r] = en.expert;
+        tok[r] = slot[r] / k;
+        wt[r] = a.topk_weights[slot[r]];  // scalar
+    }
+    // the count prefix loads first, then the first pass of the source
+    // units, every load unconditional (clamped addresses): the vector
+    // memory counter completes in order, so the row computation waits for
+    // the prefix loads only, not for the rows
+    int4 quad[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const bool live = (unsigned)ex[r] < (unsigned)a.E;
+        quad[r] = count_quad_load(a.pull_cnt + (size_t)(live ? ex[r] : 0) * P.cnt_stride, live ? b : 0);
+    }
+    v4u v[RPW][U];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        const v4u* src = a.x + (size_t)tok[r] * a.row16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[r][u] = src[min(tid + u * nth, a.row16 - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // an entry must name a slot of this block and an expert id or -1
+    // (masked): a list left by other routing is reported, never followed
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        if (i0 + r >= nent) continue;  // past the block's entries
+        if (slot[r] != raw[r] || ex[r] < -1 || ex[r] >= a.E) {
+            err |= MOEDISP_DEV_BAD_LAYOUT;
+            ex[r] = -2;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        row[r] = -1;
+        if (ex[r] < 0) continue;
+        const int e = ex[r];
+        const long long base = a.expert_offsets[e];
+        const long long rr = base + wave_sum(count_quad_sum(quad[r], b)) + (i0 + r) -
+                             a.pull_ls[(size_t)b * a.E + e];
+        if (rr < 0 || rr < base || rr >= base + a.tokens_per_expert[e] || rr >= a.capacity)
+            err |= MOEDISP_DEV_BAD_LAYOUT;
+        else
+            row[r] = (int)rr;
+    }
+    // the handle (and an fp8 row's scales), then the row stores: the wave
+    // ends right after issuing its last store
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        if (ex[r] == -2) continue;  // past the block's slots
+        if (tid == 0) {
+            a.slot_to_row[slot[r]] = row[r];
+            if (row[r] >= 0) {
+                a.recv_src_idx[row[r]] = tok[r];
+                a.recv_weights[row[r]] = wt[r];
+            }
+        }
+        if (a.scale_words && row[r] >= 0 && tid < a.scale_words)
+            a.recv_scales[(size_t)row[r] * a.scale_words + tid] = a.x_scales[(size_t)tok[r] * a.scale_words + tid];
+    }
+    // row copy (later passes for rows wider than U * nth units)
+    for (int c0 = 0; c0 < a.row16; c0 += U * nth) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            if (row[r] < 0) continue;
+            if (c0 > 0) {
+                const v4u* src = a.x + (size_t)tok[r] * a.row16;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int c = c0 + tid + u * nth;
+                    if (c < a.row16) v[r][u] = src[c];
+                }
+            }
+            v4u* dst = a.recv_x + (size_t)row[r] * a.row16;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + tid + u * nth;
+                if (c < a.row16) stream_store(v[r][u], dst, (uint32_t)a.row16 * 16u, c);
+            }
+        }
+    }
+}
+
+template <int U, int RPW>
+__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull(DispatchArgs a) {
+    const PullPlan& P = a.pull;
     const int xcd = blockIdx.x % kXcds;
     const int j = blockIdx.x / kXcds;
     const int m = j / P.wpb;
     const int b = xcd + kXcds * m;
     uint32_t err = 0;
-    if (blockIdx.x == 0 && tid == 0) {  // the routed slots must add up to the layout's total
+    if (blockIdx.x == 0 && threadIdx.x == 0) {  // the routed slots must add up to the layout's total
         int32_t routed = 0;
         for (int q = 0; q < P.nblk; ++q) routed += a.pull_n[q];
         if (routed != a.expert_offsets[a.E]) err |= MOEDISP_DEV_BAD_LAYOUT;
     }
-    const int t0 = b * P.tb;
-    const int ns = b < P.nblk ? max(0, min(P.tb, a.T - t0)) * k : 0;
+    const int ns = b < P.nblk ? max(0, min(P.tb, a.T - b * P.tb)) * a.k : 0;
     const int i0 = (j - m * P.wpb) * RPW;
-    if (i0 < ns) {
-        const PullEnt* list = a.pull_ent + (size_t)b * P.cap_b;
-        int slot[RPW], raw[RPW], ex[RPW], tok[RPW], row[RPW];
-        float wt[RPW];
-        const int slot0 = t0 * k;  // the block's first slot; ns > 0 here
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const PullEnt en = (i0 + r < ns) ? list[i0 + r] : PullEnt{slot0, -2};
-            // every address below comes from a slot clamped into the block and
-            // an expert clamped into [0, E); whether the entry itself was valid
-            // is checked after the loads are issued
-            raw[r] = en.slot;
-            slot[r] = min(max(en.slot, slot0), slot0 + ns - 1);
-            ex[r] = en.expert;
-            tok[r] = slot[r] / k;
-            wt[r] = a.topk_weights[slot[r]];  // scalar
-        }
-        // the count prefix loads first, then the first pass of the source
-        // units, every load unconditional (clamped addresses): the vector
-        // memory counter completes in order, so the row computation waits for
-        // the prefix loads only, not for the rows
-        int4 quad[RPW];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const bool live = (unsigned)ex[r] < (unsigned)a.E;
-            quad[r] = count_quad_load(a.pull_cnt + (size_t)(live ? ex[r] : 0) * P.cnt_stride, live ? b : 0);
-        }
-        v4u v[RPW][U];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const v4u* src = a.x + (size_t)tok[r] * a.row16;
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[r][u] = src[min(tid + u * nth, a.row16 - 1)];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // an entry must name a slot of this block and an expert id or -1
-        // (masked): a list left by other routing is reported, never followed
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            if (i0 + r >= ns) continue;  // past the block's entries
-            if (slot[r] != raw[r] || ex[r] < -1 || ex[r] >= a.E) {
-                err |= MOEDISP_DEV_BAD_LAYOUT;
-                ex[r] = -2;
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            row[r] = -1;
-            if (ex[r] < 0) continue;
-            const int e = ex[r];
-            const long long base = a.expert_offsets[e];
-            const long long rr = base + wave_sum(count_quad_sum(quad[r], b)) + (i0 + r) -
-                                 a.pull_ls[(size_t)b * a.E + e];
-            if (rr < 0 || rr < base || rr >= base + a.tokens_per_expert[e] || rr >= a.capacity)
-                err |= MOEDISP_DEV_BAD_LAYOUT;
-            else
-                row[r] = (int)rr;
-        }
-        // the handle (and an fp8 row's scales), then the row stores: the wave
-        // ends right after issuing its last store
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            if (ex[r] == -2) continue;  // past the block's slots
-            if (tid == 0) {
-                a.slot_to_row[slot[r]] = row[r];
-                if (row[r] >= 0) {
-                    a.recv_src_idx[row[r]] = tok[r];
-                    a.recv_weights[row[r]] = wt[r];
-                }
-            }
-            if (a.scale_words && row[r] >= 0 && tid < a.scale_words)
-                a.recv_scales[(size_t)row[r] * a.scale_words + tid] = a.x_scales[(size_t)tok[r] * a.scale_words + tid];
-        }
-        // row copy (later passes for rows wider than U * nth units)
-        for (int c0 = 0; c0 < a.row16; c0 += U * nth) {
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                if (row[r] < 0) continue;
-                if (c0 > 0) {
-                    const v4u* src = a.x + (size_t)tok[r] * a.row16;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int c = c0 + tid + u * nth;
-                        if (c < a.row16) v[r][u] = src[c];
-                    }
-                }
-                v4u* dst = a.recv_x + (size_t)row[r] * a.row16;
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + tid + u * nth;
-                    if (c < a.row16) stream_store(v[r][u], dst, (uint32_t)a.row16 * 16u, c);
-                }
-            }
-        }
+    if (i0 < ns) pull_copy<U, RPW>(a, b, i0, ns, err);
+    if (threadIdx.x == 0 && err) atomicOr(&a.hdr->status, err);
+}
+
+// Block-pull copy over compacted lists (PullPlan::compact): block b's list
+// holds its routed entries only (pull_n[b] of them; the sort wrote the masked
+// slots' handles), so the grid does not follow the slot count.  The wq
+// workgroups of XCD x (blockIdx % 8 == x) take the entries of x's blocks
+// b = x, x + 8, ... in order, workgroup m the entries m, m + wq, ...: each
+// finds its block from a wave scan of those blocks' entry counts.  A grid
+// sized for the expected entries takes each in one pass; more entries on one
+// XCD (skewed routing, or more routed slots than expected) take more passes.
+// Used for the group rows' permutation, whose source rows are read about 1.5
+// times each and so mostly come from HBM: 4 units per lane (256 lanes for a
+// 7168-wide bf16 row) keep 8 rows in flight per compute unit.  Measured at
+// T = 4096, H = 7168, E = 256, G = 8, k = 8 (21.8 k group rows): 150 us
+// against 176 us with 3 units (320 lanes), 154 us with 7 (128 lanes), 160 us
+// with a wave per row, 157 us with two entries per workgroup, and 170 us for
+// the push scatter; a grid without the 1/8 spare took 153 us.
+template <int U>
+__global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter_pull_compact(DispatchArgs a) {
+    const PullPlan& P = a.pull;
+    const int lane = threadIdx.x & 63;
+    const int xcd = blockIdx.x % kXcds;
+    const int m = blockIdx.x / kXcds;
+    uint32_t err = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {  // the routed slots must add up to the layout's total
+        int32_t routed = 0;
+        for (int q = 0; q < P.nblk; ++q) routed += a.pull_n[q];
+        if (routed != a.expert_offsets[a.E]) err |= MOEDISP_DEV_BAD_LAYOUT;
     }
-    if (tid == 0 && err) atomicOr(&a.hdr->status, err);
+    // lane l: block xcd + 8 l of this XCD (nbx <= kPullMaxBlocks / 8 = 32
+    // of them), its entry count clamped to the list's capacity
+    const int nbx = P.nblk > xcd ? (P.nblk - xcd + kXcds - 1) / kXcds : 0;
+    int c = lane < nbx ? a.pull_n[xcd + kXcds * lane] : 0;
+    if (c < 0 || c > P.cap_b) {
+        err |= MOEDISP_DEV_BAD_LAYOUT;
+        c = c < 0 ? 0 : P.cap_b;
+    }
+    const int incl = wave_inclusive_scan_dpp(c);
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    for (int q = m; q < total; q += P.wq) {
+        // the block holding entry q: the lanes whose inclusive count is <= q
+        const int l = (int)__popcll(__ballot(incl <= q));
+        const int first = __builtin_amdgcn_readlane(incl - c, l);
+        pull_copy<U, 1>(a, xcd + kXcds * l, q - first, __builtin_amdgcn_readlane(c, l), err);
+    }
+    if (threadIdx.x == 0 && err) atomicOr(&a.hdr->status, err);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,6 +693,12 @@ hipError_t launch_scatter_pull(const DispatchArgs& a, hipStream_t stream) {
     if (!grid_fits(p.blocks, p.threads)) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)p.blocks), block(p.threads);
     if (p.rpw != 1) return hipErrorInvalidConfiguration;
+    if (p.compact) {
+        if (p.wq < 1 || p.nblk > kPullMaxBlocks || p.units != kPullCompactUnits || a.slot_to_row == nullptr)
+            return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((moedisp_scatter_pull_compact<kPullCompactUnits>), grid, block, 0, stream, a);
+        return hipGetLastError();
+    }
     if (p.units == 3)
         hipLaunchKernelGGL((moedisp_scatter_pull<3, 1>), grid, block, 0, stream, a);
     else if (p.units == 2)

@@ -333,6 +333,10 @@ static __device__ inline uint32_t pull_sort(const DispatchArgs& a, int b, int32_
         if (!valid) continue;
         PullEnt en;
         en.slot = (int32_t)(slot0 + i);
+        if (e < 0 && P.compact) {  // compact lists: the masked slot's handle here
+            a.slot_to_row[en.slot] = -1;
+            continue;
+        }
         int pos;
         if (e >= 0) {
             int r = 0;

@@ -104,9 +104,11 @@ struct PullPlan {
     int cnt_stride;   // ints per expert column of the per-block counts (>= nblk, multiple of 4)
     int rpw;          // list entries (receive rows) per copy workgroup (1)
     int threads;      // copy workgroup lanes
-    int units;        // 16-byte units per lane and pass (2, or 3 for rows over 512 units)
+    int units;        // 16-byte units per lane and pass (2, or 3 for rows over 512 units; 4 when compact)
     int wpb;          // copy workgroups per block: ceil(cap_b / rpw)
-    long long blocks; // copy grid: kXcds * wpb * ceil(nblk / kXcds)
+    long long blocks; // copy grid: kXcds * wpb * ceil(nblk / kXcds), or kXcds * wq when compact
+    int compact;      // 1: lists hold the routed entries only; the sort writes masked slots' handles
+    int wq;           // compact: copy workgroups per XCD (each takes every wq-th entry of its XCD)
 };
 
 constexpr int kXcds = 8;                          // XCDs of an MI355X (round-robin workgroup dispatch)
@@ -116,6 +118,7 @@ constexpr int kPullMaxBlockSlots = 4096;          // slots of one block sorted i
 constexpr int kPullMaxBlocks = 256;               // a row's count prefix is one 16-byte load per lane of a wave
 constexpr int kPullMinBlockTokens = 32;
 constexpr int kPullMaskWords = 4096;              // the sort's token masks: E * ceil(tb / 64) 64-bit words at most
+constexpr int kPullCompactUnits = 4;              // 16-byte units per lane of the compact-list copy
 constexpr int kNotifyThreads = 1024;              // lanes of a notify workgroup (16 waves)
 
 __host__ __device__ inline int sort_mask_words(int tb) { return (tb + 63) / 64; }
@@ -152,11 +155,16 @@ struct WsPlan {
     size_t pull_ls_offset;   // block-pull: int32 [nblk][E] first list entry of each expert in a block
     size_t pull_n_offset;    // block-pull: int32 [nblk] routed entries per block
     size_t pull_ent_offset;  // block-pull: PullEnt [nblk][cap_b] sorted lists
+    // the same four tables of the group rows' local expert permutation
+    // (compact lists), laid out from the same base: the two are never used
+    // by one call, so the region is the larger of the two
+    size_t perm_cnt_offset, perm_ls_offset, perm_n_offset, perm_ent_offset;
     size_t total;
 };
 
 DispatchPlan plan_dispatch(const moedisp_shape& s);
-PullPlan plan_pull(const moedisp_shape& s);
+PullPlan plan_pull(const moedisp_shape& s, long long compact_entries = 0);
+PullPlan plan_pull_permute(const moedisp_shape& s);
 DispatchPlan plan_dispatch_quant(const moedisp_shape& s);
 DispatchPlan plan_dispatch_groups(const moedisp_shape& s);
 moedisp_shape group_rows_shape(const moedisp_shape& s);

@@ -88,6 +88,13 @@ typedef struct moedisp_plan_info {
     int64_t groups_tile_stride, groups_tiles, groups_block_slots;
     int64_t permute_tile_stride, permute_tiles, permute_block_slots;
     moedisp_launch_info groups_count, groups_scatter, permute_count, permute_scatter, group_reduce, combine_groups;
+    /* local permutation by block-pull copy over blocks of group rows with
+     * compact lists (permute_pull = 1 when it serves the shape; the permute_
+     * push fields above are then zero): block sorts with the offsets scan,
+     * then permute_pull_wgs_per_xcd copy workgroups per XCD */
+    int64_t permute_pull, permute_pull_tb, permute_pull_nblk, permute_pull_cap_b, permute_pull_cnt_stride;
+    int64_t permute_pull_units, permute_pull_wgs_per_xcd;
+    moedisp_launch_info permute_pull_notify, permute_pull_copy;
     /* ep_combine */
     int64_t combine_col_splits, combine_units_per_lane;
     moedisp_launch_info combine;
@@ -98,6 +105,9 @@ typedef struct moedisp_plan_info {
     int64_t ws_total, ws_partial_offset, ws_partial_bytes, ws_counts_offset, ws_counts_bytes;
     int64_t ws_counts_needed_flat, ws_counts_needed_groups, ws_counts_needed_rows;
     int64_t ws_pull_cnt_offset, ws_pull_ls_offset, ws_pull_n_offset, ws_pull_ent_offset, ws_pull_end;
+    /* the permutation's tables share the flat tables' base (never one call) */
+    int64_t ws_permute_pull_cnt_offset, ws_permute_pull_ls_offset, ws_permute_pull_n_offset;
+    int64_t ws_permute_pull_ent_offset, ws_permute_pull_end;
     /* limits the kernels assume */
     int64_t max_block_slots, max_tile_slots, max_threads, pull_max_block_slots, pull_max_blocks;
 } moedisp_plan_info;

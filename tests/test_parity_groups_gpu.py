@@ -119,7 +119,19 @@ CASES = {
     "all_masked": lambda: W.make_workload("all_masked", 40, 256, 8, 2, 2, seed=75, mask_frac=1.0),
     # 875 units per row: the reduce's two column ranges are 438 and 437 units
     "ragged_columns": lambda: W.make_workload("ragged_cols", 300, 7000, 64, 8, 8, seed=76, mask_frac=0.1),
+    # the push scatter permutes these: blocks of group rows would be under
+    # 32 rows, or the experts too many for the block sort
+    "push_permute_small": lambda: W.make_workload("push_small", 100, 256, 8, 2, 2, seed=79),
+    "push_permute_e1024": lambda: W.make_workload("push_e1024", 300, 256, 1024, 8, 8, seed=80, mask_frac=0.05),
 }
+
+
+def test_permute_paths_covered():
+    """The cases above reach both permutations: block-pull over compact
+    lists, and the push scatter."""
+    pull = {n: M.ep_plan_query(GH.shape_of(f()))["permute_pull"] for n, f in CASES.items()}
+    assert pull["push_permute_small"] == 0 and pull["push_permute_e1024"] == 0
+    assert pull["dsv3_ragged"] == 1 and pull["mixtral_ragged"] == 1
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -131,3 +143,44 @@ def test_group_path_parity_full_size(orc, dev):
     """DeepSeek-V3 prefill shape: every group row, permuted row, partial and
     combined token."""
     run_groups(orc, W.config(2), dev)
+
+
+def test_permute_entries_on_one_xcd(orc, dev):
+    """Every routed slot of the group rows lies in the first block of group
+    rows, which one XCD copies: that XCD's copy workgroups make several
+    passes over its compact list while the other XCDs have none.  The
+    permutation is ep_dispatch over the group rows, so the oracle's dispatch
+    of the same rows is the expected result, bit for bit."""
+    T, H, E, G, k = 512, 256, 64, 8, 8
+    shape = M.moedisp_shape.make(T, H, E, G, k, M.BF16, 0)
+    q = M.ep_plan_query(shape)
+    assert q["permute_pull"] == 1
+    cap = T * min(G, k)
+    rows = min(q["permute_pull_tb"], T)  # rows of block 0, k slots each: at most T * k entries
+    assert rows * k > 2 * q["permute_pull_wgs_per_xcd"]
+    rng = np.random.default_rng(78)
+    idx = np.full((cap, k), -1, np.int32)
+    for r in range(rows):
+        idx[r] = rng.choice(E, size=k, replace=False)
+    w = rng.random((cap, k), dtype=np.float32)
+    gx = rng.integers(0, 1 << 16, size=(cap, H), dtype=np.uint16)
+    tpe, _, _, st = orc.layout(idx, E, G)
+    assert st == 0
+    o = orc.dispatch(gx, None, idx, w, E)
+    R = int(o["expert_offsets"][-1])
+    assert R == rows * k
+
+    bufs = M.EpBuffers(shape, dev)
+    gb = M.EpGroupBuffers(bufs)
+    gb.group_x.copy_(torch.from_numpy(gx.view(np.uint8)))
+    gb.group_topk_idx.copy_(torch.from_numpy(idx))
+    gb.group_topk_weights.copy_(torch.from_numpy(w))
+    bufs.tokens_per_expert.copy_(torch.from_numpy(tpe))
+    gb.perm_slot_to_row.fill_(-7)
+    gb.permute()
+    assert bufs.status() == 0
+    eq(bufs.expert_offsets.cpu().numpy(), o["expert_offsets"], "expert_offsets")
+    eq(bufs.recv_x[:R].cpu().numpy(), o["recv_x"][:R].view(np.uint8), "rows")
+    eq(gb.perm_src_idx[:R].cpu().numpy(), o["recv_src_idx"][:R], "recv_src_idx")
+    eq(bufs.recv_weights[:R].cpu().numpy(), o["recv_weights"][:R], "recv_weights")
+    eq(gb.perm_slot_to_row.cpu().numpy(), o["slot_to_row"], "slot_to_row")

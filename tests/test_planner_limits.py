@@ -10,7 +10,9 @@ library accepts:
     column ranges cover the row, one lane per slot;
   - block-pull copy: blocks of >= 32 tokens that cover T, 8 <= blocks <= 256,
     a block's slots <= 4096 and its source rows <= 3.5 MiB, the sort's token
-    masks within bounds, an fp8 row's scales one per lane;
+    masks within bounds, an fp8 row's scales one per lane; the same for the
+    group rows' permutation (compact lists), whose copy grid is 8 workgroups
+    per XCD slot, at most one per entry an XCD's blocks can hold;
   - workspace: 256-byte-aligned regions in order, each large enough for the
     table the kernels index (layout partials, the largest per-tile count
     table, the pull tables), all inside ep_workspace_bytes."""
@@ -108,10 +110,30 @@ def check(L, sh, q):
     check_launch("groups_count", q.groups_count)
     assert q.groups_block_slots <= q.max_block_slots and q.groups_tiles <= q.groups_tile_stride, ctx
     check_launch("groups_scatter", q.groups_scatter)
-    check_launch("permute_count", q.permute_count)
-    assert q.permute_block_slots <= q.max_block_slots and q.permute_tiles <= q.permute_tile_stride, ctx
-    check_launch("permute_scatter", q.permute_scatter)
-    assert q.permute_tile_stride % 4 == 0
+    if q.permute_pull:
+        TR = q.group_rows
+        tb, nblk, cap = q.permute_pull_tb, q.permute_pull_nblk, q.permute_pull_cap_b
+        assert tb >= 32 and 8 <= nblk <= q.pull_max_blocks, ctx
+        assert nblk * tb >= TR > (nblk - 1) * tb, ctx
+        assert cap == tb * k <= q.pull_max_block_slots, ctx
+        assert tb * rb <= L2_BLOCK, ctx
+        assert E <= 512 and E * ((tb + 63) // 64) <= 4096, ctx
+        assert q.permute_pull_cnt_stride >= nblk and q.permute_pull_cnt_stride % 4 == 0, ctx
+        check_launch("permute_pull_notify", q.permute_pull_notify)
+        check_launch("permute_pull_copy", q.permute_pull_copy)
+        wq = q.permute_pull_wgs_per_xcd
+        assert 1 <= wq <= cap * -(-nblk // 8), ctx
+        assert q.permute_pull_copy.blocks == 8 * wq, ctx
+        assert q.permute_pull_notify.blocks == nblk + 1, ctx
+        if sh.scale_block:
+            assert H // sh.scale_block <= q.permute_pull_copy.threads, ctx
+        assert q.permute_scatter.blocks == 0 and q.permute_count.blocks == 0, ctx
+    else:
+        assert q.permute_pull_copy.blocks == 0 and q.permute_pull_nblk == 0
+        check_launch("permute_count", q.permute_count)
+        assert q.permute_block_slots <= q.max_block_slots and q.permute_tiles <= q.permute_tile_stride, ctx
+        check_launch("permute_scatter", q.permute_scatter)
+        assert q.permute_tile_stride % 4 == 0
     # combines
     if T > 0:
         for n in ("combine", "group_reduce", "combine_groups"):
@@ -138,12 +160,24 @@ def check(L, sh, q):
         assert q.ws_pull_ent_offset >= q.ws_pull_n_offset + q.pull_nblk * 4, ctx
         assert q.ws_pull_end == q.ws_pull_ent_offset + q.pull_nblk * q.pull_cap_b * 8, ctx
     assert q.ws_pull_end <= q.ws_total, ctx
+    # the permutation's tables: from the same base as the flat ones
+    poffs = [q.ws_permute_pull_cnt_offset, q.ws_permute_pull_ls_offset, q.ws_permute_pull_n_offset,
+             q.ws_permute_pull_ent_offset]
+    assert poffs[0] == q.ws_pull_cnt_offset, ctx
+    assert all(o % 256 == 0 for o in poffs) and poffs == sorted(poffs), (ctx, poffs)
+    if q.permute_pull:
+        nblk = q.permute_pull_nblk
+        assert poffs[1] >= poffs[0] + E * q.permute_pull_cnt_stride * 4, ctx
+        assert poffs[2] >= poffs[1] + nblk * E * 4, ctx
+        assert poffs[3] >= poffs[2] + nblk * 4, ctx
+        assert q.ws_permute_pull_end == poffs[3] + nblk * q.permute_pull_cap_b * 8, ctx
+    assert q.ws_permute_pull_end <= q.ws_total, ctx
 
 
 def test_planner_limits_over_shapes():
     L = M.load()
     q = B.moedisp_plan_info()
-    n_ok = n_pull = n_small = 0
+    n_ok = n_pull = n_small = n_perm = 0
     for (T, H, E, G, k, sb) in shapes():
         for dt in ((M.BF16,) if sb == 0 else (M.FP8_E4M3,)):
             sh = M.moedisp_shape.make(T, H, E, G, k, dt, sb)
@@ -155,8 +189,9 @@ def test_planner_limits_over_shapes():
             n_ok += 1
             n_pull += q.pull
             n_small += q.small
+            n_perm += q.permute_pull
     # the sweep reaches every planner branch
-    assert n_ok > 5000 and n_pull > 500 and n_small > 500, (n_ok, n_pull, n_small)
+    assert n_ok > 5000 and n_pull > 500 and n_small > 500 and n_perm > 500, (n_ok, n_pull, n_small, n_perm)
 
 
 def test_plan_query_rejects_like_the_entry_points():
