@@ -110,6 +110,9 @@ class Oracle:
         L.oracle_dispatch_groups.restype = C.c_int
         L.oracle_combine_groups.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int64, P, P, P, P]
         L.oracle_combine_groups.restype = C.c_int
+        L.oracle_dispatch_padded.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64, C.c_int64,
+                                             C.c_int64, P, P, P, P, P, P, P, P, P]
+        L.oracle_dispatch_padded.restype = C.c_int
         self.L = L
         self.path = path
 
@@ -158,6 +161,36 @@ class Oracle:
             raise ValueError("oracle_dispatch: bad shape")
         return dict(recv_x=recv_x, recv_scales=recv_scales, recv_src_idx=src, recv_weights=rw,
                     expert_offsets=off, slot_to_row=s2r, status=st)
+
+    def dispatch_padded(self, x, x_scales, topk_idx, topk_weights, E: int, C: int, S: int, B: int, fill=0):
+        """Padded (low-latency) layout: returns a dict with recv_x [E*S][...],
+        recv_scales, recv_src_idx [E*S], recv_weights [E*S], slot_to_row [T][k],
+        status.  Rows no slot takes keep `fill` (recv_src_idx -1, weights 0)."""
+        idx = _c(topk_idx, np.int32)
+        T, k = idx.shape
+        x = np.ascontiguousarray(x)
+        row_bytes = int(np.prod(x.shape[1:])) * x.itemsize
+        rows = E * S
+        # one spare slab past the buffer, so that a planted off-by-one in the
+        # tests' mutants writes into it instead of past the allocation
+        alloc = rows + S
+        recv_x = np.full((alloc,) + x.shape[1:], fill, x.dtype)
+        if x_scales is not None:
+            xs = np.ascontiguousarray(x_scales)
+            srb = int(np.prod(xs.shape[1:])) * xs.itemsize
+            recv_scales = np.zeros((alloc,) + xs.shape[1:], xs.dtype)
+        else:
+            xs, srb, recv_scales = None, 0, None
+        src = np.full(alloc, -1, np.int32)
+        rw = np.zeros(alloc, np.float32)
+        s2r = np.zeros((T, k), np.int32)
+        w = _c(topk_weights, np.float32)
+        st = self.L.oracle_dispatch_padded(T, k, E, C, S, B, row_bytes, srb, _p(x), _p(xs), _p(idx), _p(w),
+                                           _p(recv_x), _p(recv_scales), _p(src), _p(rw), _p(s2r))
+        if st < 0:
+            raise ValueError("oracle_dispatch_padded: bad arguments")
+        return dict(recv_x=recv_x[:rows], recv_scales=None if recv_scales is None else recv_scales[:rows],
+                    recv_src_idx=src[:rows], recv_weights=rw[:rows], slot_to_row=s2r, status=st)
 
     def combine(self, expert_out_bf16, recv_weights, slot_to_row, want_f32=True, want_bf16=True):
         """expert_out_bf16: uint16 [R][H].  Returns (out_f32 [T][H] or None, out_bf16 [T][H] or None)."""

@@ -58,7 +58,20 @@
  * Error codes (bit mask, same meaning as the library's device status bits):
  *   1  an expert id outside {-1} U [0,E)      (slot treated as masked)
  *   2  an expert id repeated within one token  (each copy is its own slot)
+ *  16  padded layout only: an expert received more routed slots than its
+ *      capacity (the extra slots get no row)
  *  -1  bad shape argument
+ *
+ * Padded (low-latency) layout (same page: the commit porting the
+ * low-latency kernels, whose dispatch signals received counts per expert into
+ * per-expert receive slots sized by a maximum token count, and the later
+ * commit adding a rank-major output option to that path).  Reading, for one
+ * source: expert e owns the C receive rows [e*S + B, e*S + B + C) of a buffer
+ * of E*S rows (S >= B + C); its routed slots take them in ascending slot
+ * order (token order), the i-th at row e*S + B + i; slots past an expert's
+ * first C get no row (slot_to_row -1) and status 16.  Rows of the buffer that
+ * no slot takes are left untouched.  With several sources, source r would
+ * take B = r*C inside slabs of S = (sources)*C rows.
  */
 #include <math.h>
 #include <stdint.h>
@@ -69,6 +82,7 @@ extern "C" {
 
 #define ORACLE_ERR_BAD_EXPERT 1
 #define ORACLE_ERR_DUP_EXPERT 2
+#define ORACLE_ERR_OVERFLOW 16
 
 /* ------------------------------------------------------------------------ */
 /* bf16 <-> binary32.                                                        */
@@ -241,6 +255,56 @@ int oracle_dispatch(int T, int k, int E, int64_t row_bytes, int64_t scale_row_by
     }
     free(cursor);
     return routing_status(T, k, E, topk_idx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* padded (low-latency) dispatch: fixed receive slots per expert              */
+/* ------------------------------------------------------------------------ */
+
+/* Arguments as oracle_dispatch, plus the per-expert capacity C, the slab
+ * stride S and the first row B of this source inside each slab.  recv_x,
+ * recv_scales, recv_src_idx and recv_weights have E*S rows.  No offsets are
+ * returned: expert e's rows start at e*S + B, and its received count is
+ * min(its routed slots, C). */
+int oracle_dispatch_padded(int T, int k, int E, int C, int64_t S, int64_t B, int64_t row_bytes,
+                           int64_t scale_row_bytes, const uint8_t* x, const uint8_t* x_scales,
+                           const int32_t* topk_idx, const float* topk_weights,
+                           uint8_t* recv_x, uint8_t* recv_scales,
+                           int32_t* recv_src_idx, float* recv_weights, int32_t* slot_to_row)
+{
+    if (T < 0 || k < 1 || k > 32 || E < 1 || C < 0 || B < 0 || S < 1 || B + C > S || row_bytes < 0 ||
+        scale_row_bytes < 0)
+        return -1;
+    /* how many of each expert's slots have been placed so far */
+    int64_t* placed = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+    if (!placed) return -1;
+    int st = 0;
+    /* slots in ascending order s = t*k + j, i.e. token by token */
+    for (int64_t s = 0; s < (int64_t)T * k; ++s) {
+        int t = (int)(s / k);
+        int32_t id = topk_idx[s];
+        if (!routed(id, E)) {
+            slot_to_row[s] = -1;
+            continue;
+        }
+        int64_t i = placed[id]++;
+        if (i >= C) {
+            slot_to_row[s] = -1;
+            st |= ORACLE_ERR_OVERFLOW;
+            continue;
+        }
+        int64_t q = (int64_t)id * S + B + i;
+        const uint8_t* src_row = x + (int64_t)t * row_bytes;
+        memcpy(recv_x + q * row_bytes, src_row, (size_t)row_bytes);
+        if (x_scales && recv_scales && scale_row_bytes > 0)
+            memcpy(recv_scales + q * scale_row_bytes, x_scales + (int64_t)t * scale_row_bytes,
+                   (size_t)scale_row_bytes);
+        recv_src_idx[q] = (int32_t)t;
+        recv_weights[q] = topk_weights[s];
+        slot_to_row[s] = (int32_t)q;
+    }
+    free(placed);
+    return st | routing_status(T, k, E, topk_idx);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -656,8 +656,103 @@ def check_groups_all(orc):
         check_groups_combine_closed_form(orc, wl, GROUP_BOUND[wl.expert_kind])
 
 
+# ---------------------------------------------------------------------------
+# padded (low-latency) layout
+# ---------------------------------------------------------------------------
+
+def check_padded_example(orc, path=os.path.join(GOLDEN, "padded_example.json")):
+    with open(path) as f:
+        g = json.load(f)
+    idx = np.array(g["topk_idx"], np.int32)
+    w = np.array(g["topk_weights"], np.float32)
+    T, k = idx.shape
+    x = (np.arange(T * 4, dtype=np.uint16) + 1).reshape(T, 4)
+    d = orc.dispatch_padded(x, None, idx, w, g["E"], g["C"], g["S"], g["B"], fill=0xFFFF)
+    assert d["status"] == g["status"]
+    assert d["slot_to_row"].tolist() == g["slot_to_row"]
+    for r, (t, wt) in g["rows"].items():
+        r = int(r)
+        assert d["recv_src_idx"][r] == t and d["recv_weights"][r] == np.float32(wt), r
+        assert np.array_equal(d["recv_x"][r], x[t]), r
+    for r in g["untouched_rows"]:
+        assert d["recv_src_idx"][r] == -1 and np.all(d["recv_x"][r] == 0xFFFF), r
+
+
+def check_padded_bruteforce(orc, shapes=((2, 1, 2, 1), (3, 1, 2, 2), (2, 2, 3, 1), (3, 2, 3, 2), (2, 3, 3, 1))):
+    """Every routing of tiny shapes, against one global sort of the
+    (expert, token, slot) keys: the i-th key of expert e takes row
+    e*S + B + i while i < C; the status reports an expert past C."""
+    H = 4
+    for (T, k, E, C) in shapes:
+        for (S, B) in ((C, 0), (C + 2, 1)):
+            opts = token_options(E, k)
+            x = (np.arange(T * H, dtype=np.uint16) + 1).reshape(T, H)
+            w = (np.arange(T * k, dtype=np.float32).reshape(T, k) + 1) / 64.0
+            for choice in itertools.product(range(len(opts)), repeat=T):
+                idx = np.array([opts[c] for c in choice], np.int32).reshape(T, k)
+                tpe, _, _, _, _, keys = sorted_key_reference(idx, E, 1)
+                d = orc.dispatch_padded(x, None, idx, w, E, C, S, B, fill=0)
+                want = -np.ones((T, k), np.int64)
+                seen = {}
+                for (e, t, j) in keys:
+                    i = seen.get(e, 0)
+                    seen[e] = i + 1
+                    if i < C:
+                        want[t, j] = e * S + B + i
+                assert np.array_equal(d["slot_to_row"], want), (idx, C, S, B, d["slot_to_row"], want)
+                assert d["status"] == (16 if tpe.max(initial=0) > C else 0), (idx, C, d["status"])
+                taken = set(int(r) for r in want.ravel() if r >= 0)
+                for t in range(T):
+                    for j in range(k):
+                        r = want[t, j]
+                        if r >= 0:
+                            assert d["recv_src_idx"][r] == t and d["recv_weights"][r] == w[t, j]
+                            assert np.array_equal(d["recv_x"][r], x[t])
+                for r in range(E * S):
+                    if r not in taken:
+                        assert d["recv_src_idx"][r] == -1 and not d["recv_x"][r].any()
+
+
+def check_padded_vs_flat(orc, wl, S_extra=3, B=2):
+    """Without overflow the padded layout is the flat one shifted per expert:
+    the row of a slot is e*S + B + (its flat row - expert_offsets[e]); rows,
+    scales, sources and weights follow the slot."""
+    d = orc.dispatch(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E)
+    off = d["expert_offsets"]
+    C = int(np.diff(off).max(initial=0))
+    S = C + B + S_extra
+    p = orc.dispatch_padded(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E, C, S, B)
+    assert p["status"] == d["status"]
+    flat = d["slot_to_row"]
+    idx = wl.topk_idx
+    routed = flat >= 0
+    e = np.where(routed, idx, 0).astype(np.int64)
+    want = np.where(routed, e * S + B + (flat - off[e]), -1)
+    assert np.array_equal(p["slot_to_row"], want)
+    fr = flat[routed]
+    pr = want[routed]
+    assert np.array_equal(p["recv_x"][pr], d["recv_x"][fr])
+    assert np.array_equal(p["recv_src_idx"][pr], d["recv_src_idx"][fr])
+    assert np.array_equal(p["recv_weights"][pr].view(np.uint32), d["recv_weights"][fr].view(np.uint32))
+    if d["recv_scales"] is not None:
+        assert np.array_equal(p["recv_scales"][pr], d["recv_scales"][fr])
+    # one capacity less than the fullest expert: exactly its last slot is dropped
+    if C > 0:
+        q = orc.dispatch_padded(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E, C - 1, S, B)
+        assert q["status"] & 16
+        assert (q["slot_to_row"] >= 0).sum() == routed.sum() - int((np.diff(off) == C).sum())
+
+
+def check_padded_all(orc):
+    check_padded_example(orc)
+    check_padded_bruteforce(orc)
+    for wl in (W.config(1), W.config(4),
+               W.make_workload("padded_zipf", 300, 64, 64, 8, 8, seed=56, routing="zipf", mask_frac=0.1)):
+        check_padded_vs_flat(orc, wl)
+
+
 ALL_BASIC = [check_bf16_rounding, check_bruteforce, check_combine_exact_dyadic, check_combine_k1_inverse,
-             check_worked_example, check_error_status]
+             check_worked_example, check_error_status, check_padded_all]
 
 
 def small_configs():

@@ -101,6 +101,14 @@ MUTANTS = {
     # group combine: the last group dropped
     "group_combine_drop": ("            for (int g = 0; g < G; ++g) {\n                int32_t r = token_group_row",
                            "            for (int g = 0; g + 1 < G; ++g) {\n                int32_t r = token_group_row"),
+    # padded layout: one slot too many kept per expert
+    "padded_capacity": ("if (i >= C) {", "if (i > C) {"),
+    # padded layout: this source's first row inside the slab ignored
+    "padded_no_base": ("int64_t q = (int64_t)id * S + B + i;", "int64_t q = (int64_t)id * S + i;"),
+    # padded layout: slabs spaced by the capacity instead of the stride
+    "padded_stride": ("int64_t q = (int64_t)id * S + B + i;", "int64_t q = (int64_t)id * C + B + i;"),
+    # padded layout: overflow not reported
+    "padded_no_status": ("st |= ORACLE_ERR_OVERFLOW;", "st |= 0;"),
     # quantised dispatch: the scales are not moved with the rows
     "quant_scales_dropped": ("st = oracle_dispatch(T, k, E, H, scale_bytes, q, sc, topk_idx",
                              "st = oracle_dispatch(T, k, E, H, scale_bytes, q, NULL, topk_idx"),

@@ -115,3 +115,21 @@ def test_group_path_invariants_and_closed_form(orc, i):
     wl = K.group_configs()[i]
     K.check_groups_invariants(orc, wl)
     K.check_groups_combine_closed_form(orc, wl, K.GROUP_BOUND[wl.expert_kind])
+
+
+def test_padded_worked_example(orc):
+    K.check_padded_example(orc)
+
+
+def test_padded_bruteforce_every_tiny_routing(orc):
+    K.check_padded_bruteforce(orc)
+
+
+@pytest.mark.parametrize("cid", [1, 4])
+def test_padded_is_flat_shifted_per_expert(orc, cid):
+    K.check_padded_vs_flat(orc, W.config(cid))
+
+
+def test_padded_is_flat_shifted_per_expert_zipf(orc):
+    K.check_padded_vs_flat(orc, W.make_workload("padded_zipf", 300, 64, 64, 8, 8, seed=56, routing="zipf",
+                                                mask_frac=0.1))
