@@ -417,7 +417,8 @@ def run_gpu_decode(cid, steps, warmup, dev):
     """Decode-step latency on config `cid` (T=128): the four calls (layout,
     notify, scatter, combine), the small-batch path (layout + dispatch in one
     launch, then combine), and that path replayed from a captured HIP graph
-    of 10 steps.  Each figure is the mean GPU time per step over back-to-back
+    of 10 steps, also with the padded (low-latency) receive layout of T rows
+    per expert.  Each figure is the mean GPU time per step over back-to-back
     steps between two events."""
     import torch
     import combine_ep_get_dispatch_amd as M
@@ -477,6 +478,23 @@ def run_gpu_decode(cid, steps, warmup, dev):
         for _ in range(per_graph):
             small(torch.cuda.current_stream())
     res["small_graph_us"] = per_step(lambda stream: graph.replay()) / per_graph
+    # the same step with the padded layout: expert e's rows at [e*T, e*T + T)
+    pb = M.EpPaddedBuffers(bufs, wl.T, wl.T, 0)
+    eo_pad = torch.zeros((wl.E * wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+
+    def small_padded(stream):
+        pb.dispatch(x, xs, idx, w, stream)
+        pb.combine(eo_pad, out, M.BF16, True, stream)
+
+    with torch.cuda.stream(side):
+        small_padded(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_pad = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_pad):
+        for _ in range(per_graph):
+            small_padded(torch.cuda.current_stream())
+    res["small_padded_graph_us"] = per_step(lambda stream: graph_pad.replay()) / per_graph
     # the small-batch dispatch alone, events around each call
     stream = torch.cuda.current_stream()
     g = EventGrid(steps, 2)
@@ -493,7 +511,7 @@ def run_gpu_decode(cid, steps, warmup, dev):
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
     res["step_bytes"] = B["step"]
     res["tokens_per_s_graph"] = wl.T / (res["small_graph_us"] * 1e-6)
-    del graph, bufs, x, xs, idx, w, eo, out
+    del graph, graph_pad, pb, eo_pad, bufs, x, xs, idx, w, eo, out
     torch.cuda.empty_cache()
     return res
 

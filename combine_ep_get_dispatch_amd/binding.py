@@ -39,13 +39,14 @@ DEV_BAD_EXPERT_ID = 1
 DEV_DUPLICATE_EXPERT = 2
 DEV_BAD_LAYOUT = 4
 DEV_BAD_HANDLE = 8
+DEV_EXPERT_OVERFLOW = 16
 
 EXPORTS = ("ep_workspace_bytes", "ep_workspace_init", "ep_get_dispatch_layout", "ep_get_dispatch_layout_notify",
            "ep_dispatch", "ep_dispatch_noalloc",
            "ep_dispatch_notify", "ep_dispatch_scatter", "ep_dispatch_quant", "ep_dispatch_scatter_quant",
            "ep_dispatch_groups", "ep_group_permute", "ep_group_reduce", "ep_combine_groups",
-           "ep_layout_dispatch_small",
-           "ep_combine", "ep_check_status", "ep_status_string")
+           "ep_layout_dispatch_small", "ep_layout_dispatch_small_padded",
+           "ep_combine", "ep_combine_padded", "ep_check_status", "ep_status_string")
 # tools (include/moedisp_tools.h): plan query and calibration probes, exported
 # by the same library
 CALIB_EXPORTS = ("ep_plan_query", "ep_probe_read", "ep_probe_copy", "ep_probe_fill")
@@ -160,6 +161,11 @@ def load(path: str = LIB_PATH):
     L.ep_combine_groups.restype = C.c_int
     L.ep_combine.argtypes = [S, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
     L.ep_combine.restype = C.c_int
+    L.ep_layout_dispatch_small_padded.argtypes = [S, C.c_int32, C.c_int32, C.c_int32, P, P, P, P, P, P, P, P, P, P,
+                                                  P, P, P, C.c_size_t, P]
+    L.ep_layout_dispatch_small_padded.restype = C.c_int
+    L.ep_combine_padded.argtypes = [S, C.c_int32, P, P, P, P, P, C.c_int32, P, C.c_size_t, P]
+    L.ep_combine_padded.restype = C.c_int
     L.ep_check_status.argtypes = [P, C.c_size_t, P, C.POINTER(C.c_int32)]
     L.ep_check_status.restype = C.c_int
     L.ep_status_string.argtypes = [C.c_int]
@@ -442,6 +448,32 @@ def ep_layout_dispatch_small(shape, x, x_scales, topk_idx, topk_weights, tokens_
         _p(recv_weights), _p(expert_offsets), _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
 
 
+def ep_layout_dispatch_small_padded(shape, expert_capacity, expert_stride, row_base, x, x_scales, topk_idx,
+                                    topk_weights, tokens_per_expert, tokens_per_group, is_token_in_group, recv_x,
+                                    recv_scales, recv_src_idx, recv_weights, slot_to_row, ws, stream=None):
+    A = _Args("ep_layout_dispatch_small_padded")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    rows = E * max(int(expert_stride), 0)
+    A.need("x", x, _rows_dtypes(shape), T * rb)
+    A.need("x_scales", x_scales, _F32, 4 * T * nsc, optional=nsc == 0)
+    A.need("topk_idx", topk_idx, _INT32, 4 * T * k)
+    A.need("topk_weights", topk_weights, _F32, 4 * T * k)
+    A.need("tokens_per_expert", tokens_per_expert, _INT32, 4 * E)
+    A.need("tokens_per_group", tokens_per_group, _INT32, 4 * G)
+    A.need("is_token_in_group", is_token_in_group, _I32, 4 * T)
+    A.need("recv_x", recv_x, _rows_dtypes(shape), rows * rb)
+    A.need("recv_scales", recv_scales, _F32, 4 * rows * nsc, optional=nsc == 0)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * rows)
+    A.need("recv_weights", recv_weights, _F32, 4 * rows)
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_layout_dispatch_small_padded(
+        C.byref(shape), int(expert_capacity), int(expert_stride), int(row_base), _p(x), _p(x_scales), _p(topk_idx),
+        _p(topk_weights), _p(tokens_per_expert), _p(tokens_per_group), _p(is_token_in_group), _p(recv_x),
+        _p(recv_scales), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(ws), _nb(ws), _s(stream)))
+
+
 def ep_dispatch_groups(shape, x, x_scales, topk_idx, topk_weights, is_token_in_group, tokens_per_group, recv_x,
                        recv_scales, recv_src_idx, recv_topk_idx, recv_topk_weights, group_offsets, token_group_row, ws,
                        stream=None):
@@ -543,6 +575,23 @@ def ep_combine(shape, expert_out, recv_src_idx, recv_weights, slot_to_row, out, 
     _check(A.call, load().ep_combine(
         C.byref(shape), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row), _p(out),
         int(out_dtype), _p(ws), _nb(ws), _s(stream)))
+
+
+def ep_combine_padded(shape, expert_stride, expert_out, recv_src_idx, recv_weights, slot_to_row, out, out_dtype, ws,
+                      stream=None):
+    A = _Args("ep_combine_padded")
+    T, H, E, G, k, rb, nsc = _dims(shape)
+    rows = E * max(int(expert_stride), 0)
+    A.need("expert_out", expert_out, _ROWS_BF16, rows * H * 2)
+    A.need("recv_src_idx", recv_src_idx, _INT32, 4 * rows, optional=True)
+    A.need("recv_weights", recv_weights, _F32, 4 * rows)
+    A.need("slot_to_row", slot_to_row, _INT32, 4 * T * k)
+    A.need("out", out, _out_dtypes(int(out_dtype)), _out_bytes(T, H, out_dtype))
+    _ws(A, ws)
+    A.done()
+    _check(A.call, load().ep_combine_padded(
+        C.byref(shape), int(expert_stride), _p(expert_out), _p(recv_src_idx), _p(recv_weights), _p(slot_to_row),
+        _p(out), int(out_dtype), _p(ws), _nb(ws), _s(stream)))
 
 
 def ep_check_status(ws, stream=None) -> int:
@@ -667,6 +716,40 @@ class EpBuffers:
 
     def status(self, stream=None) -> int:
         return ep_check_status(self.ws, stream)
+
+
+class EpPaddedBuffers:
+    """Receive buffers of the padded (low-latency) layout (plumbing) next to an
+    EpBuffers of the same shape, whose layout outputs and workspace it uses:
+    E * expert_stride rows; expert e's rows start at e * expert_stride +
+    row_base, at most expert_capacity of them."""
+
+    def __init__(self, bufs: EpBuffers, expert_capacity: int, expert_stride: int = None, row_base: int = 0):
+        s = bufs.shape
+        self.bufs, self.shape, d = bufs, s, bufs.device
+        self.capacity = int(expert_capacity)
+        self.stride = int(expert_capacity if expert_stride is None else expert_stride)
+        self.base = int(row_base)
+        rows = s.num_experts * self.stride
+        self.rows = rows
+        fp8 = s.x_dtype == FP8_E4M3
+        self.recv_x = torch.empty((rows, s.hidden * (1 if fp8 else 2)), dtype=torch.uint8, device=d)
+        nsc = s.hidden // s.scale_block if fp8 else 0
+        self.recv_scales = torch.empty((rows, nsc), dtype=torch.float32, device=d) if nsc else None
+        self.recv_src_idx = torch.empty(rows, dtype=torch.int32, device=d)
+        self.recv_weights = torch.empty(rows, dtype=torch.float32, device=d)
+        self.slot_to_row = torch.empty((max(s.num_tokens, 1), s.topk), dtype=torch.int32, device=d)
+
+    def dispatch(self, x, x_scales, topk_idx, topk_weights, stream=None):
+        b = self.bufs
+        ep_layout_dispatch_small_padded(self.shape, self.capacity, self.stride, self.base, x, x_scales, topk_idx,
+                                        topk_weights, b.tokens_per_expert, b.tokens_per_group, b.is_token_in_group,
+                                        self.recv_x, self.recv_scales, self.recv_src_idx, self.recv_weights,
+                                        self.slot_to_row, b.ws, stream)
+
+    def combine(self, expert_out, out, out_dtype=BF16, check_src=True, stream=None):
+        ep_combine_padded(self.shape, self.stride, expert_out, self.recv_src_idx if check_src else None,
+                          self.recv_weights, self.slot_to_row, out, out_dtype, self.bufs.ws, stream)
 
 
 class EpGroupBuffers:

@@ -765,9 +765,19 @@ int ep_dispatch_quant(const moedisp_shape* s, int32_t quant_block, int32_t scale
     return hip_status(launch_dispatch_scatter_quant(a, scale_fmt, (hipStream_t)stream));
 }
 
-int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,
-               const float* recv_weights, const int32_t* slot_to_row, void* out, int32_t out_dtype, void* ws,
-               size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Padded-layout arguments: C >= 0, B >= 0, B + C <= S, E * S < 2^31.
+static int check_padded(const moedisp_shape* s, long long C, long long S, long long B) {
+    if (C < 0 || B < 0 || S < 1 || B + C > S) return MOEDISP_ERR_INVALID_ARG;
+    if ((long long)s->num_experts * S > 0x7FFFFFFFll) return MOEDISP_ERR_UNSUPPORTED;
+    return MOEDISP_OK;
+}
+
+// ep_combine over receive buffers of `capacity` rows.
+static int flat_combine(const moedisp_shape* s, int capacity, const void* expert_out, const int32_t* recv_src_idx,
+                        const float* recv_weights, const int32_t* slot_to_row, void* out, int32_t out_dtype,
+                        void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(s);
     if (st) return st;
     if (out_dtype != MOEDISP_BF16 && out_dtype != MOEDISP_FP32) return MOEDISP_ERR_UNSUPPORTED;
@@ -783,7 +793,7 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     a.T = s->num_tokens;
     a.k = s->topk;
     a.row16 = (int)((size_t)s->hidden * 2 / 16);
-    a.capacity = s->num_tokens * s->topk;
+    a.capacity = capacity;
     a.col_splits = p.col_splits;
     a.threads = p.threads;
     a.units_per_lane = p.units_per_lane;
@@ -797,19 +807,44 @@ int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* re
     return hip_status(launch_combine(a, out_dtype == MOEDISP_FP32, (hipStream_t)stream));
 }
 
+extern "C" {
+
+int ep_combine(const moedisp_shape* s, const void* expert_out, const int32_t* recv_src_idx,
+               const float* recv_weights, const int32_t* slot_to_row, void* out, int32_t out_dtype, void* ws,
+               size_t ws_bytes, void* stream) {
+    const int st = check_shape(s);
+    if (st) return st;
+    return flat_combine(s, s->num_tokens * s->topk, expert_out, recv_src_idx, recv_weights, slot_to_row, out,
+                        out_dtype, ws, ws_bytes, stream);
+}
+
+int ep_combine_padded(const moedisp_shape* s, int32_t expert_stride, const void* expert_out,
+                      const int32_t* recv_src_idx, const float* recv_weights, const int32_t* slot_to_row,
+                      void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if ((st = check_padded(s, 0, expert_stride, 0))) return st;
+    return flat_combine(s, s->num_experts * expert_stride, expert_out, recv_src_idx, recv_weights, slot_to_row,
+                        out, out_dtype, ws, ws_bytes, stream);
+}
+
 // ---------------------------------------------------------------------------
 // Small-batch path: layout + dispatch in one launch
 
-int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
-                             const float* topk_weights, int32_t* tokens_per_expert, int32_t* tokens_per_group,
-                             uint32_t* is_token_in_group, void* recv_x, float* recv_scales, int32_t* recv_src_idx,
-                             float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row, void* ws,
-                             size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// The small path's checks and launch; pad_s > 0 for the padded layout (no
+// expert_offsets).
+static int small_call(const moedisp_shape* s, int pad_c, int pad_s, int pad_b, const void* x,
+                      const float* x_scales, const int32_t* topk_idx, const float* topk_weights,
+                      int32_t* tokens_per_expert, int32_t* tokens_per_group, uint32_t* is_token_in_group,
+                      void* recv_x, float* recv_scales, int32_t* recv_src_idx, float* recv_weights,
+                      int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(s);
     if (st) return st;
     const bool fp8 = s->x_dtype == MOEDISP_FP8_E4M3;
     if (!plan_small(*s).supported) return MOEDISP_ERR_UNSUPPORTED;
-    if (!tokens_per_expert || !tokens_per_group || !expert_offsets) return MOEDISP_ERR_INVALID_ARG;
+    if (!tokens_per_expert || !tokens_per_group || (pad_s == 0 && !expert_offsets)) return MOEDISP_ERR_INVALID_ARG;
     if (s->num_tokens > 0 && (!x || !topk_idx || !topk_weights || !is_token_in_group || !recv_x || !recv_src_idx ||
                               !recv_weights || !slot_to_row))
         return MOEDISP_ERR_INVALID_ARG;
@@ -831,10 +866,13 @@ int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float*
     group_index_constants(a.experts_per_group, &a.pg_shift, &a.pg_magic);
     a.row16 = (int)(row_bytes(*s) / 16);
     a.scale_words = fp8 ? scales_per_row(*s) : 0;
-    a.capacity = s->num_tokens * s->topk;
+    a.capacity = pad_s > 0 ? s->num_experts * pad_s : s->num_tokens * s->topk;
     a.split_units = sp.split_units;
     a.col_splits = sp.col_splits;
     a.threads = sp.threads;
+    a.pad_c = pad_c;
+    a.pad_s = pad_s;
+    a.pad_b = pad_b;
     a.x = (const v4u*)x;
     a.x_scales = fp8 ? x_scales : nullptr;
     a.topk_idx = topk_idx;
@@ -846,10 +884,37 @@ int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float*
     a.recv_scales = fp8 ? recv_scales : nullptr;
     a.recv_src_idx = recv_src_idx;
     a.recv_weights = recv_weights;
-    a.expert_offsets = expert_offsets;
+    a.expert_offsets = pad_s > 0 ? nullptr : expert_offsets;
     a.slot_to_row = slot_to_row;
     a.hdr = (WsHeader*)ws;
     return hip_status(launch_dispatch_fused(a, (hipStream_t)stream));
+}
+
+extern "C" {
+
+int ep_layout_dispatch_small(const moedisp_shape* s, const void* x, const float* x_scales, const int32_t* topk_idx,
+                             const float* topk_weights, int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                             uint32_t* is_token_in_group, void* recv_x, float* recv_scales, int32_t* recv_src_idx,
+                             float* recv_weights, int32_t* expert_offsets, int32_t* slot_to_row, void* ws,
+                             size_t ws_bytes, void* stream) {
+    return small_call(s, 0, 0, 0, x, x_scales, topk_idx, topk_weights, tokens_per_expert, tokens_per_group,
+                      is_token_in_group, recv_x, recv_scales, recv_src_idx, recv_weights, expert_offsets,
+                      slot_to_row, ws, ws_bytes, stream);
+}
+
+int ep_layout_dispatch_small_padded(const moedisp_shape* s, int32_t expert_capacity, int32_t expert_stride,
+                                    int32_t row_base, const void* x, const float* x_scales,
+                                    const int32_t* topk_idx, const float* topk_weights,
+                                    int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                                    uint32_t* is_token_in_group, void* recv_x, float* recv_scales,
+                                    int32_t* recv_src_idx, float* recv_weights, int32_t* slot_to_row, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if ((st = check_padded(s, expert_capacity, expert_stride, row_base))) return st;
+    return small_call(s, expert_capacity, expert_stride, row_base, x, x_scales, topk_idx, topk_weights,
+                      tokens_per_expert, tokens_per_group, is_token_in_group, recv_x, recv_scales, recv_src_idx,
+                      recv_weights, nullptr, slot_to_row, ws, ws_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------

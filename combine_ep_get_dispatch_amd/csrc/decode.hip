@@ -22,6 +22,16 @@
 // group counts) and checks ids and repeats, in parallel with the copies, one
 // lane per token; column range 0 of each token writes its handle and fp8
 // scales.
+//
+// Padded (low-latency) layout ("MSCCLPP EP implementation - #852": the
+// low-latency port gives every expert its own receive slots, sized by a
+// maximum token count, with per-expert received counts; a later commit adds
+// a rank-major output option).  Expert e owns rows [e*S + B, e*S + B + C);
+// slot (t, j) with expert e takes row e*S + B + i, where
+//     i = #{routed slots s : e * n <= key(s) < key(t, j)}
+// is its rank among e's routed slots, counted in the same pass with a lower
+// bound per key; a slot with i >= C gets no row (EXPERT_OVERFLOW).  No
+// offsets are needed, so the layout workgroup writes none.
 #include "kernels_common.h"
 
 namespace moedisp {
@@ -116,14 +126,14 @@ __device__ void fused_layout(const FusedArgs& a, int32_t* dyn, int32_t* s_gcnt, 
     const int total = lds_exclusive_scan(s_cnt, E, s_off, s_wave);
     for (int e = tid; e < E; e += nth) {
         a.tokens_per_expert[e] = s_cnt[e];
-        a.expert_offsets[e] = s_off[e];
+        if (a.expert_offsets) a.expert_offsets[e] = s_off[e];
     }
-    if (tid == 0) a.expert_offsets[E] = total;
+    if (tid == 0 && a.expert_offsets) a.expert_offsets[E] = total;
     for (int g = tid; g < a.G; g += nth) a.tokens_per_group[g] = s_gcnt[g];
 }
 
-// KM: the largest k this instance serves (8 or 32).
-template <int KM>
+// KM: the largest k this instance serves (8 or 32); PAD: the padded layout.
+template <int KM, bool PAD>
 __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_dispatch_fused(FusedArgs a) {
     extern __shared__ int32_t dyn[];  // layout workgroup: counts [E], offsets [E]
     __shared__ int32_t s_part[(kMaxDispatchThreads / 64) * KM];  // per-wave counts below the token's keys
@@ -166,9 +176,13 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_dispatch_fused(Fu
             if (tid < a.scale_words) scale = a.x_scales[(size_t)t * a.scale_words + tid];
         }
         const int kj = (lane < k && ej >= 0 && ej < E) ? ej * n + sj : -1;
-        int key_t[KM];
+        int key_t[KM], lo_t[KM];
 #pragma unroll
         for (int j = 0; j < KM; ++j) key_t[j] = __builtin_amdgcn_readlane(kj, j);
+        if (PAD) {  // the first key of the slot's expert
+#pragma unroll
+            for (int j = 0; j < KM; ++j) lo_t[j] = key_t[j] >= 0 ? key_t[j] - key_t[j] % n : 0;
+        }
         if (tid < KM) s_key[tid] = kj;
         // keys below each of the token's, over this lane's share of the table
         int c[KM];
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_dispatch_fused(Fu
                 const int s = i0 + q * nth + tid;
                 const int key = (s < n && v[q] >= 0 && v[q] < E) ? v[q] * n + s : 0x7FFFFFFF;
 #pragma unroll
-                for (int j = 0; j < KM; ++j) c[j] += key < key_t[j] ? 1 : 0;
+                for (int j = 0; j < KM; ++j) c[j] += (key < key_t[j] && (!PAD || key >= lo_t[j])) ? 1 : 0;
             }
         }
 #pragma unroll
@@ -200,8 +214,16 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_dispatch_fused(Fu
             if (s_key[tid] >= 0) {
                 r = 0;
                 for (int w = 0; w < nth / 64; ++w) r += s_part[w * KM + tid];
+                if (PAD) {  // r is the slot's rank among its expert's slots
+                    if (r >= a.pad_c) {
+                        err |= MOEDISP_DEV_EXPERT_OVERFLOW;
+                        r = -1;
+                    } else {
+                        r += (s_key[tid] / n) * a.pad_s + a.pad_b;  // < E * pad_s: inside the buffer
+                    }
+                }
             }
-            s_row[tid] = r;  // < the routed total <= T * k: inside the buffer
+            s_row[tid] = r;  // flat: < the routed total <= T * k, inside the buffer
         }
         __syncthreads();
 
@@ -244,10 +266,18 @@ hipError_t launch_dispatch_fused(const FusedArgs& a, hipStream_t stream) {
     // the layout workgroup's tables
     const size_t lds = 2 * (size_t)a.E * sizeof(int32_t);
     const unsigned blocks = (unsigned)(a.T * a.col_splits) + 1u;  // + the layout workgroup
-    if (a.k <= 8)
-        hipLaunchKernelGGL(moedisp_dispatch_fused<8>, dim3(blocks), dim3(a.threads), lds, stream, a);
-    else
-        hipLaunchKernelGGL(moedisp_dispatch_fused<kMaxTopk>, dim3(blocks), dim3(a.threads), lds, stream, a);
+    if (a.pad_s > 0) {
+        if (a.pad_c < 0 || a.pad_b < 0 || (long long)a.pad_b + a.pad_c > a.pad_s) return hipErrorInvalidValue;
+        if (a.k <= 8)
+            hipLaunchKernelGGL((moedisp_dispatch_fused<8, true>), dim3(blocks), dim3(a.threads), lds, stream, a);
+        else
+            hipLaunchKernelGGL((moedisp_dispatch_fused<kMaxTopk, true>), dim3(blocks), dim3(a.threads), lds, stream,
+                               a);
+    } else if (a.k <= 8) {
+        hipLaunchKernelGGL((moedisp_dispatch_fused<8, false>), dim3(blocks), dim3(a.threads), lds, stream, a);
+    } else {
+        hipLaunchKernelGGL((moedisp_dispatch_fused<kMaxTopk, false>), dim3(blocks), dim3(a.threads), lds, stream, a);
+    }
     return hipGetLastError();
 }
 

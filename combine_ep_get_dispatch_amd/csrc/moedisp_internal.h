@@ -318,6 +318,9 @@ struct FusedArgs {
     int scale_words;
     int capacity;
     int col_splits, split_units, threads;
+    // padded layout (pad_s > 0): expert e's slots take rows e*pad_s + pad_b + i
+    // for i < pad_c (i = the slot's rank among e's routed slots)
+    int pad_c, pad_s, pad_b;
     const v4u* x;
     const float* x_scales;
     const int32_t* topk_idx;

@@ -89,6 +89,8 @@ typedef struct {
 #define MOEDISP_DEV_DUPLICATE_EXPERT 2u  /* an expert repeated within one token (each copy still routed) */
 #define MOEDISP_DEV_BAD_LAYOUT 4u        /* tokens_per_expert disagrees with topk_idx; bad rows skipped */
 #define MOEDISP_DEV_BAD_HANDLE 8u        /* combine handle inconsistent; those slots skipped */
+#define MOEDISP_DEV_EXPERT_OVERFLOW 16u  /* padded layout: an expert got more slots than its capacity;
+                                            the extra slots get no row (slot_to_row -1) */
 
 /* Bytes of workspace the calls need for `shape`; 0 if the shape is invalid.
  * One workspace serves every call of that shape, and of any other shape whose
@@ -188,20 +190,51 @@ int ep_get_dispatch_layout_notify(const moedisp_shape* shape, const int32_t* top
 /* Small-batch (decode) path: ep_get_dispatch_layout and ep_dispatch in one
  * kernel launch, with exactly their outputs (all of them, bit for bit).  The
  * page's low-latency path is likewise a single kernel tuned for small
- * batches.  Every workgroup recomputes the routing layout from the whole
- * topk_idx in LDS, so no workgroup waits for another; this bounds the size:
- * T*k <= 8192 and (T*k + 2*E + T) * 4 bytes <= 60 KiB, else
- * MOEDISP_ERR_UNSUPPORTED (use the two calls).  Arguments as for the two calls;
- * tokens_per_expert, tokens_per_group and is_token_in_group are outputs here.
- * Status bits: BAD_EXPERT_ID, DUPLICATE_EXPERT.  With no host synchronisation
- * and no allocation, the call (and ep_combine after it) can be captured in a
- * HIP graph. */
+ * batches.  Each copy workgroup finds its token's receive rows from one pass
+ * of comparisons over the whole topk_idx, so no workgroup waits for another;
+ * the work grows with T * (T*k), which bounds the size: T*k <= 8192 and
+ * (T*k + 2*E + T) * 4 bytes <= 60 KiB, else MOEDISP_ERR_UNSUPPORTED (use the
+ * two calls).  Arguments as for the two calls; tokens_per_expert,
+ * tokens_per_group and is_token_in_group are outputs here.  Status bits:
+ * BAD_EXPERT_ID, DUPLICATE_EXPERT.  With no host synchronisation and no
+ * allocation, the call (and ep_combine after it) can be captured in a HIP
+ * graph. */
 int ep_layout_dispatch_small(const moedisp_shape* shape, const void* x, const float* x_scales,
                              const int32_t* topk_idx, const float* topk_weights, int32_t* tokens_per_expert,
                              int32_t* tokens_per_group, uint32_t* is_token_in_group, void* recv_x,
                              float* recv_scales, int32_t* recv_src_idx, float* recv_weights,
                              int32_t* expert_offsets, int32_t* slot_to_row, void* ws, size_t ws_bytes,
                              void* stream);
+
+/* Small-batch path with the padded (low-latency) receive layout
+ * ("MSCCLPP EP implementation - #852": the commit porting the low-latency
+ * kernels gives every expert its own receive slots, sized by a maximum
+ * number of dispatched tokens, and signals received counts per expert; a
+ * later commit adds a rank-major output option to that path).  Expert e owns
+ * the rows [e*expert_stride + row_base, e*expert_stride + row_base +
+ * expert_capacity) of receive buffers of E*expert_stride rows; its routed
+ * slots take them in ascending slot order (token order), the i-th at
+ * e*expert_stride + row_base + i.  A slot past its expert's first
+ * expert_capacity gets no row: slot_to_row -1 and status EXPERT_OVERFLOW.
+ * Rows no slot takes are not written.  Expert e's received count is
+ * min(tokens_per_expert[e], expert_capacity); there are no offsets.  With
+ * several sources, source r of N would write its rows at row_base = r*C
+ * inside slabs of expert_stride = N*C rows, with no count from any other
+ * source needed.
+ *   expert_capacity  C >= 0;  row_base >= 0;  row_base + C <= expert_stride;
+ *                    E * expert_stride < 2^31 (else INVALID_ARG / UNSUPPORTED)
+ *   recv_x           [E*expert_stride][H] (bf16 or fp8 codes), recv_scales
+ *                    [E*expert_stride][H/scale_block] for fp8,
+ *                    recv_src_idx, recv_weights [E*expert_stride]
+ * Other arguments, size limits and status bits as ep_layout_dispatch_small
+ * (no expert_offsets).  ep_combine_padded reads these rows back. */
+int ep_layout_dispatch_small_padded(const moedisp_shape* shape, int32_t expert_capacity, int32_t expert_stride,
+                                    int32_t row_base, const void* x, const float* x_scales,
+                                    const int32_t* topk_idx, const float* topk_weights,
+                                    int32_t* tokens_per_expert, int32_t* tokens_per_group,
+                                    uint32_t* is_token_in_group, void* recv_x, float* recv_scales,
+                                    int32_t* recv_src_idx, float* recv_weights, int32_t* slot_to_row, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Dispatch with quantisation: as ep_dispatch for a bf16 x, but every
  * received row holds OCP E4M3 codes of the token's row plus one scale per
@@ -317,6 +350,15 @@ int ep_combine_groups(const moedisp_shape* shape, const void* group_rows, const 
 int ep_combine(const moedisp_shape* shape, const void* expert_out, const int32_t* recv_src_idx,
                const float* recv_weights, const int32_t* slot_to_row, void* out,
                int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ep_combine over the padded layout of ep_layout_dispatch_small_padded: the
+ * same sum, with expert_out bf16 [E*expert_stride][H] and slot_to_row,
+ * recv_weights (and recv_src_idx, if given) from that call.  Status bits:
+ * BAD_HANDLE (a row outside the E*expert_stride rows, or naming another
+ * token). */
+int ep_combine_padded(const moedisp_shape* shape, int32_t expert_stride, const void* expert_out,
+                      const int32_t* recv_src_idx, const float* recv_weights, const int32_t* slot_to_row,
+                      void* out, int32_t out_dtype, void* ws, size_t ws_bytes, void* stream);
 
 /* Wait for `stream`, then return the device status bits accumulated in `ws`
  * since the last check in *host_status and clear them. */

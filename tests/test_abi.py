@@ -245,6 +245,28 @@ def test_host_checks_layout_dispatch_small(lib):
                                         p(), p(), p(), p(), 1 << 30, None) == B.ERR_INVALID_ARG
 
 
+def test_host_checks_layout_dispatch_small_padded(lib):
+    def rc(sh, C_=128, S=128, B_=0, x=None, ws_bytes=1 << 30, tpe=None):
+        return lib.ep_layout_dispatch_small_padded(C.byref(sh), C_, S, B_, x or p(), None, p(), p(), tpe or p(), p(),
+                                                   p(), p(), None, p(), p(), p(), p(), ws_bytes, None)
+    assert rc(shape(T=128), C_=-1) == B.ERR_INVALID_ARG           # negative capacity
+    assert rc(shape(T=128), B_=-1) == B.ERR_INVALID_ARG           # negative base
+    assert rc(shape(T=128), S=0, C_=0) == B.ERR_INVALID_ARG       # no slab
+    assert rc(shape(T=128), C_=100, S=128, B_=29) == B.ERR_INVALID_ARG  # base + capacity past the slab
+    assert rc(shape(T=128, E=256), C_=1, S=1 << 23) == B.ERR_UNSUPPORTED  # E * S >= 2^31 rows
+    assert rc(shape(T=4096)) == B.ERR_UNSUPPORTED                 # the small path's own limit
+    assert rc(shape(T=128), x=p(8)) == B.ERR_MISALIGNED
+    assert rc(shape(T=128), ws_bytes=64) == B.ERR_WORKSPACE_TOO_SMALL
+    assert rc(shape(T=128, dt=M.FP8_E4M3, sb=128)) == B.ERR_INVALID_ARG  # fp8 without scales
+    # combine over the padded rows: the same host checks as ep_combine, plus the slab
+    assert lib.ep_combine_padded(C.byref(shape(T=128)), 0, p(), p(), p(), p(), p(), M.BF16, p(), 1 << 30,
+                                 None) == B.ERR_INVALID_ARG
+    assert lib.ep_combine_padded(C.byref(shape(T=128)), 1 << 23, p(), p(), p(), p(), p(), M.BF16, p(), 1 << 30,
+                                 None) == B.ERR_UNSUPPORTED
+    assert lib.ep_combine_padded(C.byref(shape(T=128)), 128, p(2), p(), p(), p(), p(), M.BF16, p(), 1 << 30,
+                                 None) == B.ERR_MISALIGNED
+
+
 def test_host_checks_combine(lib):
     assert combine_rc(lib, shape(), out_dtype=M.FP8_E4M3) == B.ERR_UNSUPPORTED
     assert combine_rc(lib, shape(), eo=p(2)) == B.ERR_MISALIGNED

@@ -194,3 +194,137 @@ def test_prefill_step_in_hip_graph(orc, dev):
         assert rel.size == 0 or rel.max() <= GH.COMBINE_REL_TOL
         assert np.all(g32[~nz] == 0.0)
         _say(f"[graph-prefill] replay {rep} ok R={R}")
+
+
+# --- padded (low-latency) layout ---------------------------------------------
+
+def run_padded(orc, wl, dev, C, S, B):
+    """ep_layout_dispatch_small_padded against the oracle: layout outputs,
+    handle, every taken row (bytes, scales, source, weight bits) exact, and
+    every row no slot takes still holding its sentinel."""
+    o = orc.dispatch_padded(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E, C, S, B)
+    tpe, tpg, bm, st_l = orc.layout(wl.topk_idx, wl.E, wl.G)
+    bufs = M.EpBuffers(GH.shape_of(wl), dev)
+    pb = M.EpPaddedBuffers(bufs, C, S, B)
+    pb.recv_x.fill_(0xA5)
+    pb.recv_src_idx.fill_(-9)
+    pb.recv_weights.fill_(-1.0)
+    if pb.recv_scales is not None:
+        pb.recv_scales.fill_(-2.0)
+    inp = GH.GpuInputs(wl, dev)
+    pb.dispatch(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    st = bufs.status()
+    assert st == (o["status"] | st_l), f"device status {st} != oracle {o['status'] | st_l}"
+    assert np.array_equal(bufs.tokens_per_expert.cpu().numpy(), tpe)
+    assert np.array_equal(bufs.tokens_per_group.cpu().numpy(), tpg)
+    assert np.array_equal(bufs.is_token_in_group.cpu().numpy().view(np.uint32), bm)
+    s2r = pb.slot_to_row[:wl.T].cpu().numpy()
+    assert np.array_equal(s2r, o["slot_to_row"])
+    rows = wl.E * S
+    taken = np.zeros(rows, bool)
+    taken[o["slot_to_row"][o["slot_to_row"] >= 0]] = True
+    gx = pb.recv_x.cpu().numpy()
+    ox = np.ascontiguousarray(o["recv_x"]).view(np.uint8).reshape(rows, -1)
+    assert np.array_equal(gx[taken], ox[taken]), "taken rows"
+    assert np.all(gx[~taken] == 0xA5), "a row no slot takes was written"
+    assert np.array_equal(pb.recv_src_idx.cpu().numpy()[taken], o["recv_src_idx"][taken])
+    assert np.all(pb.recv_src_idx.cpu().numpy()[~taken] == -9)
+    assert np.array_equal(pb.recv_weights.cpu().numpy()[taken].view(np.uint32),
+                          o["recv_weights"][taken].view(np.uint32))
+    if pb.recv_scales is not None:
+        gs = pb.recv_scales.cpu().numpy()
+        assert np.array_equal(gs[taken].view(np.uint32), o["recv_scales"][taken].view(np.uint32))
+        assert np.all(gs[~taken] == -2.0)
+    return o, bufs, pb, inp
+
+
+def padded_expert_out(orc, wl, o_pad, S):
+    """Stand-in expert outputs at the padded rows: the flat path's output of
+    the same slot, moved to the slot's padded row."""
+    of = GH.oracle_run(orc, wl)
+    eo_flat = GH.oracle_expert_out(wl, of)
+    eo = np.zeros((wl.E * S, wl.H), np.uint16)
+    fr = of["slot_to_row"]
+    pr = o_pad["slot_to_row"]
+    m = pr >= 0
+    eo[pr[m]] = eo_flat[fr[m]]
+    return eo
+
+
+PADDED = {
+    # (workload, C, S, B): C = T is the low-latency buffer's usual size
+    "decode_fp8": (lambda: W.config(4), 128, 128, 0),
+    "decode_fp8_overflow": (lambda: W.config(4), 3, 3, 0),
+    "ragged_base_stride": (lambda: W.make_workload("pad_ragged", 77, 7168, 256, 8, 8, seed=101, routing="zipf",
+                                                   mask_frac=0.1), 20, 27, 5),
+    "k16": (lambda: W.make_workload("pad_k16", 96, 512, 64, 8, 16, seed=102), 96, 100, 4),
+    "e1024": (lambda: W.make_workload("pad_e1024", 128, 1024, 1024, 32, 8, seed=103), 8, 8, 0),
+    "mixtral_overflow": (lambda: W.make_workload("pad_mixtral", 512, 4096, 8, 8, 2, seed=104), 120, 130, 10),
+    "empty": (lambda: W.make_workload("pad_empty", 0, 256, 16, 4, 4, seed=105), 4, 4, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(PADDED))
+def test_layout_dispatch_small_padded_parity(orc, dev, name):
+    mk, C, S, B = PADDED[name]
+    wl = mk()
+    _say(f"[padded] {name} T={wl.T} H={wl.H} E={wl.E} k={wl.k} C={C} S={S} B={B}")
+    o, bufs, pb, _ = run_padded(orc, wl, dev, C, S, B)
+    if "overflow" in name:
+        assert o["status"] & M.binding.DEV_EXPERT_OVERFLOW
+    if wl.T:
+        eo_bits = padded_expert_out(orc, wl, o, S)
+        eo = GH.upload_expert_out(eo_bits, wl.E * S, wl.H, dev)
+        of = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+        ob = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+        pb.combine(eo, of, M.FP32)
+        pb.combine(eo, ob, M.BF16)
+        assert bufs.status() == 0
+        o32, o16 = orc.combine(eo_bits, o["recv_weights"], o["slot_to_row"])
+        GH.assert_combine_close(of.cpu().numpy(), ob.view(torch.int16).cpu().numpy().view(np.uint16), o32, o16)
+    _say(f"[padded] {name} ok")
+
+
+def test_padded_decode_step_in_hip_graph(orc, dev):
+    """Capture padded dispatch + combine; replay with new routing and
+    activations, every replay against the oracle."""
+    base = W.config(4)
+    C = S = base.T
+    bufs = M.EpBuffers(GH.shape_of(base), dev)
+    pb = M.EpPaddedBuffers(bufs, C, S, 0)
+    inp = GH.GpuInputs(base, dev)
+    eo = torch.zeros((base.E * S, base.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((base.T, base.H), dtype=torch.bfloat16, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pb.dispatch(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+        pb.combine(eo, out, M.BF16, True)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pb.dispatch(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+        pb.combine(eo, out, M.BF16, True)
+    for rep, seed in enumerate((106, 107, 108)):
+        wl = W.make_workload(f"pgraph{rep}", base.T, base.H, base.E, base.G, base.k, seed=seed, x_dtype=W.X_FP8,
+                             scale_block=128, routing="zipf" if rep == 1 else "uniform",
+                             mask_frac=0.05 if rep == 2 else 0.0, expert_kind="dequant_identity")
+        o = orc.dispatch_padded(wl.x, wl.x_scales, wl.topk_idx, wl.topk_weights, wl.E, C, S, 0)
+        eo_bits = padded_expert_out(orc, wl, o, S)
+        new = GH.GpuInputs(wl, dev)
+        inp.x.copy_(new.x)
+        inp.x_scales.copy_(new.x_scales)
+        inp.topk_idx.copy_(new.topk_idx)
+        inp.topk_weights.copy_(new.topk_weights)
+        eo.copy_(GH.bits16_to_bf16_tensor(eo_bits).to(dev))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert bufs.status() == 0
+        assert np.array_equal(pb.slot_to_row[:wl.T].cpu().numpy(), o["slot_to_row"])
+        o32, o16 = orc.combine(eo_bits, o["recv_weights"], o["slot_to_row"])
+        g16 = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        d = GH.bf16_ulp_distance(g16, o16)
+        assert d.size == 0 or d.max() <= GH.COMBINE_ULP_TOL, f"replay {rep}: combine off by {int(d.max())} ulp"
+        _say(f"[pgraph] replay {rep} ok")
