@@ -141,8 +141,8 @@ int ep_dispatch(const moedisp_shape* shape, const void* x, const float* x_scales
  * (8 MiB, one per device, held until the process ends) instead of `ws`: the
  * call allocates nothing, and the caller passes only inputs and outputs.
  * Shapes whose ep_workspace_bytes exceeds 8 MiB return
- * MOEDISP_ERR_WORKSPACE_TOO_SMALL (at H = 7168, E = 256, k = 8: up to
- * T = 65536) before any HIP call.  The current device must be the stream's.
+ * MOEDISP_ERR_WORKSPACE_TOO_SMALL before any HIP call (at H = 7168, E = 256,
+ * G = 8, k = 8 every T up to 345856 fits).  The current device must be the stream's.
  * Arguments as for ep_dispatch, except:
  *   status  int32 [1], device: overwritten with this call's status bits
  *           (BAD_EXPERT_ID, BAD_LAYOUT), ready when the stream reaches the

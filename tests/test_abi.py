@@ -90,10 +90,13 @@ def test_host_checks_dispatch_noalloc(lib):
     assert noalloc_rc(lib, shape(), status=p(2)) == B.ERR_MISALIGNED
     assert noalloc_rc(lib, shape(E=255), status=p()) == B.ERR_INVALID_ARG
     assert noalloc_rc(lib, shape(), status=p(), x=p(8)) == B.ERR_MISALIGNED
-    for T, E, G in ((1000000, 256, 8), (65536, 4096, 32)):
+    for T, E, G in ((1000000, 256, 8), (345857, 256, 8), (65536, 4096, 32)):
         s = shape(T=T, E=E, G=G)
         assert lib.ep_workspace_bytes(C.byref(s)) > 8 << 20
         assert noalloc_rc(lib, s, status=p()) == B.ERR_WORKSPACE_TOO_SMALL
+    # the largest fitting T of the header's example shape, and the pull shapes
+    for T in (345856, 65536, 8192, 4096):
+        assert lib.ep_workspace_bytes(C.byref(shape(T=T))) <= 8 << 20
     # the status word is not a workspace: no size argument, checked as 4 bytes
     with pytest.raises(M.MoeDispError, match="status"):
         sh = shape(T=4, H=64, E=8, G=2, k=2)
