@@ -624,6 +624,10 @@ def main():
     ap.add_argument("--profile-run", action="store_true",
                     help="the headline config's cold steps only (every leg and pass above off): the command "
                          "whose rocprofv3 kernel trace the roofline entry is checked against")
+    ap.add_argument("--profile-groups", action="store_true",
+                    help="the group-deduplicated path's timed calls only, then the bandwidth probes (whose copy "
+                         "calibrates the traffic counters); prints that leg's JSON, not the benchmark line: the "
+                         "command whose rocprofv3 trace and counters the group path's profile holds")
     args = ap.parse_args()
     if args.profile_run:
         args.no_cpu_baseline = args.no_other_workloads = args.no_probe = True
@@ -640,6 +644,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.profile_groups:
+        log("[bench] group-deduplicated path only")
+        groups = run_gpu_groups(args.config, max(20, args.steps // 4), max(5, args.warmup // 4), dev)
+        print(json.dumps({"group_path": groups, "ceilings_gbps": probe_ceilings(dev)}), flush=True)
+        return
     log(f"[bench] config {args.config}: {args.warmup} warmup + {args.steps} timed cold steps")
     main_res = run_gpu(args.config, args.steps, args.warmup, dev, warm=not args.no_warm,
                        split=not args.profile_run)

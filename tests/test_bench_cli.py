@@ -19,5 +19,6 @@ def test_help_lists_the_legs():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 0
-    for flag in ("--steps", "--warmup", "--gpus", "--no-warm", "--profile-run", "--no-cpu-baseline", "--no-probe"):
+    for flag in ("--steps", "--warmup", "--gpus", "--no-warm", "--profile-run", "--profile-groups", "--no-cpu-baseline",
+                 "--no-probe"):
         assert flag in r.stdout
