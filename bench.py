@@ -312,6 +312,26 @@ def dc_summary(res, which="cold"):
             "calls": "ep_dispatch_scatter + ep_combine (the notify phase runs in ep_get_dispatch_layout_notify)"}
 
 
+def page_conventions(res, which="cold"):
+    """The bandwidth figures of the source page's own benchmark conventions,
+    for context (not this line's metric): per phase, token bytes T*H*elt
+    over the phase's time (the high-throughput bench counts the tokens sent,
+    not the expanded receive layout), and per routed copy R*H*elt (the
+    low-latency combine counts one copy per dispatched token, as dispatch
+    does).  Phases: the scatter (the dispatch's copy) and the combine, cold
+    medians."""
+    ph = res[which]
+    t_d = ph["scatter_us"]["median"] * 1e-6
+    t_c = ph["combine_us"]["median"] * 1e-6
+    elt = 1 if res["x_dtype"] == "fp8_e4m3" else 2
+    tok = res["T"] * res["H"] * elt
+    copies = res["R"] * res["H"] * elt
+    out = res["R"] * res["H"] * 2
+    return {"dispatch_us": t_d * 1e6, "combine_us": t_c * 1e6, "token_bytes": tok,
+            "dispatch_token_gbps": tok / t_d / 1e9, "combine_token_gbps": res["T"] * res["H"] * 2 / t_c / 1e9,
+            "copy_bytes": copies, "dispatch_copy_gbps": copies / t_d / 1e9, "combine_copy_gbps": out / t_c / 1e9}
+
+
 def run_gpu_quant(cid, block, fmt, steps, warmup, dev):
     """Quantise-on-dispatch (notify + quantising scatter) on config `cid`,
     back to back; medians over `steps`."""
@@ -757,6 +777,7 @@ def main():
             "step_us": main_res["warm"]["step_us"]["median"],
             "tokens_per_s": main_res["T"] / (main_res["warm"]["step_us"]["median"] * 1e-6),
             "dispatch_combine": dc_summary(main_res, "warm"), "all": main_res["warm"]},
+        "page_conventions": page_conventions(main_res),
         "calls_cold_us": main_res["calls_cold"],
         "kernels": main_res["kernels"],
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBPS,
