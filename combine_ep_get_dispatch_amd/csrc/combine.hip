@@ -53,11 +53,19 @@ __device__ inline void fma8(float* acc, float w, v4u v) {
     acc[7] = __builtin_fmaf(w, bf16_hi(v.w), acc[7]);
 }
 
+// One output unit of token t (16 bytes of bf16, or 32 of fp32) at column
+// unit cc.  bf16 rows (the path's output) go out as buffer stores from the
+// token's row (a wave-uniform base) with the sc1 policy.  At T = 4096,
+// H = 7168, k = 8 the combine's reads alone run at the rate of a plain read
+// stream (a bare gather-sum without its stores: 68.4 against 68.3 us), and
+// its 58.7 MB of output writes cost 20 us more; with sc1 they cost about
+// 1.8 us less than with non-temporal stores (median of 5 cold A/B rounds:
+// 89.5 against 91.3 us), nt with sc0 and sc1 no better; the same at k = 2.
 template <bool kF32>
-__device__ inline void store_out(void* out, size_t unit, const float* acc) {
+__device__ inline void store_out(void* out, int row16, int t, int cc, const float* acc) {
     if constexpr (kF32) {
         typedef float f4 __attribute__((ext_vector_type(4)));
-        f4* o = reinterpret_cast<f4*>(out) + 2 * unit;
+        f4* o = reinterpret_cast<f4*>(out) + 2 * ((size_t)t * row16 + cc);
         const f4 a0 = {acc[0], acc[1], acc[2], acc[3]};
         const f4 a1 = {acc[4], acc[5], acc[6], acc[7]};
         __builtin_nontemporal_store(a0, o);
@@ -68,7 +76,9 @@ __device__ inline void store_out(void* out, size_t unit, const float* acc) {
         r.y = pack_bf16x2(acc[2], acc[3]);
         r.z = pack_bf16x2(acc[4], acc[5]);
         r.w = pack_bf16x2(acc[6], acc[7]);
-        __builtin_nontemporal_store(r, reinterpret_cast<v4u*>(out) + unit);
+        v4u* row = reinterpret_cast<v4u*>(out) + (size_t)t * row16;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, row16 * 16, kRawBufferWord3);
+        __builtin_amdgcn_raw_buffer_store_b128(r, rs, cc * 16, 0, kCombineStorePolicy);
     }
 }
 
@@ -146,7 +156,7 @@ __device__ inline void gather_sum(const CombineArgs& a, int t, int c0, int c1, c
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int cc = c + u * nth;
-            if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
+            if (cc < c1) store_out<kF32>(a.out, a.row16, t, cc, acc[u]);
         }
         c += U * nth;
         if (c >= c1) break;
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(kMaxCombineThreads) void moedisp_combine(CombineArg
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int cc = c + u * nth;
-                if (cc < c1) store_out<kF32>(a.out, (size_t)t * a.row16 + cc, acc[u]);
+                if (cc < c1) store_out<kF32>(a.out, a.row16, t, cc, acc[u]);
             }
         }
     }

@@ -25,6 +25,7 @@ constexpr int kStreamStorePolicy = 1 | 2 | 16;  // sc0 | nt | sc1
 // value 4 at bits 15..18), no swizzle, no index stride.  Accesses past
 // `row_bytes` are dropped by the hardware; the callers stay inside the row.
 constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kCombineStorePolicy = 16;  // sc1: the combine's bf16 output rows
 __device__ inline void stream_store(v4u v, v4u* row, uint32_t row_bytes, int unit) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(row, (short)0, (int)row_bytes, kRawBufferWord3);
     __builtin_amdgcn_raw_buffer_store_b128(v, rs, unit * 16, 0, kStreamStorePolicy);
