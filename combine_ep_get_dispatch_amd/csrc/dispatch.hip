@@ -343,7 +343,10 @@ __global__ __launch_bounds__(kMaxDispatchThreads) void moedisp_scatter(DispatchA
 // and a wave sum, done by every wave (no barrier); its loads are issued before
 // the source row's, so the row computation does not wait for the row (sums of
 // the column with scalar loads measured slower: 109-117 against 94-98 us at
-// T = 4096, H = 7168, k = 8).  A row outside its expert's segment or the buffer is not
+// T = 4096, H = 7168, k = 8).  The wave sum uses DPP moves: with lane
+// shuffles (ds_bpermute) each of its six steps waits on the LDS counter,
+// which the entry's scalar loads share; the DPP sum measured the same cold
+// and 1-4 us faster back to back.  A row outside its expert's segment or the buffer is not
 // written and raises BAD_LAYOUT; masked entries only set slot_to_row to -1.
 
 // This lane's quad of expert column `col` for the prefix over blocks [0, b),
@@ -420,7 +423,7 @@ __device__ __forceinline__ void pull_copy(const DispatchArgs& a, int b, int i0, 
         if (ex[r] < 0) continue;
         const int e = ex[r];
         const long long base = a.expert_offsets[e];
-        const long long rr = base + wave_sum(count_quad_sum(quad[r], b)) + (i0 + r) -
+        const long long rr = base + wave_sum_dpp(count_quad_sum(quad[r], b)) + (i0 + r) -
                              a.pull_ls[(size_t)b * a.E + e];
         if (rr < 0 || rr < base || rr >= base + a.tokens_per_expert[e] || rr >= a.capacity)
             err |= MOEDISP_DEV_BAD_LAYOUT;

@@ -29,7 +29,6 @@ static __device__ inline uint32_t div_const(uint32_t x, int shift, uint32_t magi
     return shift >= 0 ? x >> shift : __umulhi(x, magic);
 }
 
-// Sum of v over the 64 lanes of the wave (every lane gets the sum).
 // Inclusive scan over the wave with DPP moves (no LDS round trip): sums
 // inside each 16-lane row (row_shr 1, 2, 4, 8), then row 0's total into
 // rows 1 and 3 and row 1's running total into rows 2 and 3 (row_bcast 15
@@ -45,14 +44,10 @@ static __device__ inline int32_t wave_inclusive_scan_dpp(int32_t v) {
     return v;
 }
 
+// Sum of v over the 64 lanes of the wave (every lane gets it, in a scalar
+// register); whole wave, all lanes active.
 static __device__ inline int32_t wave_sum_dpp(int32_t v) {
     return __builtin_amdgcn_readlane(wave_inclusive_scan_dpp(v), 63);
-}
-
-static __device__ inline int32_t wave_sum(int32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-    return v;
 }
 
 // Exclusive scan of in[0..n) (global or LDS) into out (LDS), by the whole
