@@ -438,8 +438,9 @@ def run_gpu_decode(cid, steps, warmup, dev):
     notify, scatter, combine), the small-batch path (layout + dispatch in one
     launch, then combine), and that path replayed from a captured HIP graph
     of 10 steps, also with the padded (low-latency) receive layout of T rows
-    per expert.  Each figure is the mean GPU time per step over back-to-back
-    steps between two events."""
+    per expert; beside them, the same graph with two minimal kernels per step
+    (the floor of two dependent launches on this part).  Each figure is the
+    mean GPU time per step over back-to-back steps between two events."""
     import torch
     import combine_ep_get_dispatch_amd as M
     from combine_ep_get_dispatch_amd import workloads as W
@@ -515,6 +516,25 @@ def run_gpu_decode(cid, steps, warmup, dev):
         for _ in range(per_graph):
             small_padded(torch.cuda.current_stream())
     res["small_padded_graph_us"] = per_step(lambda stream: graph_pad.replay()) / per_graph
+    # the floor of a step of two dependent launches on this part: the same
+    # graph of 10 steps with two minimal kernels per step (one workgroup
+    # reading 16 KiB each)
+    probe_src = torch.zeros(16384, dtype=torch.uint8, device=dev)
+    probe_sink = torch.zeros(16, dtype=torch.uint8, device=dev)
+
+    def two_minimal(stream):
+        M.ep_probe_read(probe_src, 16384, probe_sink, stream)
+        M.ep_probe_read(probe_src, 16384, probe_sink, stream)
+
+    with torch.cuda.stream(side):
+        two_minimal(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_floor = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_floor):
+        for _ in range(per_graph):
+            two_minimal(torch.cuda.current_stream())
+    res["graph_floor_us"] = per_step(lambda stream: graph_floor.replay()) / per_graph
     # the small-batch dispatch alone, events around each call
     stream = torch.cuda.current_stream()
     g = EventGrid(steps, 2)
@@ -531,7 +551,11 @@ def run_gpu_decode(cid, steps, warmup, dev):
     B = algorithmic_bytes(wl.T, wl.H, wl.E, wl.G, wl.k, R, x_elt, wl.scale_block)
     res["step_bytes"] = B["step"]
     res["tokens_per_s_graph"] = wl.T / (res["small_graph_us"] * 1e-6)
-    del graph, graph_pad, pb, eo_pad, bufs, x, xs, idx, w, eo, out
+    # the step's bytes over its time above the two-launch floor
+    above = res["small_graph_us"] - res["graph_floor_us"]
+    res["above_floor_us"] = above
+    res["above_floor_gbps"] = B["step"] / (above * 1e-6) / 1e9 if above > 0 else None
+    del graph, graph_pad, graph_floor, pb, eo_pad, bufs, x, xs, idx, w, eo, out, probe_src, probe_sink
     torch.cuda.empty_cache()
     return res
 
