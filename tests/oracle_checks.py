@@ -312,6 +312,30 @@ def check_worked_example(orc, path=os.path.join(GOLDEN, "worked_example.json")):
     assert np.array_equal(ob, torch_bf16_bits(np.array(g["out"], np.float32)))
 
 
+def check_sum_order(orc, path=os.path.join(GOLDEN, "sum_order.json")):
+    """Both combines sum in a fixed fp32 order: the flat one by fused
+    multiply-add over ascending slots, the group one over ascending groups.
+    Hand-derived cases (the fixture's derivation) whose binary32 results
+    change under any other order, under row order, or with the product
+    rounded before the add."""
+    with open(path) as f:
+        g = json.load(f)
+    fl = g["flat"]
+    eo = torch_bf16_bits(np.array(fl["expert_out"], np.float32))
+    assert bf16_to_f64(eo).tolist() == fl["expert_out"], "rows must be exact in bf16"
+    w = np.array(fl["recv_weights"], np.float32)
+    assert w.astype(np.float64).tolist() == fl["recv_weights"], "weights must be exact in fp32"
+    of, ob = orc.combine(eo, w, np.array(fl["slot_to_row"], np.int32))
+    assert of.astype(np.float64).tolist() == fl["out_f32"], of
+    assert np.array_equal(ob, torch_bf16_bits(of))
+    gr = g["groups"]
+    rows = torch_bf16_bits(np.array(gr["group_rows"], np.float32))
+    assert bf16_to_f64(rows).tolist() == gr["group_rows"]
+    of, ob = orc.combine_groups(rows, np.array(gr["token_group_row"], np.int32))
+    assert of.astype(np.float64).tolist() == gr["out_f32"], of
+    assert np.array_equal(ob, torch_bf16_bits(of))
+
+
 def check_error_status(orc):
     idx = np.array([[0, 5], [1, 1], [-1, 2]], np.int32)   # 5 >= E: bad id; repeat in token 1
     tpe, tpg, bm, st = orc.layout(idx, 4, 2)
@@ -752,7 +776,7 @@ def check_padded_all(orc):
 
 
 ALL_BASIC = [check_bf16_rounding, check_bruteforce, check_combine_exact_dyadic, check_combine_k1_inverse,
-             check_worked_example, check_error_status, check_padded_all]
+             check_worked_example, check_sum_order, check_error_status, check_padded_all]
 
 
 def small_configs():

@@ -109,6 +109,29 @@ MUTANTS = {
     "padded_stride": ("int64_t q = (int64_t)id * S + B + i;", "int64_t q = (int64_t)id * C + B + i;"),
     # padded layout: overflow not reported
     "padded_no_status": ("st |= ORACLE_ERR_OVERFLOW;", "st |= 0;"),
+    # combine: slots summed in descending order
+    "combine_reverse_order": ("            for (int j = 0; j < k; ++j) {\n                int32_t r = slot_to_row",
+                              "            for (int j = k - 1; j >= 0; --j) {\n                int32_t r = slot_to_row"),
+    # combine: the product rounded to fp32 before the add (no fused multiply-add)
+    "combine_no_fma": ("acc = fmaf(recv_weights[r], v, acc);",
+                       "{ volatile float p = recv_weights[r] * v; acc = acc + p; }"),
+    # group combine: groups summed in descending order
+    "group_combine_reverse": ("            for (int g = 0; g < G; ++g) {\n                int32_t r = token_group_row",
+                              "            for (int g = G - 1; g >= 0; --g) {\n                int32_t r = token_group_row"),
+    # layout: a count set instead of incremented
+    "layout_count_assign": ("if (routed(id, E)) tokens_per_expert[id] += 1;",
+                            "if (routed(id, E)) tokens_per_expert[id] = 1;"),
+    # dispatch: fp8 scales not moved with the rows
+    "dispatch_scales_dropped": ("memcpy(recv_x + r * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);\n"
+                                "            if (x_scales && recv_scales && scale_row_bytes > 0)",
+                                "memcpy(recv_x + r * row_bytes, x + (int64_t)t * row_bytes, (size_t)row_bytes);\n"
+                                "            if (0)"),
+    # group dispatch: the group rows' total one short
+    "group_total_off": ("    group_offsets[G] = (int32_t)run;", "    group_offsets[G] = (int32_t)(run - 1);"),
+    # group dispatch: wrong source token recorded
+    "group_src_idx": ("recv_src_idx[r] = (int32_t)t;", "recv_src_idx[r] = (int32_t)(T - 1 - t);"),
+    # padded layout: the token's first weight for every copy
+    "padded_weight_slot": ("recv_weights[q] = topk_weights[s];", "recv_weights[q] = topk_weights[(int64_t)t * k];"),
     # quantised dispatch: the scales are not moved with the rows
     "quant_scales_dropped": ("st = oracle_dispatch(T, k, E, H, scale_bytes, q, sc, topk_idx",
                              "st = oracle_dispatch(T, k, E, H, scale_bytes, q, NULL, topk_idx"),

@@ -19,6 +19,12 @@ def test_worked_example(orc):
     K.check_worked_example(orc)
 
 
+def test_sum_order(orc):
+    """Both combines' fp32 summation order (ascending slots by FMA, ascending
+    groups), from hand-derived binary32 cases (tests/golden/sum_order.json)."""
+    K.check_sum_order(orc)
+
+
 def test_error_status_bits(orc):
     K.check_error_status(orc)
 

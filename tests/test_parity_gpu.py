@@ -1,9 +1,9 @@
 """GPU parity of libmoedisp against the CPU oracle (needs an MI355X).
 
 Bit-exact: layout counts, bitmap, offsets, slot_to_row, recv_src_idx,
-recv_weights, received rows and scales.  Combine: max relative error 1e-3 in
-fp32 and at most one bf16 ulp after rounding, on every token of every case,
-the full sizes included (they run in the same launch configuration as the
+recv_weights, received rows and scales.  Combine: bit for bit in fp32 and in
+its bf16 rounding (the kernel sums in the oracle's order by fused
+multiply-add), on every token of every case, the full sizes included (they run in the same launch configuration as the
 benchmark).  Shapes with at least 256 tokens and at most 512 experts take the
 block-pull dispatch (blocks of tokens per XCD, a sorted list per block);
 smaller ones take the push scatter; both are covered here.

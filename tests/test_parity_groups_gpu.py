@@ -6,8 +6,8 @@ Bit-exact: group offsets, the token -> group-row handle, group rows and
 scales, source tokens, restricted routing (ids and weight bits), the rows
 past the last group row marked unrouted, and everything the local expert
 permutation writes (its rows, offsets, weights and handle).  The local reduce
-and the group combine are held to the combine bar (max relative error 1e-3
-in fp32, at most one bf16 ulp); each runs on the oracle's own inputs.
+and the group combine are held to the combine bar (bit for bit in fp32 and
+in the bf16 rounding); each runs on the oracle's own inputs.
 """
 import numpy as np
 import pytest
