@@ -161,7 +161,9 @@ int ep_dispatch_noalloc(const moedisp_shape* shape, const void* x, const float* 
  *   expert_offsets[E+1] (exclusive scan of tokens_per_expert).
  * ep_dispatch_scatter: everything else ep_dispatch writes; it reads the counts
  *   and expert_offsets that ep_dispatch_notify left for the same topk_idx and
- *   tokens_per_expert in the same `ws` (stream-ordered before it).
+ *   tokens_per_expert in the same `ws` (stream-ordered before it, with no
+ *   other dispatch-family call on that `ws` in between: those reuse the
+ *   same workspace tables).
  * Arguments, layouts and status bits as for ep_dispatch. */
 int ep_dispatch_notify(const moedisp_shape* shape, const int32_t* topk_idx, const int32_t* tokens_per_expert,
                        int32_t* expert_offsets, void* ws, size_t ws_bytes, void* stream);
