@@ -23,7 +23,9 @@ before the scatter, before the combine and after it.  Every figure is the
 median over the K timed steps, with the min and the mean beside it.
 value = T / median step time; ms_per_step = that median.  The timed region
 is exactly K steps, each with its flush read, between two device
-synchronisations; its wall time is timed_region_ms.
+synchronisations; its wall time is timed_region_ms (about 1 s at the
+default K = 3000, so that the GPU's busy time is long enough to be seen by a
+sampler outside the process).
 
 dispatch_combine = the scatter and the combine (the dispatch's notify phase
 runs inside the layout call), between the events before the scatter and
@@ -655,7 +657,7 @@ def cpu_baseline(reps: int = 3):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[1])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, help="workload for the headline line (default 2)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
