@@ -184,3 +184,47 @@ def test_permute_entries_on_one_xcd(orc, dev):
     eq(gb.perm_src_idx[:R].cpu().numpy(), o["recv_src_idx"][:R], "recv_src_idx")
     eq(bufs.recv_weights[:R].cpu().numpy(), o["recv_weights"][:R], "recv_weights")
     eq(gb.perm_slot_to_row.cpu().numpy(), o["slot_to_row"], "slot_to_row")
+
+
+ERROR_CASES = {
+    # the local permutation on the block-pull copy, and on the push scatter
+    "pull_permute": lambda: W.make_workload("err_pull", 600, 512, 64, 8, 8, seed=86),
+    "push_permute": lambda: W.make_workload("err_push", 100, 256, 8, 2, 2, seed=87),
+}
+
+
+@pytest.mark.parametrize("name", list(ERROR_CASES))
+def test_group_path_inconsistent_counts_are_reported(dev, name):
+    """tokens_per_group, then tokens_per_expert, changed so that they disagree
+    with the routing: ep_dispatch_groups and ep_group_permute report
+    BAD_LAYOUT, write every handle entry (a row or -1), and no handle names a
+    row outside its receive buffer."""
+    wl = ERROR_CASES[name]()
+    shape = GH.shape_of(wl)
+    assert M.ep_plan_query(shape)["permute_pull"] == (name == "pull_permute")
+    bufs = M.EpBuffers(shape, dev)
+    gb = M.EpGroupBuffers(bufs)
+    inp = GH.GpuInputs(wl, dev)
+    bufs.layout(inp.topk_idx)
+    assert bufs.status() == 0
+    _say(f"[groups-err] {name}: group counts")
+    good = bufs.tokens_per_group.clone()
+    bufs.tokens_per_group[0] += 3
+    bufs.tokens_per_group[1] -= 1
+    gb.token_group_row.fill_(-7)
+    gb.dispatch_groups(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    assert bufs.status() & M.binding.DEV_BAD_LAYOUT
+    tgr = gb.token_group_row.cpu().numpy()
+    assert tgr.min() >= -1 and tgr.max() < gb.capacity
+
+    _say(f"[groups-err] {name}: expert counts")
+    bufs.tokens_per_group.copy_(good)
+    gb.dispatch_groups(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    assert bufs.status() == 0
+    bufs.tokens_per_expert[0] += 2
+    bufs.tokens_per_expert[wl.E - 1] -= 1
+    gb.perm_slot_to_row.fill_(-7)
+    gb.permute()
+    assert bufs.status() & M.binding.DEV_BAD_LAYOUT
+    p = gb.perm_slot_to_row.cpu().numpy()
+    assert p.min() >= -1 and p.max() < wl.T * wl.k
