@@ -175,3 +175,24 @@ def test_quant_every_bf16_amax(orc, dev, fmt, two_phase):
     value in turn, bit-exact against the oracle (whose UE8M0 exponent rule is
     itself pinned by brute force over the same values)."""
     run_case(orc, amax_sweep_workload(), dev, 32, fmt, two_phase)
+
+
+@pytest.mark.parametrize("fmt", [FP32, UE8M0], ids=["fp32", "ue8m0"])
+def test_quant_inconsistent_counts_are_reported(dev, fmt):
+    """tokens_per_expert changed so that it disagrees with the routing (and
+    its total exceeds the T*k receive rows): ep_dispatch_quant reports
+    BAD_LAYOUT, writes every slot's handle entry, and names no row outside
+    the receive buffer."""
+    wl = W.make_workload("quant_bad_counts", 300, 512, 16, 4, 4, seed=88)
+    bufs = M.EpBuffers(GH.shape_of(wl), dev).enable_quant(128, fmt)
+    inp = GH.GpuInputs(wl, dev)
+    bufs.layout(inp.topk_idx)
+    assert bufs.status() == 0
+    _say(f"[quant-err] fmt={fmt}")
+    bufs.tokens_per_expert[0] += 3
+    bufs.tokens_per_expert[wl.E - 1] -= 1
+    bufs.slot_to_row.fill_(-7)
+    bufs.dispatch_quant(inp.x, inp.topk_idx, inp.topk_weights)
+    assert bufs.status() & M.binding.DEV_BAD_LAYOUT
+    s = bufs.slot_to_row.cpu().numpy()
+    assert s.min() >= -1 and s.max() < wl.T * wl.k
