@@ -228,3 +228,37 @@ def test_group_path_inconsistent_counts_are_reported(dev, name):
     assert bufs.status() & M.binding.DEV_BAD_LAYOUT
     p = gb.perm_slot_to_row.cpu().numpy()
     assert p.min() >= -1 and p.max() < wl.T * wl.k
+
+
+def test_group_reduce_and_combine_report_bad_handles(dev):
+    """A handle entry past the rows it indexes, and a row whose source no
+    longer names its group row (reduce) or token (group combine): each call
+    raises BAD_HANDLE and skips those slots (no load through them)."""
+    wl = W.make_workload("grp_bad_handle", 64, 256, 16, 4, 4, seed=89)
+    bufs = M.EpBuffers(GH.shape_of(wl), dev)
+    gb = M.EpGroupBuffers(bufs)
+    inp = GH.GpuInputs(wl, dev)
+    bufs.layout(inp.topk_idx)
+    gb.dispatch_groups(inp.x, inp.x_scales, inp.topk_idx, inp.topk_weights)
+    gb.permute()
+    assert bufs.status() == 0
+    cap = gb.capacity
+    _say("[groups-err] reduce handle")
+    p = gb.perm_slot_to_row
+    p[0, 0] = wl.T * wl.k + 50                  # past the expert rows
+    row1 = p[1].cpu().numpy()
+    gb.perm_src_idx[int(row1[row1 >= 0][0])] = 0  # no longer names group row 1
+    eo = bufs.recv_x.view(torch.bfloat16)
+    red = torch.empty((cap, wl.H), dtype=torch.float32, device=dev)
+    gb.reduce(eo, red, M.FP32)
+    assert bufs.status() & M.binding.DEV_BAD_HANDLE
+    _say("[groups-err] group combine handle")
+    t = gb.token_group_row
+    t[3, 0] = cap + 9                           # past the group rows
+    row7 = t[7].cpu().numpy()
+    gb.group_src_idx[int(row7[row7 >= 0][0])] = 0  # no longer names token 7
+    grows = torch.zeros((cap, wl.H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+    gb.combine_groups(grows, out, M.FP32)
+    assert bufs.status() & M.binding.DEV_BAD_HANDLE
+    assert torch.count_nonzero(out) == 0        # every other slot summed its zero rows
